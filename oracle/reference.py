@@ -1,0 +1,124 @@
+"""GEMM, low-rank and dequantization references (oracle; test infrastructure only).
+
+* ``y = X W^T`` with W stored [N, K], the nn.Linear convention that the Nunchaku
+  post's "Introducing Nunchaku Lite" section patches.
+* Quantized linears (Diffusers "BFL (fp8r / nvfp4)" guide, intro bullets and the
+  "Kernels" table): the result is defined as dequantize-then-multiply, with both
+  dequantized operands exact in float64 and the product taken by a float64
+  matmul (a library routine; only its rounding order is unspecified).
+* SVDQuant branch ("Bringing Nunchaku 4-bit Diffusion Inference to Diffusers",
+  section "Background: SVDQuant and Nunchaku"): a 16-bit low-rank term
+  ``(X L1) L2`` is added to the 4-bit product before the output is rounded.
+* Fallback (guide, "Kernels" section, last paragraph): weights dequantized to the
+  compute dtype (bf16) on every forward.
+* Acceptance test for a bf16 GEMM output against the float64 reference.
+"""
+import math
+
+import numpy as np
+
+from .formats import bf16_bits_to_f32, e2m1_decode, e4m3_decode, f32_to_bf16_bits
+from .quant import unpack_e2m1
+
+F32 = np.float32
+
+
+def dequant_fp8r(codes, scale):
+    """float64 [R, K] = dec(codes) * scale[row] (exact)."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+def dequant_nvfp4(packed, block_scale, g):
+    """float64 [R, K] = dec2(code) * dec(block_scale) * g (exact: <= 30 bits)."""
+    c = unpack_e2m1(packed)
+    R, K = c.shape
+    v = e2m1_decode(c).reshape(R, K // 16, 16)
+    sf = e4m3_decode(block_scale)[:, :, None]
+    return (v * sf * np.float64(F32(g))).reshape(R, K)
+
+
+def qlinear_fp8r_ref(x_codes, x_scale, w_codes, w_scale):
+    """float64 [M, N] reference of the fp8r linear on the same quantized operands."""
+    return dequant_fp8r(x_codes, x_scale) @ dequant_fp8r(w_codes, w_scale).T
+
+
+def qlinear_nvfp4_ref(x_packed, x_bs, input_scale, w_packed, w_bs, weight_scale_2):
+    """float64 [M, N] reference of the nvfp4 linear on the same quantized operands."""
+    return dequant_nvfp4(x_packed, x_bs, input_scale) @ dequant_nvfp4(w_packed, w_bs, weight_scale_2).T
+
+
+def lowrank_ref(x_bits, l1_bits, l2_bits):
+    """float64 [M, N] = (X L1) L2 from bf16 X [M,K], L1 [K,R], L2 [R,N], no
+    intermediate rounding beyond float64."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    l1 = bf16_bits_to_f32(l1_bits).astype(np.float64)
+    l2 = bf16_bits_to_f32(l2_bits).astype(np.float64)
+    return (x @ l1) @ l2
+
+
+def lowrank_abs(x_bits, l1_bits, l2_bits):
+    """(|X| |L1|) |L2|, the magnitude sum that bounds rounding in the low-rank term."""
+    x = np.abs(bf16_bits_to_f32(x_bits).astype(np.float64))
+    l1 = np.abs(bf16_bits_to_f32(l1_bits).astype(np.float64))
+    l2 = np.abs(bf16_bits_to_f32(l2_bits).astype(np.float64))
+    return (x @ l1) @ l2
+
+
+def dequant_weight_fp8r(w_codes, w_scale):
+    """bf16 bits [N, K] = bf16_RNE(fp32(dec(w) * s[n]))."""
+    p = (e4m3_decode(w_codes).astype(F32) * np.asarray(w_scale, F32)[:, None]).astype(F32)
+    return f32_to_bf16_bits(p)
+
+
+def dequant_weight_nvfp4(w_packed, w_bs, weight_scale_2):
+    """bf16 bits [N, K] = bf16_RNE(fp32(fp32(dec2(w) * dec(sf)) * weight_scale_2))."""
+    c = unpack_e2m1(w_packed)
+    N, K = c.shape
+    v = e2m1_decode(c).astype(F32).reshape(N, K // 16, 16)
+    sf = e4m3_decode(w_bs).astype(F32)[:, :, None]
+    p = (v * sf).astype(F32)
+    p = (p * F32(weight_scale_2)).astype(F32)
+    return f32_to_bf16_bits(p.reshape(N, K))
+
+
+def ulp_bf16(r):
+    """Unit in the last place of bf16 at |r| (float64): 2**(max(floor(log2|r|), -126) - 7),
+    and the smallest subnormal step 2**-133 at r == 0."""
+    r = np.abs(np.asarray(r, dtype=np.float64))
+    e = np.full(r.shape, -126, dtype=np.int64)
+    nz = r > 0
+    e[nz] = np.maximum(np.frexp(r[nz])[1].astype(np.int64) - 1, -126)
+    u = np.ldexp(1.0, e - 7)
+    return np.where(nz, u, 2.0 ** -133)
+
+
+def gemm_gamma(K):
+    """Floor coefficient for fp32 accumulation of K exact products, summed in
+    blocks of 16 or more: ceil(K / 16) * 2**-24."""
+    return math.ceil(K / 16) * 2.0 ** -24
+
+
+def check_gemm(y_bits, ref, abs_sum, K, extra_abs=None, max_ulps=4.0, frob_tol=2e-3):
+    """Acceptance test of a bf16 GEMM output against its float64 reference.
+
+    * relative Frobenius error ||y - ref|| / ||ref|| <= frob_tol over the whole output;
+    * per element |y - ref| <= max_ulps * ulp_bf16(ref) + gamma(K) * sum_k |a_k w_k|
+      (plus gamma * the low-rank magnitude sum when given).
+
+    Returns a dict with the figures and a boolean ``ok``.
+    """
+    y = bf16_bits_to_f32(y_bits).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(y - ref)
+    den = np.linalg.norm(ref)
+    frob = float(np.linalg.norm(y - ref) / den) if den > 0 else float(np.linalg.norm(y))
+    ulp = ulp_bf16(ref)
+    floor = gemm_gamma(K) * np.asarray(abs_sum, dtype=np.float64)
+    if extra_abs is not None:
+        floor = floor + gemm_gamma(K) * np.asarray(extra_abs, dtype=np.float64)
+    bound = max_ulps * ulp + floor
+    fails = int(np.count_nonzero(err > bound))
+    only_floor = int(np.count_nonzero((err > max_ulps * ulp) & (err <= bound)))
+    max_ulp_err = float(np.max(err / ulp)) if err.size else 0.0
+    ok = (frob <= frob_tol) and fails == 0 and bool(np.all(np.isfinite(y)))
+    return dict(ok=ok, frob=frob, fails=fails, only_floor=only_floor, max_ulp_err=max_ulp_err)

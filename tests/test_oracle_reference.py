@@ -1,0 +1,163 @@
+"""Pins for oracle.reference: the float64 GEMM references against exact rational
+brute force on tiny shapes, special cases with closed forms, the dequantize
+fallback against torch's float8/bf16 conversions, and the acceptance test."""
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from conftest import read_golden
+
+from oracle.formats import bf16_bits_to_f32, e4m3_decode, f32_to_bf16_bits
+from oracle.quant import amax_bf16, global_scale, quant_fp8_row, quant_nvfp4, unpack_e2m1
+from oracle.reference import (check_gemm, dequant_weight_fp8r, dequant_weight_nvfp4, gemm_gamma,
+                              lowrank_ref, qlinear_fp8r_ref, qlinear_nvfp4_ref, ulp_bf16)
+from synthetic import bf16_round
+
+F32 = np.float32
+E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+
+
+def e4m3_frac(c):
+    c = int(c)
+    s = -1 if c & 0x80 else 1
+    e, m = (c >> 3) & 15, c & 7
+    if e == 0:
+        return s * Fraction(m, 8) * Fraction(1, 64)
+    return s * (1 + Fraction(m, 8)) * (Fraction(2) ** (e - 7))
+
+
+def e2m1_frac(n):
+    n = int(n)
+    return (-1 if n & 8 else 1) * E2M1[n & 7]
+
+
+def rand_bf16(shape, seed, scale=1.0):
+    return bf16_round(np.random.default_rng(seed).standard_normal(shape).astype(F32) * F32(scale))
+
+
+def test_fp8r_ref_matches_rational_bruteforce():
+    x, w = rand_bf16((3, 32), 1), rand_bf16((5, 32), 2, 0.02)
+    xq, xs = quant_fp8_row(x)
+    wq, ws = quant_fp8_row(w)
+    ref = qlinear_fp8r_ref(xq, xs, wq, ws)
+    for m in range(3):
+        for n in range(5):
+            terms = [e4m3_frac(xq[m, k]) * Fraction(float(xs[m])) * e4m3_frac(wq[n, k]) * Fraction(float(ws[n]))
+                     for k in range(32)]
+            exact, mag = sum(terms), sum(abs(t) for t in terms)
+            assert abs(Fraction(ref[m, n]) - exact) <= mag * Fraction(32, 2 ** 52)
+
+
+def test_nvfp4_ref_matches_rational_bruteforce():
+    x, w = rand_bf16((3, 48), 3), rand_bf16((4, 48), 4, 0.02)
+    gx, gw = global_scale(amax_bf16(x)), global_scale(amax_bf16(w))
+    xp, xb = quant_nvfp4(x, gx)
+    wp, wb = quant_nvfp4(w, gw)
+    ref = qlinear_nvfp4_ref(xp, xb, gx, wp, wb, gw)
+    xc, wc = unpack_e2m1(xp), unpack_e2m1(wp)
+    for m in range(3):
+        for n in range(4):
+            exact, mag = Fraction(0), Fraction(0)
+            for k in range(48):
+                a = e2m1_frac(xc[m, k]) * e4m3_frac(xb[m, k // 16]) * Fraction(float(gx))
+                b = e2m1_frac(wc[n, k]) * e4m3_frac(wb[n, k // 16]) * Fraction(float(gw))
+                exact += a * b
+                mag += abs(a * b)
+            assert abs(Fraction(ref[m, n]) - exact) <= mag * Fraction(48, 2 ** 52)
+
+
+def test_fp8r_one_hot_weight_selects_a_column():
+    # W row n is one-hot at k = n with code 0x38 (1.0) and scale 1: y[:, n] = dequantized x[:, n]
+    x = rand_bf16((6, 32), 5)
+    xq, xs = quant_fp8_row(x)
+    wq = np.zeros((8, 32), np.uint8)
+    wq[np.arange(8), np.arange(8)] = 0x38
+    y = qlinear_fp8r_ref(xq, xs, wq, np.ones(8, F32))
+    assert np.array_equal(y, e4m3_decode(xq[:, :8]) * xs[:, None].astype(np.float64))
+
+
+def test_nvfp4_transposed_operand_would_fail():
+    # a reference that forgot the transpose or swapped operands differs on non-square shapes
+    x, w = rand_bf16((4, 32), 6), rand_bf16((4, 32), 7)
+    gx, gw = global_scale(amax_bf16(x)), global_scale(amax_bf16(w))
+    xp, xb = quant_nvfp4(x, gx)
+    wp, wb = quant_nvfp4(w, gw)
+    y = qlinear_nvfp4_ref(xp, xb, gx, wp, wb, gw)
+    y_swapped = qlinear_nvfp4_ref(wp, wb, gw, xp, xb, gx)
+    assert np.allclose(y, y_swapped.T) and not np.allclose(y, y_swapped)
+
+
+def test_lowrank_ref_matches_rational_bruteforce():
+    x, l1, l2 = rand_bf16((2, 16), 8), rand_bf16((16, 3), 9, 0.05), rand_bf16((3, 4), 10, 0.05)
+    ref = lowrank_ref(x, l1, l2)
+    X, A, B = (bf16_bits_to_f32(t).astype(np.float64) for t in (x, l1, l2))
+    for m in range(2):
+        for n in range(4):
+            terms = [Fraction(X[m, k]) * Fraction(A[k, r]) * Fraction(B[r, n]) for k in range(16) for r in range(3)]
+            exact, mag = sum(terms), sum(abs(t) for t in terms)
+            assert abs(Fraction(ref[m, n]) - exact) <= mag * Fraction(64, 2 ** 52)
+
+
+def test_dequant_weight_fp8r_matches_torch_path():
+    w = rand_bf16((16, 64), 11, 0.02)
+    wq, ws = quant_fp8_row(w)
+    t = torch.from_numpy(wq).view(torch.float8_e4m3fn).float() * torch.from_numpy(ws)[:, None]
+    exp = t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(dequant_weight_fp8r(wq, ws), exp)
+
+
+def test_dequant_weight_nvfp4_matches_table_path():
+    w = rand_bf16((8, 64), 12, 0.02)
+    g = global_scale(amax_bf16(w))
+    wp, wb = quant_nvfp4(w, g)
+    got = dequant_weight_nvfp4(wp, wb, g)
+    codes = unpack_e2m1(wp)
+    # the E2M1 value table of the OCP MX spec (keeps -0.0 for code 8)
+    table = np.zeros(16, np.float32)
+    for code, val in read_golden("e2m1_values.txt"):
+        table[int(code)] = float(val)
+    sf = torch.from_numpy(wb).view(torch.float8_e4m3fn).float().numpy()
+    v = table[codes] * np.repeat(sf, 16, axis=1)         # exact in float32
+    t = torch.from_numpy((v * np.float32(g)).astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(got, t.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_ulp_bf16_matches_bf16_spacing():
+    x = np.abs(bf16_bits_to_f32(rand_bf16((1000,), 13, 100.0))).astype(np.float32)
+    x = x[x > 1e-30]
+    nxt = torch.nextafter(torch.from_numpy(x).to(torch.bfloat16), torch.tensor(float("inf"), dtype=torch.bfloat16))
+    spacing = (nxt.double() - torch.from_numpy(x).double()).numpy()
+    assert np.array_equal(ulp_bf16(x), spacing)
+
+
+def test_check_gemm_detects_planted_errors():
+    rng = np.random.default_rng(14)
+    ref = rng.standard_normal((64, 64))
+    abs_sum = np.abs(ref) * 10
+    y = f32_to_bf16_bits(ref.astype(F32))
+    assert check_gemm(y, ref, abs_sum * 0, 16)["ok"]
+    # one element off by 6 ulps fails; 3 ulps passes
+    for k, ok in ((6, False), (3, True)):
+        ref2 = ref.copy()
+        ref2[3, 5] += k * ulp_bf16(ref2[3, 5])
+        res = check_gemm(y, ref2, abs_sum * 0, 16)
+        assert res["ok"] is ok, (k, res)
+    # a uniform relative error of 3e-3 fails the Frobenius bound
+    y3 = f32_to_bf16_bits((ref * 1.003).astype(F32))
+    assert not check_gemm(y3, ref, abs_sum * 0, 16)["ok"]
+
+
+def test_gamma_floor_covers_blocked_fp32_accumulation():
+    # fp32 accumulation of exact products, in blocks of 32 (one MFMA-sized chunk at a time)
+    rng = np.random.default_rng(15)
+    K = 3072
+    a = rng.standard_normal((256, K)).astype(F32)
+    b = rng.standard_normal(K).astype(F32)
+    prod = a.astype(np.float64) * b.astype(np.float64)
+    acc = np.zeros(256, F32)
+    for k0 in range(0, K, 32):
+        acc = (acc + prod[:, k0:k0 + 32].sum(axis=1).astype(F32)).astype(F32)
+    exact = prod.sum(axis=1)
+    bound = gemm_gamma(K) * np.abs(prod).sum(axis=1)
+    assert np.all(np.abs(acc - exact) <= bound)
