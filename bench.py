@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized-linear hot path on one MI355X.
+
+One step runs every step of the path once, at the DiT projection shapes of the
+BFL schemes (M = 4608 tokens = 4096 image + 512 text):
+
+* fp8r   4608 x 3072 x 12288: row-wise E4M3 activation quantize + FP8 GEMM;
+* nvfp4  4608 x 3072 x 12288: NVFP4 activation quantize (calibrated input_scale)
+         + block-scaled GEMM;
+* svdq   4608 x 3072 x 3072 + rank 32: NVFP4 quantize, x L1, GEMM with the
+         low-rank up-projection in the epilogue.
+
+value = total GEMM FLOPs (2 M N K per linear, low-rank FLOPs not counted) / step
+time, with every input resident in HBM.  Weights are quantized once before
+timing by the library's own quantizers, as a pre-quantized checkpoint would
+arrive.  Inputs are seeded synthetic data (see synthetic/workloads.py).
+
+The roofline object covers the dominant kernel (the nvfp4 GEMM at 4608 x 3072 x
+12288): its launches are timed with HIP events on the launch stream inside the
+timed region (the library's event timing).  The cpu_baseline object times the
+CPU oracle on a bounded sample of the same workload (rank 0, one GPU only).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+HBM_GBS = 8000.0
+METRIC = "qlinear TFLOP/s (act-quant+GEMM) and % of FP8/FP4 MFMA peak, M=4608"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_4608x3072x12288.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="activation rows per linear in the CPU sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import precision_quantized_linear_amd as qpl
+    from synthetic import calibration_batches, make
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def global_scale_of(tensors):
+        amax = torch.zeros((1,), dtype=torch.float32, device=dev)
+        for t in tensors:
+            qpl.amax_bf16(t, amax=amax)
+        return qpl.nvfp4_global_scale(float(amax.item()))
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    lin = {}
+    d = make("fp8r_dit_n12288")
+    w = bf16(d["w"])
+    wq, ws = qpl.quant_act_fp8_row(w)
+    lin["fp8r"] = dict(M=d["M"], K=d["K"], N=d["N"], R=0, x=bf16(d["x"]), wq=wq, ws=ws, host=d)
+    del w
+    for key, name in (("nvfp4", "nvfp4_dit"), ("svdq", "svdq_w4a4")):
+        d = make(name)
+        w = bf16(d["w"])
+        g_w = global_scale_of([w])
+        g_in = global_scale_of(bf16(b) for b in calibration_batches(name))
+        wq, wbs = qpl.quant_act_nvfp4(w, g_w)
+        e = dict(M=d["M"], K=d["K"], N=d["N"], R=d.get("R", 0), x=bf16(d["x"]), wq=wq, wbs=wbs, g_w=g_w, g_in=g_in,
+                 host=d)
+        if e["R"]:
+            e["l1"], e["l2"] = bf16(d["l1"]), bf16(d["l2"])
+        lin[key] = e
+        del w
+    for key, e in lin.items():
+        scheme = qpl.QPL_FP8R if key == "fp8r" else qpl.QPL_NVFP4
+        e["y"] = torch.empty((e["M"], e["N"]), dtype=torch.bfloat16, device=dev)
+        e["ws_buf"] = torch.empty((qpl.qlinear_workspace_bytes(scheme, e["M"], e["K"], e["N"], e["R"]),),
+                                  dtype=torch.uint8, device=dev)
+        e["flops"] = 2.0 * e["M"] * e["N"] * e["K"]
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    def run(key):
+        e = lin[key]
+        if key == "fp8r":
+            qpl.qlinear_fp8r(e["x"], e["wq"], e["ws"], y=e["y"], workspace=e["ws_buf"])
+        else:
+            kw = dict(lora_down=e["l1"], lora_up=e["l2"]) if e["R"] else {}
+            qpl.qlinear_nvfp4(e["x"], e["wq"], e["wbs"], e["g_w"], e["g_in"], y=e["y"], workspace=e["ws_buf"], **kw)
+
+    order = ("fp8r", "nvfp4", "svdq")
+    for _ in range(args.warmup):
+        for k in order:
+            run(k)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed region
+    ev = {k: [] for k in order}
+    qpl.timing_collect()  # drop anything recorded so far
+    qpl.timing_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        for k in order:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run(k)
+            b.record()
+            ev[k].append((a, b))
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    qpl.timing_enable(False)
+    kern = qpl.timing_collect()
+    log(f"timed {args.steps} steps in {t_total * 1e3:.1f} ms")
+
+    ms_step = t_total * 1e3 / args.steps
+    total_flops = sum(lin[k]["flops"] for k in order)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    parts = {}
+    for k in order:
+        ms = sum(a.elapsed_time(b) for a, b in ev[k]) / len(ev[k])
+        e = lin[k]
+        tf = e["flops"] / (ms * 1e-3) / 1e12
+        peak = "fp8" if k == "fp8r" else "fp4"
+        parts[k] = {"shape": [e["M"], e["K"], e["N"]] + ([e["R"]] if e["R"] else []), "ms": round(ms, 4),
+                    "tflops": round(tf, 1), f"pct_{peak}_peak": round(100 * tf / PEAK_TFLOPS[peak], 2)}
+        if k != "fp8r":
+            parts[k]["pct_bf16_peak"] = round(100 * tf / PEAK_TFLOPS["bf16"], 2)
+    kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for k, (n, t) in kern.items() if n}
+
+    # ---------------------------------------------------------------- roofline (dominant kernel)
+    n_g, t_g = kern["gemm_nvfp4"]
+    avg_s = t_g / n_g * 1e-3
+    e = lin["nvfp4"]
+    achieved = e["flops"] / avg_s / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"kernel": "gemm_nvfp4 (bf16 MFMA, 4608x3072x12288)", "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                "traffic": traffic, "avg_us": round(avg_s * 1e6, 2),
+                "frac_of_fp4_peak": round(achieved / PEAK_TFLOPS["fp4"], 4)}
+    nq, tq = kern["quant_fp8_row"]
+    qbytes = 3.0 * lin["fp8r"]["M"] * lin["fp8r"]["K"] + 4.0 * lin["fp8r"]["M"]
+    quant_gbs = qbytes / (tq / nq * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(lin, args.cpu_rows)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e4m3/e2m1 operands, fp32 accumulate, bf16 out", "data": "synthetic",
+        "config": {"workload": "dit_linear_m4608: fp8r 4608x3072x12288 + nvfp4 4608x3072x12288 + "
+                               "svdq nvfp4 4608x3072x3072 r32",
+                   "global_batch": 4608, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "parts": parts,
+        "kernels": kernels,
+        "quant_fp8_row_gbs": round(quant_gbs, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(lin, rows):
+    """The oracle, as written, on `rows` activation rows of each linear: activation
+    quantize, dequantize both operands, float64 matmul (plus the low-rank term)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.quant import amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4
+    from oracle.reference import dequant_fp8r, dequant_nvfp4, lowrank_ref
+    from synthetic import calibration_batches
+
+    prep = {}
+    for k, e in lin.items():
+        h = e["host"]
+        if k == "fp8r":
+            prep[k] = quant_fp8_row(h["w"])
+        else:
+            g_w = global_scale(amax_bf16(h["w"]))
+            name = "nvfp4_dit" if k == "nvfp4" else "svdq_w4a4"
+            g_in = calibrate_input_scale(calibration_batches(name))
+            prep[k] = quant_nvfp4(h["w"], g_w) + (g_w, g_in)
+    flops = 0.0
+    t0 = time.perf_counter()
+    for k, e in lin.items():
+        h = e["host"]
+        x = h["x"][:rows]
+        if k == "fp8r":
+            wq, ws = prep[k]
+            xq, xs = quant_fp8_row(x)
+            y = dequant_fp8r(xq, xs) @ dequant_fp8r(wq, ws).T
+        else:
+            wq, wbs, g_w, g_in = prep[k]
+            xq, xbs = quant_nvfp4(x, g_in)
+            y = dequant_nvfp4(xq, xbs, g_in) @ dequant_nvfp4(wq, wbs, g_w).T
+            if e["R"]:
+                y = y + lowrank_ref(x, h["l1"], h["l2"])
+        flops += 2.0 * rows * e["N"] * e["K"]
+        del y
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} activation rows of each of the 3 linears (full weights), {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * qpl.h - C ABI of the MI355X (gfx950) quantized linear library (libqpl.so).
+ *
+ * The operations are those of the two checkpoint schemes in the Diffusers guide
+ * "BFL (fp8r / nvfp4)" (intro bullets and the "Kernels" section), plus the
+ * low-rank branch of SVDQuant ("Bringing Nunchaku 4-bit Diffusion Inference to
+ * Diffusers", section "Background: SVDQuant and Nunchaku").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major, in device memory owned by the caller.  The
+ *   library allocates nothing and keeps no pointer after a call returns.
+ * - bf16 values travel as their 16-bit patterns (uint16_t).
+ * - E4M3 is the OCP FP8 E4M3 encoding (bias 7, largest finite 448, NaN only at
+ *   S.1111.111, no infinity).  E2M1 is the OCP MX FP4 element type (magnitudes
+ *   0, 0.5, 1, 1.5, 2, 3, 4, 6).  Encoders round to nearest even, saturate at the
+ *   largest finite magnitude and keep the sign of zero.
+ * - A linear is y[M,N] = x[M,K] * W[N,K]^T (the nn.Linear layout).
+ * - Packed E2M1: byte j of a row holds element 2j in its low nibble and element
+ *   2j+1 in its high nibble.  Block scales are row-major [rows, K/16].
+ * - `stream` is a hipStream_t (NULL = the default stream).  Work is queued on it
+ *   and the call returns without waiting; no entry point synchronizes the host.
+ * - Arguments are checked on the host before anything is queued; a bad argument
+ *   returns a non-zero status and touches no memory.  Checks: non-NULL pointers,
+ *   16-byte aligned pointers, M, N >= 1, K >= 16 and K % 16 == 0, scalars finite
+ *   and > 0, workspace large enough, and a current HIP device that is gfx950.
+ * - Inputs must be finite: NaN or infinity in x or W is outside the contract.
+ * - Faults inside a kernel surface at the caller's next synchronization.
+ */
+#ifndef QPL_H
+#define QPL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QPL_OK = 0,
+  QPL_ERR_NULL = 1,      /* a required pointer is NULL */
+  QPL_ERR_SHAPE = 2,     /* M or N < 1, K < 16, K % 16 != 0, R outside [0, 128], or a size overflows */
+  QPL_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  QPL_ERR_ARG = 4,       /* a scale is not finite and > 0, unknown scheme, or low-rank pointers inconsistent with R */
+  QPL_ERR_WORKSPACE = 5, /* ws_bytes < qlinear_workspace_bytes(...) */
+  QPL_ERR_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */
+  QPL_ERR_LAUNCH = 7     /* the HIP runtime rejected a kernel launch */
+} qpl_status;
+
+typedef enum { QPL_FP8R = 0, QPL_NVFP4 = 1 } qpl_scheme;
+
+/*
+ * Row-wise FP8 quantization (guide "BFL (fp8r / nvfp4)", intro bullet on fp8r:
+ * activations are quantized per row to E4M3 at run time).  The same routine
+ * quantizes a weight [N,K] into `weight` / `weight_scale`.
+ *   x        bf16 [M,K]            input
+ *   x_q      uint8 E4M3 [M,K]      out: codes, E4M3(x / s[m]) with a correctly
+ *                                  rounded fp32 division
+ *   x_scale  float [M]             out: s[m] = max_k |x[m,k]| / 448 (fp32); an
+ *                                  all-zero row gives s = 0 and signed-zero codes
+ */
+qpl_status quant_act_fp8_row(const uint16_t* x, int64_t M, int64_t K,
+                             uint8_t* x_q, float* x_scale, void* stream);
+
+/*
+ * NVFP4 quantization under a global scale g (guide, intro bullet on nvfp4: packed
+ * E2M1 values with an E4M3 scale per 16 elements and a calibrated fp32
+ * `input_scale`).  With g = weight_scale_2 the same routine quantizes a weight.
+ * Per 16-element block: sf = E4M3(bmax / (6 g)), d = dec(sf) * g (fp32),
+ * codes E2M1(x / d) (signed zeros when d == 0).
+ *   x              bf16 [M,K]                  input
+ *   input_scale    g, finite and > 0
+ *   x_q            uint8 [M,K/2]               out: packed E2M1 codes
+ *   x_block_scale  uint8 E4M3 [M,K/16]         out: block scales
+ */
+qpl_status quant_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, float input_scale,
+                           uint8_t* x_q, uint8_t* x_block_scale, void* stream);
+
+/*
+ * fp8r linear (guide, "Kernels" table, fp8r row: a row-wise scaled FP8 GEMM):
+ *   y[m,n] = bf16_rne( sum_k dec(xq[m,k]) dec(w[n,k]) * s_x[m] * weight_scale[n] )
+ * with xq, s_x from quant_act_fp8_row(x), fp32 accumulation.
+ *   weight        uint8 E4M3 [N,K]
+ *   weight_scale  float [N]
+ *   y             bf16 [M,N]          out
+ *   ws, ws_bytes  scratch of at least qlinear_workspace_bytes(QPL_FP8R, M, K, N, 0)
+ */
+qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                        const uint8_t* weight, const float* weight_scale,
+                        uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4 linear (guide, "Kernels" table, nvfp4 row: an activation quantize followed
+ * by a block-scaled FP4 GEMM), optionally with the SVDQuant low-rank branch:
+ *   y = bf16_rne( input_scale * weight_scale_2 *
+ *                 sum_b sx[m,b] sw[n,b] sum_{k in b} e2m1(xq) e2m1(w)  +  (x L1) L2 )
+ * where xq, sx come from quant_act_nvfp4(x, input_scale) and the low-rank term is
+ * accumulated in fp32 before the single rounding to bf16.
+ *   weight          uint8 [N,K/2]        packed E2M1
+ *   weight_scale    uint8 E4M3 [N,K/16]
+ *   weight_scale_2  global weight scale, finite and > 0
+ *   input_scale     calibrated activation scale, finite and > 0
+ *   lora_down       bf16 [K,R] (L1) or NULL when R == 0
+ *   lora_up         bf16 [R,N] (L2) or NULL when R == 0
+ *   R               rank, 0..128
+ *   y               bf16 [M,N]          out
+ *   ws, ws_bytes    scratch of at least qlinear_workspace_bytes(QPL_NVFP4, M, K, N, R)
+ */
+qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                         const uint8_t* weight, const uint8_t* weight_scale,
+                         float weight_scale_2, float input_scale,
+                         const uint16_t* lora_down, const uint16_t* lora_up, int64_t R,
+                         uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dequantize a weight to bf16 (guide, "Kernels" section, last paragraph: on other
+ * devices the weight is dequantized to compute_dtype on every forward and the
+ * layer runs as a regular linear; that linear is the caller's).
+ *   QPL_FP8R:  weight uint8 E4M3 [N,K], weight_scale float [N];
+ *              w[n,k] = bf16_rne(dec(w) * s[n])
+ *   QPL_NVFP4: weight uint8 [N,K/2] packed E2M1, weight_scale uint8 E4M3 [N,K/16];
+ *              w[n,k] = bf16_rne((e2m1(w) * dec(sf)) * weight_scale_2)
+ *   weight_scale_2 is ignored for QPL_FP8R.
+ *   w_bf16  bf16 [N,K]  out
+ */
+qpl_status dequant_weight(qpl_scheme scheme, const uint8_t* weight, const void* weight_scale,
+                          float weight_scale_2, int64_t N, int64_t K,
+                          uint16_t* w_bf16, void* stream);
+
+/* Bytes of scratch that qlinear_fp8r / qlinear_nvfp4 need for these sizes
+ * (0 if the sizes are invalid).  The scratch may be reused between calls that
+ * are ordered on one stream. */
+size_t qlinear_workspace_bytes(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R);
+
+/*
+ * Calibration helper for the nvfp4 global scales (guide, intro bullet on nvfp4:
+ * `weight_scale_2` and the calibrated `input_scale`).
+ *   qpl_amax_bf16: *amax (device float) = max(*amax, max_i |x[i]|) over n >= 1
+ *                  bf16 values; the caller sets *amax to 0 before the first batch.
+ *                  x needs 16-byte alignment; amax needs 4-byte alignment.
+ *   qpl_nvfp4_global_scale: amax / (448 * 6) in fp32 (host function).
+ */
+qpl_status qpl_amax_bf16(const uint16_t* x, int64_t n, float* amax, void* stream);
+float qpl_nvfp4_global_scale(float amax);
+
+/*
+ * Per-kernel timing (a profiling aid, off by default).  While enabled, every kernel
+ * launch of the library is bracketed by two HIP events recorded on the launch's
+ * stream.  qpl_timing_collect waits for all recorded events, writes per kernel
+ * kind the number of launches and their summed duration in milliseconds since
+ * the previous collect (arrays of QPL_KERNEL_COUNT entries, caller-owned host
+ * memory), and clears the records.  Events are created by the library on first
+ * use and reused.  Not thread-safe with respect to concurrent collect calls.
+ */
+typedef enum {
+  QPL_KERNEL_QUANT_FP8_ROW = 0,     /* fp8r activation / weight quantize */
+  QPL_KERNEL_QUANT_NVFP4 = 1,       /* nvfp4 quantize to packed codes */
+  QPL_KERNEL_QUANT_NVFP4_BF16 = 2,  /* nvfp4 quantize inside qlinear_nvfp4 (bf16 output) */
+  QPL_KERNEL_GEMM_FP8R = 3,
+  QPL_KERNEL_GEMM_NVFP4 = 4,
+  QPL_KERNEL_GEMM_NVFP4_LOWRANK = 5, /* nvfp4 GEMM with the low-rank epilogue */
+  QPL_KERNEL_LOWRANK_PREP = 6,      /* x L1 and the factor transposes */
+  QPL_KERNEL_DEQUANT = 7,
+  QPL_KERNEL_AMAX = 8,
+  QPL_KERNEL_COUNT = 9
+} qpl_kernel;
+
+void qpl_timing_enable(int on);
+qpl_status qpl_timing_collect(int64_t* launches, double* total_ms);
+
+/* Static description of a status code. */
+const char* qpl_status_str(qpl_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QPL_H */

@@ -98,12 +98,14 @@ def gemm_gamma(K):
     return math.ceil(K / 16) * 2.0 ** -24
 
 
-def check_gemm(y_bits, ref, abs_sum, K, extra_abs=None, max_ulps=4.0, frob_tol=2e-3):
+def check_gemm(y_bits, ref, abs_sum, K, extra_abs=None, max_ulps=4.0, frob_tol=2e-3, gamma=None):
     """Acceptance test of a bf16 GEMM output against its float64 reference.
 
     * relative Frobenius error ||y - ref|| / ||ref|| <= frob_tol over the whole output;
-    * per element |y - ref| <= max_ulps * ulp_bf16(ref) + gamma(K) * sum_k |a_k w_k|
-      (plus gamma * the low-rank magnitude sum when given).
+    * per element |y - ref| <= max_ulps * ulp_bf16(ref) + gamma * sum_k |a_k w_k|
+      (plus gamma * the low-rank magnitude sum when given).  ``gamma`` is the
+      accumulation floor of the arithmetic under test; it defaults to the fp32
+      floor ``gemm_gamma(K)``.
 
     Returns a dict with the figures and a boolean ``ok``.
     """
@@ -113,7 +115,8 @@ def check_gemm(y_bits, ref, abs_sum, K, extra_abs=None, max_ulps=4.0, frob_tol=2
     den = np.linalg.norm(ref)
     frob = float(np.linalg.norm(y - ref) / den) if den > 0 else float(np.linalg.norm(y))
     ulp = ulp_bf16(ref)
-    floor = gemm_gamma(K) * np.asarray(abs_sum, dtype=np.float64)
+    g = gemm_gamma(K) if gamma is None else gamma
+    floor = g * np.asarray(abs_sum, dtype=np.float64)
     if extra_abs is not None:
         floor = floor + gemm_gamma(K) * np.asarray(extra_abs, dtype=np.float64)
     bound = max_ulps * ulp + floor

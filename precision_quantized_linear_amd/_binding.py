@@ -1,0 +1,198 @@
+"""ctypes binding of libqpl.so: argument marshalling only.
+
+Every call forwards raw device pointers, sizes and the current HIP stream to the
+C ABI declared in include/qpl.h; all arithmetic runs in the library's gfx950
+kernels.  torch is used for device memory and streams only.  There is no CPU
+fallback: a missing library or a non-OK status raises.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqpl.so")
+
+QPL_FP8R = 0
+QPL_NVFP4 = 1
+
+EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp4", "dequant_weight",
+           "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
+           "qpl_timing_enable", "qpl_timing_collect")
+
+# qpl_kernel order of include/qpl.h
+KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_bf16", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
+           "lowrank_prep", "dequant", "amax")
+
+_lib = None
+
+
+class QPLError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libqpl.so (once) and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m precision_quantized_linear_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "quant_act_fp8_row": [P, I64, I64, P, P, P],
+        "quant_act_nvfp4": [P, I64, I64, F, P, P, P],
+        "qlinear_fp8r": [P, I64, I64, I64, P, P, P, P, SZ, P],
+        "qlinear_nvfp4": [P, I64, I64, I64, P, P, F, F, P, P, I64, P, P, SZ, P],
+        "dequant_weight": [ctypes.c_int, P, P, F, I64, I64, P, P],
+        "qpl_amax_bf16": [P, I64, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.qlinear_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64, I64]
+    lib.qlinear_workspace_bytes.restype = SZ
+    lib.qpl_nvfp4_global_scale.argtypes = [F]
+    lib.qpl_nvfp4_global_scale.restype = F
+    lib.qpl_status_str.argtypes = [ctypes.c_int]
+    lib.qpl_status_str.restype = ctypes.c_char_p
+    lib.qpl_timing_enable.argtypes = [ctypes.c_int]
+    lib.qpl_timing_enable.restype = None
+    lib.qpl_timing_collect.argtypes = [P, P]
+    lib.qpl_timing_collect.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise QPLError(fn, status, load().qpl_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on a GPU, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+
+
+def _bits(t):
+    """bf16 tensor -> same storage viewed as int16 (the C ABI takes the bit patterns)."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def quant_act_fp8_row(x, x_q=None, x_scale=None, stream=None):
+    """bf16 [M,K] -> (E4M3 codes uint8 [M,K], fp32 row scales [M])."""
+    M, K = x.shape
+    _expect(x, torch.bfloat16, (M, K), "x")
+    x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if x_q is None else x_q
+    x_scale = torch.empty((M,), dtype=torch.float32, device=x.device) if x_scale is None else x_scale
+    _check("quant_act_fp8_row", load().quant_act_fp8_row(_ptr(x), M, K, _ptr(x_q), _ptr(x_scale), _stream(stream)))
+    return x_q, x_scale
+
+
+def quant_act_nvfp4(x, input_scale, x_q=None, x_block_scale=None, stream=None):
+    """bf16 [M,K] -> (packed E2M1 uint8 [M,K/2], E4M3 block scales uint8 [M,K/16])."""
+    M, K = x.shape
+    _expect(x, torch.bfloat16, (M, K), "x")
+    x_q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device) if x_q is None else x_q
+    x_block_scale = (torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+                     if x_block_scale is None else x_block_scale)
+    _check("quant_act_nvfp4", load().quant_act_nvfp4(_ptr(x), M, K, float(input_scale), _ptr(x_q),
+                                                      _ptr(x_block_scale), _stream(stream)))
+    return x_q, x_block_scale
+
+
+def qlinear_workspace_bytes(scheme, M, K, N, R=0):
+    return int(load().qlinear_workspace_bytes(scheme, M, K, N, R))
+
+
+def _workspace(scheme, M, K, N, R, ws, device):
+    need = qlinear_workspace_bytes(scheme, M, K, N, R)
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def qlinear_fp8r(x, weight, weight_scale, y=None, workspace=None, stream=None):
+    """y[M,N] bf16 = fp8r linear of bf16 x [M,K] with E4M3 weight [N,K] and fp32 weight_scale [N]."""
+    M, K = x.shape
+    N = weight.shape[0]
+    _expect(x, torch.bfloat16, (M, K), "x")
+    _expect(weight, torch.uint8, (N, K), "weight")
+    _expect(weight_scale, torch.float32, (N,), "weight_scale")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    ws, nbytes = _workspace(QPL_FP8R, M, K, N, 0, workspace, x.device)
+    _check("qlinear_fp8r", load().qlinear_fp8r(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale), _ptr(y),
+                                               _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_down=None, lora_up=None, y=None,
+                  workspace=None, stream=None):
+    """y[M,N] bf16 = nvfp4 linear (+ (x L1) L2 when lora_down [K,R] / lora_up [R,N] are given)."""
+    M, K = x.shape
+    N = weight.shape[0]
+    _expect(x, torch.bfloat16, (M, K), "x")
+    _expect(weight, torch.uint8, (N, K // 2), "weight")
+    _expect(weight_scale, torch.uint8, (N, K // 16), "weight_scale")
+    R = 0
+    if lora_down is not None:
+        R = lora_down.shape[1]
+        _expect(lora_down, torch.bfloat16, (K, R), "lora_down")
+        _expect(lora_up, torch.bfloat16, (R, N), "lora_up")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    ws, nbytes = _workspace(QPL_NVFP4, M, K, N, R, workspace, x.device)
+    _check("qlinear_nvfp4", load().qlinear_nvfp4(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale),
+                                                 float(weight_scale_2), float(input_scale), _ptr(lora_down),
+                                                 _ptr(lora_up), R, _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def dequant_weight(scheme, weight, weight_scale, weight_scale_2=1.0, K=None, out=None, stream=None):
+    """Dequantize an fp8r or nvfp4 weight to bf16 [N,K]."""
+    N = weight.shape[0]
+    if K is None:
+        K = weight.shape[1] * (2 if scheme == QPL_NVFP4 else 1)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=weight.device) if out is None else out
+    _check("dequant_weight", load().dequant_weight(scheme, _ptr(weight), _ptr(weight_scale), float(weight_scale_2),
+                                                   N, K, _ptr(out), _stream(stream)))
+    return out
+
+
+def amax_bf16(x, amax=None, stream=None):
+    """Running max |x| into a device float32 [1] (initialised to 0 when not given)."""
+    amax = torch.zeros((1,), dtype=torch.float32, device=x.device) if amax is None else amax
+    _check("qpl_amax_bf16", load().qpl_amax_bf16(_ptr(x), x.numel(), _ptr(amax), _stream(stream)))
+    return amax
+
+
+def nvfp4_global_scale(amax):
+    """amax / (448 * 6) in fp32 (host)."""
+    return float(load().qpl_nvfp4_global_scale(float(amax)))
+
+
+def timing_enable(on=True):
+    """Bracket every library kernel launch with HIP events (profiling aid)."""
+    load().qpl_timing_enable(1 if on else 0)
+
+
+def timing_collect():
+    """Wait for the recorded events; return {kernel: (launches, total_ms)} and clear."""
+    n = len(KERNELS)
+    launches = (ctypes.c_int64 * n)()
+    total = (ctypes.c_double * n)()
+    _check("qpl_timing_collect", load().qpl_timing_collect(ctypes.cast(launches, ctypes.c_void_p),
+                                                           ctypes.cast(total, ctypes.c_void_p)))
+    return {k: (int(launches[i]), float(total[i])) for i, k in enumerate(KERNELS)}

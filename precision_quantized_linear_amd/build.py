@@ -1,0 +1,56 @@
+"""Build libqpl.so for gfx950 with hipcc (cross-compiles; no GPU needed).
+
+Every HIP source under csrc/ is compiled to an object in _build/ and linked into
+precision_quantized_linear_amd/libqpl.so.  Flags that matter for the numerics:
+correctly rounded fp32 division, no floating-point contraction, no fast-math,
+denormals kept; packed-fp32 instructions are disabled.
+
+    python -m precision_quantized_linear_amd.build
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libqpl.so")
+SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "qpl_api.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+CFLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 target feature; that warning is harmless
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed: {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
+    cmds = [[HIPCC, *CFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+        for err in ex.map(_run, cmds):
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

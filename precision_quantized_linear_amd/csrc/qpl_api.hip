@@ -1,0 +1,317 @@
+// C ABI of libqpl.so (declared in include/qpl.h): argument checks on the host,
+// workspace carving and kernel launches on the caller's stream.  No entry point
+// allocates memory, synchronizes, or lets a C++ exception cross the boundary.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "qpl.h"
+#include "qpl_internal.h"
+
+#define QPL_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;    // rows, columns and K each below 2^31
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // any operand below 2^40 elements
+constexpr int64_t kMaxRank = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool positive_finite(float v) { return std::isfinite(v) && v > 0.0f; }
+
+qpl_status check_dims(int64_t M, int64_t K) {
+  if (M < 1 || K < 16 || K % 16 != 0 || M >= kMaxDim || K >= kMaxDim) return QPL_ERR_SHAPE;
+  if (M > kMaxElems / K) return QPL_ERR_SHAPE;
+  return QPL_OK;
+}
+
+qpl_status check_gemm_dims(int64_t M, int64_t K, int64_t N) {
+  qpl_status s = check_dims(M, K);
+  if (s != QPL_OK) return s;
+  if (N < 1 || N >= kMaxDim || N > kMaxElems / K || M > kMaxElems / N) return QPL_ERR_SHAPE;
+  return QPL_OK;
+}
+
+// The current device must be a gfx950; the answer is cached per device ordinal.
+std::atomic<int> g_device_state[64];
+
+qpl_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return QPL_ERR_DEVICE;
+  }
+  const int st = g_device_state[dev].load(std::memory_order_relaxed);
+  if (st == 1) return QPL_OK;
+  if (st == 2) return QPL_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  bool ok = false;
+  if (hipGetDeviceProperties(&prop, dev) == hipSuccess) ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  (void)hipGetLastError();
+  g_device_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? QPL_OK : QPL_ERR_DEVICE;
+}
+
+qpl_status launched(hipError_t e) { return e == hipSuccess ? QPL_OK : QPL_ERR_LAUNCH; }
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+int64_t rank_pad(int64_t R) { return (R + 31) / 32 * 32; }
+
+// Workspace layout.  fp8r: [xq: M*K bytes][xs: 4*M bytes].  nvfp4: [xe: 2*M*K
+// bytes (bf16 expanded activations)] then, when R > 0, [l1t: 2*rpad*K][t: 2*M*KL]
+// [l2t: 2*N*KL] with rpad = 32*ceil(R/32) and KL = 2*rpad.  Each part is rounded
+// up to 256 bytes.
+struct Layout {
+  size_t off[4] = {0, 0, 0, 0};
+  size_t total = 0;
+};
+
+Layout layout(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R) {
+  Layout L;
+  size_t parts[4] = {0, 0, 0, 0};
+  if (scheme == QPL_FP8R) {
+    parts[0] = size_t(M) * size_t(K);
+    parts[1] = size_t(4) * size_t(M);
+  } else {
+    parts[0] = size_t(2) * size_t(M) * size_t(K);
+    if (R > 0) {
+      const int64_t rp = rank_pad(R), kl = 2 * rp;
+      parts[1] = size_t(2) * size_t(rp) * size_t(K);
+      parts[2] = size_t(2) * size_t(M) * size_t(kl);
+      parts[3] = size_t(2) * size_t(N) * size_t(kl);
+    }
+  }
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) {
+    L.off[i] = o;
+    o += round256(parts[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+// ---- per-kernel timing -------------------------------------------------------
+std::atomic<bool> g_timing{false};
+std::mutex g_tmu;
+struct TimingRec {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+// Records an event before the launch and one after it when timing is on.
+class Timed {
+ public:
+  Timed(qpl_kernel kind, hipStream_t s) : kind_(kind), s_(s) {
+    if (!g_timing.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    start_ = take_event();
+    if (start_ && hipEventRecord(start_, s_) != hipSuccess) {
+      (void)hipGetLastError();
+      g_pool.push_back(start_);
+      start_ = nullptr;
+    }
+  }
+  hipError_t operator()(hipError_t launch) {
+    if (!start_) return launch;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    hipEvent_t stop = take_event();
+    if (stop && hipEventRecord(stop, s_) == hipSuccess) {
+      g_recs.push_back({int(kind_), start_, stop});
+    } else {
+      (void)hipGetLastError();
+      g_pool.push_back(start_);
+      if (stop) g_pool.push_back(stop);
+    }
+    start_ = nullptr;
+    return launch;
+  }
+
+ private:
+  qpl_kernel kind_;
+  hipStream_t s_;
+  hipEvent_t start_ = nullptr;
+};
+
+}  // namespace
+
+QPL_EXPORT void qpl_timing_enable(int on) { g_timing.store(on != 0); }
+
+QPL_EXPORT qpl_status qpl_timing_collect(int64_t* launches, double* total_ms) {
+  if (!launches || !total_ms) return QPL_ERR_NULL;
+  for (int i = 0; i < QPL_KERNEL_COUNT; ++i) {
+    launches[i] = 0;
+    total_ms[i] = 0.0;
+  }
+  std::lock_guard<std::mutex> lk(g_tmu);
+  qpl_status st = QPL_OK;
+  for (const TimingRec& r : g_recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      (void)hipGetLastError();
+      st = QPL_ERR_DEVICE;
+    } else {
+      launches[r.kind] += 1;
+      total_ms[r.kind] += ms;
+    }
+    g_pool.push_back(r.start);
+    g_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  return st;
+}
+
+QPL_EXPORT const char* qpl_status_str(qpl_status status) {
+  switch (status) {
+    case QPL_OK: return "ok";
+    case QPL_ERR_NULL: return "a required pointer is NULL";
+    case QPL_ERR_SHAPE: return "invalid shape (need M, N >= 1, K >= 16, K % 16 == 0, 0 <= R <= 128, sizes in range)";
+    case QPL_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case QPL_ERR_ARG: return "invalid argument (scales must be finite and > 0; scheme; low-rank pointers vs R)";
+    case QPL_ERR_WORKSPACE: return "workspace too small";
+    case QPL_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+    case QPL_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+QPL_EXPORT float qpl_nvfp4_global_scale(float amax) { return amax / 2688.0f; }
+
+QPL_EXPORT size_t qlinear_workspace_bytes(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R) {
+  if (scheme != QPL_FP8R && scheme != QPL_NVFP4) return 0;
+  if (check_gemm_dims(M, K, N) != QPL_OK || R < 0 || R > kMaxRank) return 0;
+  if (scheme == QPL_FP8R && R != 0) return 0;
+  return layout(scheme, M, K, N, R).total;
+}
+
+QPL_EXPORT qpl_status quant_act_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* x_q, float* x_scale,
+                                        void* stream) {
+  if (!x || !x_q || !x_scale) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x_q) || !aligned16(x_scale)) return QPL_ERR_ALIGN;
+  qpl_status s = check_dims(M, K);
+  if (s != QPL_OK) return s;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(Timed(QPL_KERNEL_QUANT_FP8_ROW, st)(qpl::launch_quant_fp8_row(x, M, K, x_q, x_scale, st)));
+}
+
+QPL_EXPORT qpl_status quant_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, float input_scale, uint8_t* x_q,
+                                      uint8_t* x_block_scale, void* stream) {
+  if (!x || !x_q || !x_block_scale) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x_q) || !aligned16(x_block_scale)) return QPL_ERR_ALIGN;
+  qpl_status s = check_dims(M, K);
+  if (s != QPL_OK) return s;
+  if (!positive_finite(input_scale) || !positive_finite(6.0f * input_scale)) return QPL_ERR_ARG;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(
+      Timed(QPL_KERNEL_QUANT_NVFP4, st)(qpl::launch_quant_nvfp4(x, M, K, input_scale, x_q, x_block_scale, st)));
+}
+
+QPL_EXPORT qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                   const float* weight_scale, uint16_t* y, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!x || !weight || !weight_scale || !y || !ws) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws))
+    return QPL_ERR_ALIGN;
+  qpl_status s = check_gemm_dims(M, K, N);
+  if (s != QPL_OK) return s;
+  const Layout L = layout(QPL_FP8R, M, K, N, 0);
+  if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* xq = base + L.off[0];
+  float* xs = reinterpret_cast<float*>(base + L.off[1]);
+  if ((s = launched(Timed(QPL_KERNEL_QUANT_FP8_ROW, st)(qpl::launch_quant_fp8_row(x, M, K, xq, xs, st)))) != QPL_OK)
+    return s;
+  return launched(Timed(QPL_KERNEL_GEMM_FP8R, st)(qpl::launch_gemm_fp8r(xq, xs, weight, weight_scale, M, K, N, y, st)));
+}
+
+QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                    const uint8_t* weight_scale, float weight_scale_2, float input_scale,
+                                    const uint16_t* lora_down, const uint16_t* lora_up, int64_t R, uint16_t* y,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !weight || !weight_scale || !y || !ws) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws))
+    return QPL_ERR_ALIGN;
+  qpl_status s = check_gemm_dims(M, K, N);
+  if (s != QPL_OK) return s;
+  if (R < 0 || R > kMaxRank) return QPL_ERR_SHAPE;
+  if (R > 0 && (!lora_down || !lora_up)) return QPL_ERR_NULL;
+  if (R == 0 && (lora_down || lora_up)) return QPL_ERR_ARG;
+  if (R > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return QPL_ERR_ALIGN;
+  if (!positive_finite(weight_scale_2) || !positive_finite(input_scale) || !positive_finite(6.0f * input_scale))
+    return QPL_ERR_ARG;
+  const float gscale = input_scale * weight_scale_2;
+  if (!std::isfinite(gscale)) return QPL_ERR_ARG;
+  const Layout L = layout(QPL_NVFP4, M, K, N, R);
+  if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint16_t* xe = reinterpret_cast<uint16_t*>(base + L.off[0]);
+  if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, xe, st)))) !=
+      QPL_OK)
+    return s;
+  qpl::LowRank lr;
+  if (R > 0) {
+    const int64_t kl = 2 * rank_pad(R);
+    uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[1]);
+    uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[2]);
+    uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[3]);
+    if ((s = launched(Timed(QPL_KERNEL_LOWRANK_PREP, st)(
+             qpl::launch_lowrank_prep(x, lora_down, lora_up, M, K, N, R, kl, l1t, t, l2t, st)))) != QPL_OK)
+      return s;
+    lr.t = t;
+    lr.l2t = l2t;
+    lr.kl = kl;
+  }
+  return launched(Timed(R > 0 ? QPL_KERNEL_GEMM_NVFP4_LOWRANK : QPL_KERNEL_GEMM_NVFP4, st)(
+      qpl::launch_gemm_nvfp4(xe, weight, weight_scale, gscale, M, K, N, lr, y, st)));
+}
+
+QPL_EXPORT qpl_status dequant_weight(qpl_scheme scheme, const uint8_t* weight, const void* weight_scale,
+                                     float weight_scale_2, int64_t N, int64_t K, uint16_t* w_bf16, void* stream) {
+  if (scheme != QPL_FP8R && scheme != QPL_NVFP4) return QPL_ERR_ARG;
+  if (!weight || !weight_scale || !w_bf16) return QPL_ERR_NULL;
+  if (!aligned16(weight) || !aligned16(weight_scale) || !aligned16(w_bf16)) return QPL_ERR_ALIGN;
+  qpl_status s = check_dims(N, K);
+  if (s != QPL_OK) return s;
+  if (scheme == QPL_NVFP4 && !positive_finite(weight_scale_2)) return QPL_ERR_ARG;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Timed timed(QPL_KERNEL_DEQUANT, st);
+  if (scheme == QPL_FP8R)
+    return launched(timed(qpl::launch_dequant_fp8r(weight, static_cast<const float*>(weight_scale), N, K, w_bf16, st)));
+  return launched(timed(qpl::launch_dequant_nvfp4(weight, static_cast<const uint8_t*>(weight_scale), weight_scale_2,
+                                                  N, K, w_bf16, st)));
+}
+
+QPL_EXPORT qpl_status qpl_amax_bf16(const uint16_t* x, int64_t n, float* amax, void* stream) {
+  if (!x || !amax) return QPL_ERR_NULL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(amax) & 3u) != 0) return QPL_ERR_ALIGN;
+  if (n < 1 || n >= kMaxElems) return QPL_ERR_SHAPE;
+  qpl_status s = check_device();
+  if (s != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(Timed(QPL_KERNEL_AMAX, st)(qpl::launch_amax_bf16(x, n, amax, st)));
+}

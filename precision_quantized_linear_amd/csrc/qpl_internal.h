@@ -1,0 +1,43 @@
+// Launchers of the gfx950 kernels, called by the C ABI in qpl_api.hip after the
+// arguments have been checked.  Every launcher queues work on `stream` and returns
+// the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qpl {
+
+hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
+                                hipStream_t stream);
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, uint8_t* xq,
+                              uint8_t* xbs, hipStream_t stream);
+// nvfp4 quantization that writes each quantized value e2m1(q) * dec(sf) as bf16
+// (exact: at most 6 significant bits) instead of packed codes.
+hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, uint16_t* xe,
+                                     hipStream_t stream);
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
+hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
+                               hipStream_t stream);
+hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K,
+                                uint16_t* out, hipStream_t stream);
+
+hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws,
+                            int64_t M, int64_t K, int64_t N, uint16_t* y, hipStream_t stream);
+
+// Low-rank operands for the nvfp4 GEMM epilogue: t [M, KL] bf16 holds T = x L1 split
+// into hi and lo bf16 halves, l2t [N, KL] bf16 holds L2^T twice; KL = 2 * ceil(R/32) * 32.
+struct LowRank {
+  const uint16_t* t = nullptr;
+  const uint16_t* l2t = nullptr;
+  int64_t kl = 0;
+};
+
+hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint8_t* w, const uint8_t* wbs, float gscale,
+                             int64_t M, int64_t K, int64_t N, LowRank lr, uint16_t* y, hipStream_t stream);
+
+hipError_t launch_lowrank_prep(const uint16_t* x, const uint16_t* l1, const uint16_t* l2, int64_t M, int64_t K,
+                               int64_t N, int64_t R, int64_t kl, uint16_t* l1t, uint16_t* t, uint16_t* l2t,
+                               hipStream_t stream);
+
+}  // namespace qpl

@@ -1,0 +1,114 @@
+"""Host-side checks of libqpl.so that need no GPU: the library loads, exports every
+entry point include/qpl.h declares, and rejects bad arguments before touching a
+device (each status is forced from the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import precision_quantized_linear_amd as qpl
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qpl.h")
+OK, NULL, SHAPE, ALIGN, ARG, WORKSPACE, DEVICE, LAUNCH = range(8)
+P = ctypes.c_void_p
+A = P(1 << 20)  # aligned, never dereferenced: every call below fails validation first
+B = P(1 << 21)
+C = P(1 << 22)
+D = P(1 << 23)
+MIS = P((1 << 20) + 4)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qpl.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(qpl.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.qpl_status_str(s)
+    assert lib.qpl_status_str(99) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    M, K, N = 4608, 3072, 12288
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, M, K, N) == M * K + M * 4
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N) == 2 * M * K
+    r = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, 3072, 32)
+    assert r == 2 * M * K + 2 * 32 * K + 2 * M * 64 + 2 * 3072 * 64
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 24, 4) == 0      # K % 16 != 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 32, 4, 129) == 0  # rank too large
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, 4, 32, 4, 1) == 0     # fp8r has no low rank
+    assert qpl.qlinear_workspace_bytes(7, 4, 32, 4) == 0
+
+
+def test_global_scale(lib):
+    assert qpl.nvfp4_global_scale(2688.0) == 1.0
+    import numpy as np
+    assert qpl.nvfp4_global_scale(5.25) == float(np.float32(5.25) / np.float32(2688))
+
+
+def test_quant_validation(lib):
+    assert lib.quant_act_fp8_row(None, 4, 16, B, C, None) == NULL
+    assert lib.quant_act_fp8_row(MIS, 4, 16, B, C, None) == ALIGN
+    assert lib.quant_act_fp8_row(A, 0, 16, B, C, None) == SHAPE
+    assert lib.quant_act_fp8_row(A, 4, 24, B, C, None) == SHAPE
+    assert lib.quant_act_fp8_row(A, 4, 0, B, C, None) == SHAPE
+    assert lib.quant_act_nvfp4(A, 4, 32, 1.0, None, C, None) == NULL
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e38):
+        assert lib.quant_act_nvfp4(A, 4, 32, bad, B, C, None) == ARG, bad
+
+
+def test_qlinear_validation(lib):
+    ws = 1 << 30
+    assert lib.qlinear_fp8r(A, 4, 32, 8, B, C, D, None, ws, None) == NULL
+    assert lib.qlinear_fp8r(A, 4, 32, 0, B, C, D, A, ws, None) == SHAPE
+    assert lib.qlinear_fp8r(A, 4, 32, 8, B, C, D, A, 10, None) == WORKSPACE
+    assert lib.qlinear_fp8r(A, 4, 32, 8, B, MIS, D, A, ws, None) == ALIGN
+    args = (A, 4, 32, 8, B, C)
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, None, 0, D, A, 10, None) == WORKSPACE
+    assert lib.qlinear_nvfp4(*args, 0.0, 1.0, None, None, 0, D, A, ws, None) == ARG
+    assert lib.qlinear_nvfp4(*args, 1.0, float("nan"), None, None, 0, D, A, ws, None) == ARG
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, A, None, 4, D, A, ws, None) == NULL
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, A, B, 0, D, A, ws, None) == ARG
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, A, B, 200, D, A, ws, None) == SHAPE
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, MIS, B, 4, D, A, ws, None) == ALIGN
+    assert lib.dequant_weight(5, A, B, 1.0, 4, 32, C, None) == ARG
+    assert lib.dequant_weight(1, A, B, -1.0, 4, 32, C, None) == ARG
+    assert lib.dequant_weight(0, A, None, 1.0, 4, 32, C, None) == NULL
+    assert lib.qpl_amax_bf16(A, 0, B, None) == SHAPE
+    assert lib.qpl_amax_bf16(A, 10, P((1 << 21) + 2), None) == ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="forces the no-device status; a GPU is present")
+def test_no_device_status(lib):
+    assert lib.quant_act_fp8_row(A, 4, 16, B, C, None) == DEVICE
+    assert lib.qlinear_nvfp4(A, 4, 32, 8, B, C, 1.0, 1.0, None, None, 0, D, A, 1 << 30, None) == DEVICE
+
+
+def test_timing_collect_empty(lib):
+    qpl.timing_enable(False)
+    res = qpl.timing_collect()
+    assert set(res) == set(qpl.KERNELS) and all(v == (0, 0.0) for v in res.values())
+    assert lib.qpl_timing_collect(None, None) == NULL
+
+
+def test_binding_rejects_wrong_tensors():
+    x = torch.zeros((4, 32), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        qpl.quant_act_fp8_row(x)

@@ -1,0 +1,202 @@
+"""GPU parity of qlinear_fp8r / qlinear_nvfp4 (with and without the low-rank branch)
+against the oracle's float64 dequantize-then-multiply reference.
+
+Acceptance (written in oracle.reference.check_gemm): relative Frobenius error
+<= 2e-3 over the compared outputs, and per element |y - ref| <= 4 bf16 ulps of ref
+plus an accumulation floor gamma * sum_k |a_k w_k|:
+
+* nvfp4 runs on the bf16 MFMA, whose dot products behave like fp32 sums:
+  gamma = ceil(K/16) * 2^-24.
+* fp8r runs on the full-rate f8f6f4 MFMA, whose 64-product dot unit keeps a
+  limited number of bits below the largest product of a group (it does not sum
+  like IEEE fp32).  Its floor is FP8_MFMA_GAMMA + ceil(K/64) * 2^-24: twice the
+  largest per-instruction error measured on inputs spread over the whole E4M3
+  range (2.1e-4 of sum |a w|), plus fp32 accumulation across instructions.
+  test_fp8_mfma_accumulation_bound pins that bound through qlinear_fp8r.
+
+Small shapes compare every output; full-size workloads compare sampled rows (all
+columns), including the first and last rows of edge tiles."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import precision_quantized_linear_amd as qpl
+from helpers import bf16_bits, to_dev, to_dev_bf16
+from oracle.formats import bf16_bits_to_f32
+from oracle.quant import amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4
+from oracle.reference import (check_gemm, dequant_fp8r, dequant_nvfp4, lowrank_abs, lowrank_ref)
+from synthetic import calibration_batches, make
+
+pytestmark = pytest.mark.gpu
+
+FP8_MFMA_GAMMA = 2.0 ** -11
+
+
+def fp8_gamma(K):
+    return FP8_MFMA_GAMMA + math.ceil(K / 64) * 2.0 ** -24
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def sample_rows(M, n=64, seed=0):
+    fixed = [r for r in (0, 1, 31, 32, 255, 256, M - 1, M - 2) if 0 <= r < M]
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(M, size=n - len(fixed), replace=False)
+    return np.unique(np.concatenate([fixed, extra]))
+
+
+def fp8r_case(d, rows):
+    x, w = d["x"], d["w"]
+    K = x.shape[1]
+    xq, xs = quant_fp8_row(x[rows])
+    wq, ws = quant_fp8_row(w)
+    a, b = dequant_fp8r(xq, xs), dequant_fp8r(wq, ws)
+    ref, absum = a @ b.T, np.abs(a) @ np.abs(b).T
+    y = qpl.qlinear_fp8r(to_dev_bf16(x), to_dev(wq), to_dev(ws))
+    torch.cuda.synchronize()
+    return check_gemm(bf16_bits(y)[rows], ref, absum, K, gamma=fp8_gamma(K))
+
+
+def nvfp4_case(d, rows, g_in):
+    x, w = d["x"], d["w"]
+    K = x.shape[1]
+    g_w = global_scale(amax_bf16(w))
+    xp, xb = quant_nvfp4(x[rows], g_in)
+    wp, wb = quant_nvfp4(w, g_w)
+    a, b = dequant_nvfp4(xp, xb, g_in), dequant_nvfp4(wp, wb, g_w)
+    ref, absum = a @ b.T, np.abs(a) @ np.abs(b).T
+    extra = None
+    lora = {}
+    if "l1" in d:
+        ref = ref + lowrank_ref(x[rows], d["l1"], d["l2"])
+        extra = lowrank_abs(x[rows], d["l1"], d["l2"])
+        lora = dict(lora_down=to_dev_bf16(d["l1"]), lora_up=to_dev_bf16(d["l2"]))
+    y = qpl.qlinear_nvfp4(to_dev_bf16(x), to_dev(wp), to_dev(wb), g_w, g_in, **lora)
+    torch.cuda.synchronize()
+    return check_gemm(bf16_bits(y)[rows], ref, absum, K, extra_abs=extra)
+
+
+FP8R_SHAPES = [
+    ("fp8r_tiny", None, None, None),            # 64 x 256 x 512, all outputs
+    ("fp8r_dit_n3072", 300, 400, 520),          # ragged M, K (not a multiple of 128) and N
+    ("fp8r_dit_n3072", 512, 512, 512),          # whole tiles
+    ("fp8r_dit_n3072", 1, 16, 1),               # degenerate
+    ("fp8r_dit_n3072", 257, 272, 300),          # one row / column past a tile, N % 8 != 0
+]
+
+
+@pytest.mark.parametrize("name,M,K,N", FP8R_SHAPES)
+def test_qlinear_fp8r_small(name, M, K, N):
+    d = make(name, M=M, K=K, N=N)
+    say("qlinear_fp8r", name, d["M"], d["K"], d["N"])
+    r = fp8r_case(d, np.arange(d["M"]))
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("name", ["fp8r_dit_n3072", "fp8r_dit_n12288"])
+def test_qlinear_fp8r_full(name):
+    d = make(name)
+    say("qlinear_fp8r full", name, d["M"], d["K"], d["N"])
+    r = fp8r_case(d, sample_rows(d["M"]))
+    say(r)
+    assert r["ok"], r
+
+
+NVFP4_SHAPES = [
+    ("nvfp4_dit", 300, 400, 520),               # K % 64 != 0: byte-wise weight loads
+    ("nvfp4_dit", 512, 512, 512),
+    ("nvfp4_dit", 1, 16, 1),
+    ("nvfp4_mlp_down_cfg", 257, 1024, 300),
+    ("svdq_w4a4", 300, 448, 264),               # low-rank branch, ragged
+    ("svdq_w4a4", 256, 512, 256),
+]
+
+
+@pytest.mark.parametrize("name,M,K,N", NVFP4_SHAPES)
+def test_qlinear_nvfp4_small(name, M, K, N):
+    d = make(name, M=M, K=K, N=N)
+    g_in = calibrate_input_scale(calibration_batches(name, M=M, K=K))
+    say("qlinear_nvfp4", name, d["M"], d["K"], d["N"], "R", d.get("R", 0))
+    r = nvfp4_case(d, np.arange(d["M"]), g_in)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("name", ["nvfp4_dit", "nvfp4_mlp_down_cfg", "svdq_w4a4"])
+def test_qlinear_nvfp4_full(name):
+    d = make(name)
+    g_in = calibrate_input_scale(calibration_batches(name))
+    say("qlinear_nvfp4 full", name, d["M"], d["K"], d["N"], "R", d.get("R", 0))
+    r = nvfp4_case(d, sample_rows(d["M"]), g_in)
+    say(r)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("R", [1, 20, 64, 100])
+def test_qlinear_nvfp4_lowrank_ranks(R):
+    d = make("svdq_w4a4", M=130, K=256, N=200)
+    rng = np.random.default_rng(R)
+    from synthetic import bf16_round
+    d["l1"] = bf16_round((rng.standard_normal((256, R)) * 0.05).astype(np.float32))
+    d["l2"] = bf16_round((rng.standard_normal((R, 200)) * 0.05).astype(np.float32))
+    say("qlinear_nvfp4 rank", R)
+    r = nvfp4_case(d, np.arange(130), np.float32(0.01))
+    assert r["ok"], r
+
+
+def test_qlinear_one_hot_weight_fp8r():
+    # W row n is one-hot at k = n (code 1.0, scale 1): y[:, n] = bf16(dec(xq[:, n]) * s_x)
+    d = make("fp8r_tiny")
+    x = d["x"]
+    wq = np.zeros((64, 256), np.uint8)
+    wq[np.arange(64), np.arange(64)] = 0x38
+    ws = np.ones(64, np.float32)
+    y = qpl.qlinear_fp8r(to_dev_bf16(x), to_dev(wq), to_dev(ws))
+    torch.cuda.synchronize()
+    xq, xs = quant_fp8_row(x)
+    from oracle.formats import f32_to_bf16_bits
+    exp = f32_to_bf16_bits((dequant_fp8r(xq[:, :64], xs)).astype(np.float32))
+    assert np.array_equal(bf16_bits(y), exp)
+
+
+def test_qlinear_deterministic():
+    d = make("svdq_w4a4", M=256, K=512, N=256)
+    g_w = global_scale(amax_bf16(d["w"]))
+    wp, wb = quant_nvfp4(d["w"], g_w)
+    args = (to_dev_bf16(d["x"]), to_dev(wp), to_dev(wb), g_w, 0.01)
+    kw = dict(lora_down=to_dev_bf16(d["l1"]), lora_up=to_dev_bf16(d["l2"]))
+    y1 = bf16_bits(qpl.qlinear_nvfp4(*args, **kw))
+    y2 = bf16_bits(qpl.qlinear_nvfp4(*args, **kw))
+    assert np.array_equal(y1, y2)
+
+
+def test_fp8_mfma_accumulation_bound():
+    # Activations and weights are exact E4M3 values spread over the whole exponent
+    # range, with row amax 448 (so the row scale is 1 and the kernel's codes are the
+    # chosen values).  The per-element error of the product, relative to
+    # sum_k |a_k w_k|, must stay below FP8_MFMA_GAMMA; it also shows the floor is
+    # needed (the fp32 floor alone is exceeded).
+    from oracle.formats import e4m3_decode
+    rng = np.random.default_rng(17)
+    M, N, K = 256, 256, 64
+    codes = rng.integers(0, 0x7F, (M + N, K)).astype(np.uint8) | (rng.integers(0, 2, (M + N, K)).astype(np.uint8) << 7)
+    codes[:, 0] = 0x7E                      # every row holds 448, so its scale is exactly 1
+    vals = e4m3_decode(codes)
+    from synthetic import bf16_round
+    xa = bf16_round(vals[:M].astype(np.float32))
+    wq = codes[M:]
+    y = qpl.qlinear_fp8r(to_dev_bf16(xa), to_dev(wq), to_dev(np.ones(N, np.float32)))
+    torch.cuda.synchronize()
+    a, b = vals[:M], vals[M:]
+    ref, absum = a @ b.T, np.abs(a) @ np.abs(b).T
+    yb = bf16_bits_to_f32(bf16_bits(y)).astype(np.float64)
+    from oracle.reference import ulp_bf16
+    excess = np.maximum(np.abs(yb - ref) - 4 * ulp_bf16(ref), 0) / absum
+    say("fp8 MFMA excess error / sum|aw|: max", excess.max())
+    assert excess.max() <= FP8_MFMA_GAMMA

@@ -1,0 +1,165 @@
+"""GPU parity of the quantizers, the dequant fallback and the amax helper against the
+oracle: bit-exact codes and scales (integer/byte outputs)."""
+import numpy as np
+import pytest
+import torch
+
+import precision_quantized_linear_amd as qpl
+from helpers import adversarial_rows, bf16_bits, host, to_dev, to_dev_bf16
+from oracle.formats import bf16_bits_to_f32
+from oracle.quant import amax_bf16, global_scale, quant_fp8_row, quant_nvfp4
+from oracle.reference import dequant_weight_fp8r, dequant_weight_nvfp4
+from synthetic import bf16_round, make
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_fp8_row(bits):
+    q, s = qpl.quant_act_fp8_row(to_dev_bf16(bits))
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+def gpu_nvfp4(bits, g):
+    q, s = qpl.quant_act_nvfp4(to_dev_bf16(bits), g)
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+def assert_fp8_equal(bits):
+    cq, cs = quant_fp8_row(bits)
+    gq, gs = gpu_fp8_row(bits)
+    assert np.array_equal(gs.view(np.uint32), cs.view(np.uint32)), "row scales differ"
+    bad = np.argwhere(gq != cq)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}: gpu {gq[tuple(bad[0])]:#x} oracle {cq[tuple(bad[0])]:#x}"
+
+
+def assert_nvfp4_equal(bits, g):
+    cq, cs = quant_nvfp4(bits, g)
+    gq, gs = gpu_nvfp4(bits, g)
+    assert np.array_equal(gs, cs), f"{np.count_nonzero(gs != cs)} block scales differ"
+    bad = np.argwhere(gq != cq)
+    assert bad.size == 0, f"{len(bad)} code bytes differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("name,M,K", [
+    ("fp8r_tiny", None, None),                 # 64 x 256
+    ("fp8r_dit_n3072", None, None),            # 4608 x 3072, full size
+    ("fp8r_dit_n3072", 300, 400),              # ragged: K not a multiple of 128
+    ("fp8r_dit_n3072", 1, 16),                 # smallest legal shape
+    ("fp8r_dit_n3072", 7, 12288),              # long rows held in registers
+    ("fp8r_dit_n3072", 3, 16400),              # rows too long for registers: two-pass path
+])
+def test_quant_fp8_row_activations(name, M, K):
+    d = make(name, M=M, K=K)
+    say("quant_act_fp8_row", name, d["x"].shape)
+    assert_fp8_equal(d["x"])
+
+
+@pytest.mark.parametrize("name", ["fp8r_tiny", "fp8r_dit_n12288"])
+def test_quant_fp8_row_weights(name):
+    w = make(name, M=8)["w"]
+    say("quant_act_fp8_row weight", name, w.shape)
+    assert_fp8_equal(w)
+
+
+@pytest.mark.parametrize("K", [16, 256, 3072])
+def test_quant_fp8_row_adversarial(K):
+    say("quant_act_fp8_row adversarial", K)
+    assert_fp8_equal(adversarial_rows(K, seed=K))
+
+
+def test_quant_fp8_row_exact_ties():
+    # rows with amax 448 * 2^j: s = 2^j and bf16 values on E4M3 midpoints are exact ties
+    from oracle.formats import e4m3_decode
+    pos = e4m3_decode(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2
+    rows = []
+    for j in (-4, 0, 3):
+        v = np.ldexp(mids, j)
+        v = v[np.abs(v) < 448 * 2.0 ** j]
+        row = np.concatenate([[448 * 2.0 ** j], v, -v]).astype(np.float32)
+        b = bf16_round(row)
+        b = b[bf16_bits_to_f32(b) == row]
+        rows.append(np.resize(b, 256))
+    say("quant_act_fp8_row ties")
+    assert_fp8_equal(np.stack(rows))
+
+
+@pytest.mark.parametrize("name,M,K", [
+    ("nvfp4_dit", None, None),                     # 4608 x 3072
+    ("nvfp4_mlp_down_cfg", None, None),            # 9216 x 12288, heavy tails: saturation
+    ("svdq_w4a4", 300, 400),                       # ragged
+    ("nvfp4_dit", 1, 16),
+])
+def test_quant_nvfp4_activations(name, M, K):
+    from synthetic import calibration_batches
+    from oracle.quant import calibrate_input_scale
+    d = make(name, M=M, K=K)
+    g = calibrate_input_scale(calibration_batches(name, M=M, K=K))
+    say("quant_act_nvfp4", name, d["x"].shape, "input_scale", g)
+    assert_nvfp4_equal(d["x"], g)
+
+
+@pytest.mark.parametrize("name", ["nvfp4_dit", "nvfp4_mlp_down_cfg", "svdq_w4a4"])
+def test_quant_nvfp4_weights(name):
+    w = make(name, M=8)["w"]
+    g = global_scale(amax_bf16(w))
+    say("quant_act_nvfp4 weight", name, w.shape, g)
+    assert_nvfp4_equal(w, g)
+
+
+@pytest.mark.parametrize("g", [1e-4, 0.01, 0.25, 3.0, 1e6])
+def test_quant_nvfp4_adversarial(g):
+    # small g saturates block scales at 448; huge g underflows them to 0 (signed-zero codes)
+    say("quant_act_nvfp4 adversarial", g)
+    assert_nvfp4_equal(adversarial_rows(256, seed=5), np.float32(g))
+
+
+def test_quant_nvfp4_exact_ties():
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    row = np.array([6.0] + ties + [-t for t in ties] + [0.0], dtype=np.float32)
+    bits = np.tile(bf16_round(row), (4, 4))
+    say("quant_act_nvfp4 ties")
+    assert_nvfp4_equal(bits, np.float32(0.25))
+
+
+def test_dequant_weight_fp8r():
+    w = make("fp8r_dit_n12288", M=8, K=1024, N=333)["w"]
+    wq, ws = quant_fp8_row(w)
+    say("dequant_weight fp8r", wq.shape)
+    out = qpl.dequant_weight(qpl.QPL_FP8R, to_dev(wq), to_dev(ws))
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), dequant_weight_fp8r(wq, ws))
+
+
+def test_dequant_weight_nvfp4():
+    w = make("nvfp4_dit", M=8, K=1040, N=129)["w"]
+    g = global_scale(amax_bf16(w))
+    wp, wb = quant_nvfp4(w, g)
+    say("dequant_weight nvfp4", wp.shape)
+    out = qpl.dequant_weight(qpl.QPL_NVFP4, to_dev(wp), to_dev(wb), g, K=1040)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), dequant_weight_nvfp4(wp, wb, g))
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 1000, 4608 * 3072 + 3])
+def test_amax(n):
+    x = bf16_round((np.random.default_rng(n).standard_normal(n) * 3).astype(np.float32))
+    say("qpl_amax_bf16", n)
+    a = qpl.amax_bf16(to_dev_bf16(x))
+    a = qpl.amax_bf16(to_dev_bf16(x[: max(1, n // 2)]), amax=a)  # running max keeps the larger
+    torch.cuda.synchronize()
+    assert host(a)[0] == amax_bf16(x)
+
+
+def test_quant_deterministic():
+    d = make("nvfp4_dit", M=512)
+    x = to_dev_bf16(d["x"])
+    a = [host(t) for t in qpl.quant_act_nvfp4(x, 0.01)]
+    b = [host(t) for t in qpl.quant_act_nvfp4(x, 0.01)]
+    assert all(np.array_equal(p, q) for p, q in zip(a, b))
