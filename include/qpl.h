@@ -163,7 +163,8 @@ typedef enum {
   QPL_KERNEL_LOWRANK_PREP = 6,      /* x L1 and the factor transposes */
   QPL_KERNEL_DEQUANT = 7,
   QPL_KERNEL_AMAX = 8,
-  QPL_KERNEL_COUNT = 9
+  QPL_KERNEL_WEIGHT_BF16 = 9,       /* nvfp4 weight expansion inside qlinear_nvfp4 */
+  QPL_KERNEL_COUNT = 10
 } qpl_kernel;
 
 void qpl_timing_enable(int on);

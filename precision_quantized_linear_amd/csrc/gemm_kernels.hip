@@ -1,29 +1,38 @@
-// Quantized GEMMs for gfx950 (CDNA4): y[M,N] = x[M,K] * W[N,K]^T, fp32 accumulation
-// in the MFMA units, bf16 output rounded to nearest even.
+// Quantized GEMMs for gfx950 (CDNA4): y[M,N] = x[M,K] * W[N,K]^T with fp32
+// accumulation in the MFMA units and bf16 output rounded to nearest even.
 //
 // fp8r (Diffusers guide "BFL (fp8r / nvfp4)", "Kernels" table, fp8r row): E4M3 x
-// E4M3 on the f8f6f4 MFMA (V_MFMA_SCALE_F32_32X32X64_F8F6F4 with unit E8M0 scales),
-// epilogue (acc * s_x[m]) * s_w[n].
+// E4M3 on the f8f6f4 MFMA (V_MFMA_SCALE_F32_32X32X64_F8F6F4 with unit E8M0
+// scales); output (acc * s_x[m]) * s_w[n].
 //
 // nvfp4 ("Kernels" table, nvfp4 row): the guide's kernel is a block-scaled FP4
-// GEMM with one E4M3 scale per 16 elements.  gfx950's scaled MFMA takes one
+// GEMM with one E4M3 scale per 16 elements.  gfx950's scaled MFMA applies one
 // power-of-two (E8M0) scale per 32 elements, and a code times an E4M3 scale needs
 // up to 6 significant bits, which no 8-, 6- or 4-bit operand format holds.  The
-// exact route taken here expands each value e2m1(code) * dec(sf) to bf16 (exact)
-// and runs the bf16 MFMA (V_MFMA_F32_32X32X16_BF16): activations arrive already
-// expanded from the quantize kernel, weight codes stay packed in HBM and are
-// expanded once per workgroup tile while being staged into LDS.  The global
-// factor input_scale * weight_scale_2 and the optional SVDQuant low-rank term
-// (Nunchaku post, "Background: SVDQuant and Nunchaku": up-projection fused into
-// the 4-bit GEMM) are applied in the fp32 accumulators before the bf16 rounding.
+// exact route taken here: both operands are expanded to bf16 values
+// e2m1(code) * dec(sf) (exact) -- activations by the quantize kernel, weights by
+// one streaming pass over the packed weight -- and multiplied on the bf16 MFMA
+// (V_MFMA_F32_32X32X16_BF16).  The global factor input_scale * weight_scale_2
+// and the optional SVDQuant low-rank term (Nunchaku post, "Background: SVDQuant
+// and Nunchaku": the up-projection fused into the GEMM) are applied to the fp32
+// accumulators before the single bf16 rounding.
 //
-// Tiling: a 256-thread workgroup (4 wavefronts, 2 x 2) owns a 256 x 256 output
-// tile; each wavefront owns 128 x 128 (16 MFMA tiles of 32 x 32, 256 fp32
-// accumulators per lane, one wavefront per SIMD).  Each K-step stages a 256-row x
-// 128-byte slab of both operands in LDS (fp8: 128 elements, bf16: 64 elements),
-// double-buffered (128 KB of the 160 KB LDS), with the 16-byte chunks of a row
-// XOR-swizzled so the MFMA operand reads are bank-conflict free.  The output tile
-// is transposed through LDS so every global store is a 16-byte row segment.
+// Pipeline (both GEMMs):
+// * a 256-thread workgroup (4 wavefronts, 2 x 2) owns a 256 x 256 output tile; a
+//   wavefront owns 128 x 128 (16 MFMA tiles of 32 x 32, 256 fp32 accumulators
+//   per lane in AGPRs, one wavefront per SIMD);
+// * K is walked in 64-byte slabs (64 fp8 or 32 bf16 elements per row); each
+//   stage holds the 256-row slab of both operands (32 KB) and four stages ring
+//   through 128 KB of the 160 KB LDS;
+// * slabs move global -> LDS with buffer_load_dwordx4 ... lds (no register
+//   staging), issued four stages ahead and spread between the MFMAs; rows past
+//   the matrix and bytes past K read as zero through the buffer range check;
+// * the 16-byte chunks of each 64-byte row are XOR-swizzled with
+//   (r ^ r >> 3) & 3, which makes the MFMA operand reads bank-conflict free;
+// * operand fragments of the next slab are read into the registers of the
+//   current slab's fragments as each one is used for the last time;
+// * operands are swapped (the MFMA computes y^T), so each lane ends with four
+//   consecutive output columns of a row and stores them as one 8-byte segment.
 #include "qpl_device.h"
 #include "qpl_internal.h"
 
@@ -31,41 +40,21 @@ namespace qpl {
 
 namespace {
 
-constexpr int TM = 256;        // tile rows (M)
-constexpr int TN = 256;        // tile columns (N)
-constexpr int ROWB = 128;      // bytes per LDS slab row
-constexpr int SLAB = TM * ROWB;  // 32 KB per operand per stage
-constexpr int LDS_BYTES = 4 * SLAB;
+constexpr int SROW = 64;            // bytes per slab row
+constexpr int SLAB = 256 * SROW;    // 16 KB per operand per stage
+constexpr int STAGE = 2 * SLAB;     // x slab then W slab
+constexpr int NST = 4;              // stages in the ring
+constexpr int DMA_PER_STAGE = 8;    // per wavefront: 4 x-slab and 4 W-slab instructions of 1 KB
+constexpr uint32_t kOutOfRange = 0x40000000u;
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // gfx9 buffer descriptor word 3: raw 32-bit elements
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int ch) { return r * ROWB + ((ch ^ swz(r)) << 4); }
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int soff(int r, int c) { return r * SROW + ((c ^ swz(r)) << 4); }
 
-// 256 rows x 128 bytes of a row-major byte matrix (pitch bytes per row), rows and
-// bytes beyond the limits read as zero.  Thread t loads chunk t % 8 of rows
-// t / 8 + 32 i, so eight consecutive threads read one 128-byte row segment.
-struct Slab {
-  u32x4 v[8];
-};
-
-__device__ __forceinline__ void load_slab(Slab& s, const uint8_t* __restrict__ base, int64_t pitch,
-                                          int64_t rows_left, int64_t bytes_left, int t) {
-  const int ch = t & 7;
-  const bool kin = (int64_t)ch * 16 < bytes_left;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = i * 32 + (t >> 3);
-    if (kin && r < rows_left)
-      s.v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)r * pitch + ch * 16);
-    else
-      s.v[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-__device__ __forceinline__ void store_slab(const Slab& s, uint8_t* lds, int t) {
-  const int ch = t & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(lds + lds_off(i * 32 + (t >> 3), ch)) = s.v[i];
-}
+// s_waitcnt with one counter constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8).
+#define QPL_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+#define QPL_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 typedef f32x16 Acc[4][4];
 
@@ -76,285 +65,246 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 }
 
-// One 128-element fp8 K-step: two 32x32x64 sub-steps.  Lane l holds row (l % 32)
-// of its 32-row fragment and the 32 K-values 64 s + 32 (l / 32) + [0, 32); the B
-// operand holds the same K-values, so each MFMA sums a complete 64-wide K range.
-__device__ __forceinline__ void mma_fp8(const uint8_t* lA, const uint8_t* lB, Acc& acc, int wm, int wn,
-                                        int lane) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    i32x8 a[4], b[4];
-    const int c0 = 4 * s + 2 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + i * 32 + (lane & 31);
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(lA + lds_off(ra, c0));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(lA + lds_off(ra, c0 + 1));
-      a[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const int rb = wn * 128 + i * 32 + (lane & 31);
-      const u32x4 lo2 = *reinterpret_cast<const u32x4*>(lB + lds_off(rb, c0));
-      const u32x4 hi2 = *reinterpret_cast<const u32x4*>(lB + lds_off(rb, c0 + 1));
-      b[i] = i32x8{(int)lo2.x, (int)lo2.y, (int)lo2.z, (int)lo2.w, (int)hi2.x, (int)hi2.y, (int)hi2.z, (int)hi2.w};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
-  }
+// Buffer descriptor (in scalar registers) over the tile's rows of a row-major
+// byte matrix: reads past the tile's last valid row return zero.
+__device__ __forceinline__ u32x4 tile_desc(const void* base, int64_t rows_left, int64_t pitch) {
+  const int64_t rows = rows_left < 256 ? rows_left : 256;
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  d.y = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  d.z = __builtin_amdgcn_readfirstlane((uint32_t)(rows * pitch));
+  d.w = kRawBufferWord3;
+  return d;
 }
 
-// One 64-element bf16 K-step: four 32x32x16 sub-steps, lane l holding the 8
-// K-values 16 s + 8 (l / 32) + [0, 8) of its row.
-__device__ __forceinline__ void mma_bf16(const uint8_t* lA, const uint8_t* lB, Acc& acc, int wm, int wn,
-                                         int lane) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x8 a[4], b[4];
-    const int c = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8*>(lA + lds_off(wm * 128 + i * 32 + (lane & 31), c));
-      b[i] = *reinterpret_cast<const bf16x8*>(lB + lds_off(wn * 128 + i * 32 + (lane & 31), c));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+// 16 bytes per lane from global memory into LDS: lane l writes LDS bytes
+// [lds_addr + 16 l, + 16); an offset past the descriptor's size writes zeros.  It
+// is inline assembly so that the compiler does not wait for these loads at every
+// LDS read: the pipeline counts them itself (QPL_WAIT_VMCNT).
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, u32x4 desc, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soffset)
+               : "memory");
 }
 
-// Packed E2M1 weight slab for one K-step of 64 elements: thread t owns weight row
-// n0 + t (32 bytes of codes and 4 block-scale bytes).
-struct Fp4Slab {
-  uint32_t c[8];
-  uint32_t s;
+// Operand fragments.  fp8: a 32x32x64 MFMA operand (32 K-bytes per lane, two
+// chunks).  bf16: a 32x32x16 MFMA operand (8 K-values per lane, one chunk); a
+// 64-byte slab holds two of them (sub-steps).
+struct Fp8Mma {
+  static constexpr int SUB = 1;
+  typedef i32x8 Frag;
+  static __device__ __forceinline__ Frag read(const uint8_t* slab, int row, int sub, int lane) {
+    (void)sub;
+    const int c = 2 * (lane >> 5);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(slab + soff(row, c));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(slab + soff(row, c + 1));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  static __device__ __forceinline__ f32x16 mma(const Frag& w, const Frag& x, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, c, 0, 0, 0, 127, 0, 127);
+  }
 };
 
-template <bool ALIGNED>
-__device__ __forceinline__ void load_fp4(Fp4Slab& f, const uint8_t* __restrict__ w, const uint8_t* __restrict__ wbs,
-                                         int64_t K, int64_t n, int64_t N, int64_t k0) {
-  if (n >= N) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f.c[i] = 0u;
-    f.s = 0u;
-    return;
+struct Bf16Mma {
+  static constexpr int SUB = 2;
+  typedef bf16x8 Frag;
+  static __device__ __forceinline__ Frag read(const uint8_t* slab, int row, int sub, int lane) {
+    return *reinterpret_cast<const bf16x8*>(slab + soff(row, 2 * sub + (lane >> 5)));
   }
-  if constexpr (ALIGNED) {  // K % 64 == 0: rows 32-byte aligned, K-steps always full
-    const u32x4* src = reinterpret_cast<const u32x4*>(w + n * (K / 2) + k0 / 2);
-    const u32x4 a = src[0], b = src[1];
-    f.c[0] = a.x; f.c[1] = a.y; f.c[2] = a.z; f.c[3] = a.w;
-    f.c[4] = b.x; f.c[5] = b.y; f.c[6] = b.z; f.c[7] = b.w;
-    f.s = *reinterpret_cast<const uint32_t*>(wbs + n * (K / 16) + k0 / 16);
-  } else {  // K % 16 == 0 only: byte loads, blocks past K read as zero
-    const uint8_t* row = w + n * (K / 2);
-    const uint8_t* srow = wbs + n * (K / 16);
+  static __device__ __forceinline__ f32x16 mma(const Frag& w, const Frag& x, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, x, c, 0, 0, 0);
+  }
+};
+
+// One pass of the pipeline over K: acc += W_tile x_tile^T in the D^T layout
+// (acc[i][j] row index = W row, column index = x row).  dx / dw are descriptors
+// over the tile's x rows and W rows (same pitch, kbytes valid bytes per row).
+// Ends with every load drained and all waves past a barrier, so LDS is free.
+template <class T>
+__device__ __forceinline__ void gemm_pass(Acc& acc, uint8_t* lds, uint32_t lbase, u32x4 dx, u32x4 dw, int pitch,
+                                          int kbytes, int wv, int wm, int wn, int lane) {
+  uint32_t vbase[4];
+  int cb[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      uint32_t v = 0;
-      if (k0 + 8 * q < K) {
+  for (int q = 0; q < 4; ++q) {
+    // instruction q of this wave covers slab rows 16 (4 wv + q) .. + 15; lane l
+    // fills physical chunk l % 4 of row ... + l / 4, i.e. logical chunk (l % 4) ^ swz
+    const int row = 16 * (4 * wv + q) + (lane >> 2);
+    cb[q] = ((lane & 3) ^ swz(row)) * 16;
+    vbase[q] = (uint32_t)(row * pitch + cb[q]);
+  }
+  const int nk = (kbytes + SROW - 1) / SROW;
+  auto voff = [&](int s, int q) -> uint32_t { return (s < nk && s * SROW + cb[q] < kbytes) ? vbase[q] : kOutOfRange; };
+  auto dma = [&](int s, int q, bool w_slab) {
+    const uint32_t dst = lbase + (s % NST) * STAGE + (w_slab ? SLAB : 0) + (4 * wv + q) * 1024;
+    dma16(dst, voff(s, q), w_slab ? dw : dx, s * SROW);
+  };
 #pragma unroll
-        for (int b = 0; b < 4; ++b) v |= (uint32_t)row[(k0 + 8 * q) / 2 + b] << (8 * b);
-      }
-      f.c[q] = v;
+  for (int s = 0; s < NST; ++s)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dma(s, q, false);
+      dma(s, q, true);
     }
-    uint32_t s = 0;
+  QPL_WAIT_VMCNT((NST - 1) * DMA_PER_STAGE);
+  __builtin_amdgcn_s_barrier();
+  typename T::Frag fw[T::SUB][4], fx[T::SUB][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (k0 + 16 * b < K) s |= (uint32_t)srow[k0 / 16 + b] << (8 * b);
-    f.s = s;
-  }
-}
-
-// Upper halves of two floats whose values are exact in bf16: (lo, hi) packed.
-__device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// Expand 64 packed codes of one weight row to bf16 e2m1(code) * dec(sf) (exact)
-// and write them as 8 swizzled 16-byte chunks of LDS row t.  The hardware
-// conversion applies only the exponent of its scale operand, so it runs with
-// scale 1 and the E4M3 block scale is multiplied in fp32 (exact product); the
-// upper halves of the fp32 results are then the bf16 values.
-__device__ __forceinline__ void store_fp4_expanded(const Fp4Slab& f, uint8_t* lB, int t) {
+  for (int u = 0; u < T::SUB; ++u)
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const float sf = e4m3_decode((f.s >> (8 * (q >> 1))) & 0xFFu);
-    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.c[q], 1.0f, 0);
-    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.c[q], 1.0f, 1);
-    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.c[q], 1.0f, 2);
-    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(f.c[q], 1.0f, 3);
-    const uint32_t o[4] = {pack_bf16_hi(v0[0] * sf, v0[1] * sf), pack_bf16_hi(v1[0] * sf, v1[1] * sf),
-                           pack_bf16_hi(v2[0] * sf, v2[1] * sf), pack_bf16_hi(v3[0] * sf, v3[1] * sf)};
-    *reinterpret_cast<u32x4*>(lB + lds_off(t, q)) = u32x4{o[0], o[1], o[2], o[3]};
-  }
-}
-
-// Write the 256 x 256 tile: scale in fp32, round to bf16, transpose through LDS,
-// then store 16-byte row segments (element stores when N % 8 != 0).
-template <class Scale>
-__device__ __forceinline__ void epilogue(Acc& acc, uint8_t* lds, int wm, int wn, int lane, int t, int64_t m0,
-                                         int64_t n0, int64_t M, int64_t N, uint16_t* __restrict__ y,
-                                         const Scale& scale) {
-  uint16_t* ly = reinterpret_cast<uint16_t*>(lds);
-  __syncthreads();
-  float fc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fc[j] = scale.col(wn * 128 + j * 32 + (lane & 31));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const float fr = scale.row(row);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = wn * 128 + j * 32 + (lane & 31);
-        ly[row * TN + col] = (uint16_t)f32_to_bf16((acc[i][j][r] * fr) * fc[j]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      fw[u][i] = T::read(lds + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
+      fx[u][i] = T::read(lds, wm * 128 + i * 32 + (lane & 31), u, lane);
     }
-  __syncthreads();
-  const bool vec = (N % 8) == 0;
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int c = it * 256 + t;
-    const int row = c >> 5, ch = c & 31;
-    const int64_t gm = m0 + row, gn = n0 + ch * 8;
-    if (gm >= M || gn >= N) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ly + row * TN + ch * 8);
-    if (vec) {
-      *reinterpret_cast<u32x4*>(y + gm * N + gn) = v;
-    } else {
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  constexpr int NMMA = 16 * T::SUB;
+  for (int kt = 0; kt < nk; ++kt) {
+    // slab kt + 1 has landed for every wave, and every wave is done with step kt - 1
+    QPL_WAIT_LGKM0();
+    QPL_WAIT_VMCNT((NST - 2) * DMA_PER_STAGE);
+    __builtin_amdgcn_s_barrier();
+    const uint8_t* nx = lds + ((kt + 1) % NST) * STAGE;
+    const int sref = kt + NST;  // refill the buffer slab kt used with slab kt + NST
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gn + e < N) y[gm * N + gn + e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-    }
+    for (int u = 0; u < T::SUB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = T::mma(fw[u][i], fx[u][j], acc[i][j]);
+          const int k = 16 * u + 4 * i + j;
+          if (i == 3) fx[u][j] = T::read(nx, wm * 128 + j * 32 + (lane & 31), u, lane);
+          if (j == 3) fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
+          // spread this step's 8 refill loads over its MFMAs
+          constexpr int every = NMMA / DMA_PER_STAGE;
+          if (k % every == every - 1) {
+            const int d = k / every;
+            dma(sref, d & 3, d >= 4);
+          }
+        }
   }
+  QPL_WAIT_VMCNT(0);
+  QPL_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
 }
 
-// Tile order: workgroups are dispatched round-robin over the 8 XCDs, so give each
-// XCD a contiguous run of tiles (row-major over the tile grid) to share its L2.
+// Tile order.  Workgroups are dispatched round-robin over the 8 XCDs and each XCD
+// has its own L2, so each XCD gets a contiguous run of the tile sequence; the
+// sequence walks groups of GROUP_M tile-rows column by column, so the ~32 tiles an
+// XCD runs at once form a 4 x 8 block that shares 4 activation slabs and 8 weight
+// slabs in that XCD's L2.
+constexpr int GROUP_M = 4;
+
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
   const int T = tiles_m * tiles_n;
   int b = blockIdx.x;
   if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
-  m0 = (int64_t)(b / tiles_n) * TM;
-  n0 = (int64_t)(b % tiles_n) * TN;
+  const int per_group = GROUP_M * tiles_n;
+  const int g = b / per_group;
+  const int first_m = g * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int r = b - g * per_group;
+  m0 = (int64_t)(first_m + r % gm) * 256;
+  n0 = (int64_t)(r / gm) * 256;
 }
 
-// Output scaling y = (acc * row(m)) * col(n).
-struct RowColScale {
-  const float* sa;
-  const float* sb;
-  int64_t m0, n0, M, N;
-  __device__ float row(int r) const { return m0 + r < M ? sa[m0 + r] : 0.0f; }
-  __device__ float col(int c) const { return n0 + c < N ? sb[n0 + c] : 0.0f; }
-};
-
-struct UniformScale {
-  float g;
-  __device__ float row(int) const { return g; }
-  __device__ float col(int) const { return 1.0f; }
-};
+// Store the tile: y[m][n .. n+3] = bf16((acc * rs(m)) * cs(n .. n+3)) as 8-byte
+// segments (element stores at the N edge or when N % 4 != 0).
+template <class RowScale, class ColScale>
+__device__ __forceinline__ void store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
+                                           int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
+                                           const ColScale& cs) {
+  const bool vec = (N & 3) == 0;
+  float fr[4];
+  f32x4 fc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fr[j] = rs(wm * 128 + j * 32 + (lane & 31));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fc[i][g] = cs(wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (acc[i][j][g * 4 + e] * fr[j]) * fc[i][g][e];
+        if (vec && n < N) {
+          u32x2 o;
+          o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+          o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<u32x2*>(y + m * N + n) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) y[m * N + n + e] = (uint16_t)f32_to_bf16(v[e]);
+        }
+      }
+  }
+}
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_fp8r(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
     const float* __restrict__ sb, int64_t M, int64_t K, int64_t N, uint16_t* __restrict__ Y, int tiles_m,
     int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+  __shared__ __attribute__((aligned(16))) float lscale[2][256];  // the tile's row scales and column scales
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
   int64_t m0, n0;
   tile_coords(tiles_m, tiles_n, m0, n0);
-  const uint8_t* Ab = A + m0 * K;
-  const uint8_t* Bb = B + n0 * K;
-  const int64_t nk = (K + ROWB - 1) / ROWB;
+  lscale[0][t] = m0 + t < M ? sa[m0 + t] : 0.0f;
+  lscale[1][t] = n0 + t < N ? sb[n0 + t] : 0.0f;
+  const uint32_t lbase =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds));
   Acc acc;
   zero_acc(acc);
-  Slab ra, rb;
-  load_slab(ra, Ab, K, M - m0, K, t);
-  load_slab(rb, Bb, K, N - n0, K, t);
-  store_slab(ra, lds, t);
-  store_slab(rb, lds + SLAB, t);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = lds + (kt & 1) * 2 * SLAB;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * 2 * SLAB;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t k1 = (kt + 1) * ROWB;
-      load_slab(ra, Ab + k1, K, M - m0, K - k1, t);
-      load_slab(rb, Bb + k1, K, N - n0, K - k1, t);
-    }
-    mma_fp8(cur, cur + SLAB, acc, wm, wn, lane);
-    if (more) {
-      store_slab(ra, nxt, t);
-      store_slab(rb, nxt + SLAB, t);
-    }
-    __syncthreads();
-  }
-  epilogue(acc, lds, wm, wn, lane, t, m0, n0, M, N, Y, RowColScale{sa, sb, m0, n0, M, N});
+  gemm_pass<Fp8Mma>(acc, lds, lbase, tile_desc(A + m0 * K, M - m0, K), tile_desc(B + n0 * K, N - n0, K), (int)K,
+                    (int)K, wv, wm, wn, lane);
+  store_tile(acc, wm, wn, lane, m0, n0, M, N, Y, [&](int r) { return lscale[0][r]; },
+             [&](int c) { return *reinterpret_cast<const f32x4*>(&lscale[1][c]); });
 }
 
-template <bool ALIGNED, bool LOWRANK>
+template <bool LOWRANK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
-    const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const uint8_t* __restrict__ Wbs, float gscale,
-    int64_t M, int64_t K, int64_t N, const uint16_t* __restrict__ T, const uint16_t* __restrict__ L2t, int64_t KL,
-    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, float gscale, int64_t M, int64_t K, int64_t N,
+    const uint16_t* __restrict__ T, const uint16_t* __restrict__ L2t, int64_t KL, uint16_t* __restrict__ Y,
+    int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
   int64_t m0, n0;
   tile_coords(tiles_m, tiles_n, m0, n0);
-  const uint8_t* Ab = reinterpret_cast<const uint8_t*>(A + m0 * K);
-  const int64_t kb = 2 * K;  // bytes per activation row
-  const int64_t nk = (K + 63) / 64;
+  const uint32_t lbase =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds));
   Acc acc;
   zero_acc(acc);
-  Slab ra;
-  Fp4Slab fw;
-  load_slab(ra, Ab, kb, M - m0, kb, t);
-  load_fp4<ALIGNED>(fw, W, Wbs, K, n0 + t, N, 0);
-  store_slab(ra, lds, t);
-  store_fp4_expanded(fw, lds + SLAB, t);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = lds + (kt & 1) * 2 * SLAB;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * 2 * SLAB;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_slab(ra, Ab + (kt + 1) * ROWB, kb, M - m0, kb - (kt + 1) * ROWB, t);
-      load_fp4<ALIGNED>(fw, W, Wbs, K, n0 + t, N, (kt + 1) * 64);
-    }
-    mma_bf16(cur, cur + SLAB, acc, wm, wn, lane);
-    if (more) {
-      store_slab(ra, nxt, t);
-      store_fp4_expanded(fw, nxt + SLAB, t);
-    }
-    __syncthreads();
-  }
+  const int kb = (int)(2 * K);
+  gemm_pass<Bf16Mma>(acc, lds, lbase, tile_desc(A + m0 * K, M - m0, kb), tile_desc(W + n0 * K, N - n0, kb), kb, kb,
+                     wv, wm, wn, lane);
   float oscale = gscale;
   if constexpr (LOWRANK) {
-    // SVDQuant up-projection: acc = g * acc + [T_hi | T_lo] [L2^T | L2^T]^T, in fp32.
+    // SVDQuant up-projection: acc = g * acc + [T_hi | T_lo] [L2^T | L2^T]^T, in fp32
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] *= gscale;
-    const uint8_t* Tb = reinterpret_cast<const uint8_t*>(T + m0 * KL);
-    const uint8_t* Lb = reinterpret_cast<const uint8_t*>(L2t + n0 * KL);
-    const int64_t lb = 2 * KL;
-    Slab rl;
-    for (int64_t k1 = 0; k1 < lb; k1 += ROWB) {
-      load_slab(ra, Tb + k1, lb, M - m0, lb - k1, t);
-      load_slab(rl, Lb + k1, lb, N - n0, lb - k1, t);
-      store_slab(ra, lds, t);
-      store_slab(rl, lds + SLAB, t);
-      __syncthreads();
-      mma_bf16(lds, lds + SLAB, acc, wm, wn, lane);
-      __syncthreads();
-    }
+    const int lb = (int)(2 * KL);
+    gemm_pass<Bf16Mma>(acc, lds, lbase, tile_desc(T + m0 * KL, M - m0, lb), tile_desc(L2t + n0 * KL, N - n0, lb), lb,
+                       lb, wv, wm, wn, lane);
     oscale = 1.0f;
   }
-  epilogue(acc, lds, wm, wn, lane, t, m0, n0, M, N, Y, UniformScale{oscale});
+  store_tile(acc, wm, wn, lane, m0, n0, M, N, Y, [&](int) { return oscale; },
+             [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
 }
 
 // T = x L1 for the low-rank branch: one workgroup per 32 rows x 32 rank columns,
@@ -413,25 +363,22 @@ __global__ __launch_bounds__(256) void k_lowrank_transpose(const uint16_t* __res
 
 hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws, int64_t M,
                             int64_t K, int64_t N, uint16_t* y, hipStream_t stream) {
-  const int tm = (int)((M + TM - 1) / TM), tn = (int)((N + TN - 1) / TN);
+  const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
   hipLaunchKernelGGL(k_gemm_fp8r, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, xq, xs, w, ws, M, K, N, y, tm,
                      tn);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint8_t* w, const uint8_t* wbs, float gscale, int64_t M,
-                             int64_t K, int64_t N, LowRank lr, uint16_t* y, hipStream_t stream) {
-  const int tm = (int)((M + TM - 1) / TM), tn = (int)((N + TN - 1) / TN);
+hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
+                             LowRank lr, uint16_t* y, hipStream_t stream) {
+  const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
   const dim3 grid((unsigned)(tm * tn)), block(256);
-#define QPL_NVFP4_GEMM(AL, LR)                                                                                   \
-  hipLaunchKernelGGL((k_gemm_nvfp4<AL, LR>), grid, block, 0, stream, xe, w, wbs, gscale, M, K, N, lr.t, lr.l2t, \
-                     lr.kl, y, tm, tn)
-  const bool aligned = K % 64 == 0, lowrank = lr.kl > 0;
-  if (aligned && !lowrank) QPL_NVFP4_GEMM(true, false);
-  else if (aligned) QPL_NVFP4_GEMM(true, true);
-  else if (!lowrank) QPL_NVFP4_GEMM(false, false);
-  else QPL_NVFP4_GEMM(false, true);
-#undef QPL_NVFP4_GEMM
+  if (lr.kl > 0)
+    hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, block, 0, stream, xe, we, gscale, M, K, N, lr.t, lr.l2t, lr.kl, y,
+                       tm, tn);
+  else
+    hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, block, 0, stream, xe, we, gscale, M, K, N, lr.t, lr.l2t, lr.kl, y,
+                       tm, tn);
   return hipGetLastError();
 }
 

@@ -60,32 +60,33 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 int64_t rank_pad(int64_t R) { return (R + 31) / 32 * 32; }
 
-// Workspace layout.  fp8r: [xq: M*K bytes][xs: 4*M bytes].  nvfp4: [xe: 2*M*K
-// bytes (bf16 expanded activations)] then, when R > 0, [l1t: 2*rpad*K][t: 2*M*KL]
-// [l2t: 2*N*KL] with rpad = 32*ceil(R/32) and KL = 2*rpad.  Each part is rounded
-// up to 256 bytes.
+// Workspace layout.  fp8r: [xq: M*K bytes][xs: 4*M bytes].  nvfp4: [xe: 2*M*K]
+// [we: 2*N*K] (bf16 expansions of the quantized activations and weights) then,
+// when R > 0, [l1t: 2*rpad*K][t: 2*M*KL][l2t: 2*N*KL] with rpad = 32*ceil(R/32)
+// and KL = 2*rpad.  Each part is rounded up to 256 bytes.
 struct Layout {
-  size_t off[4] = {0, 0, 0, 0};
+  size_t off[5] = {0, 0, 0, 0, 0};
   size_t total = 0;
 };
 
 Layout layout(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R) {
   Layout L;
-  size_t parts[4] = {0, 0, 0, 0};
+  size_t parts[5] = {0, 0, 0, 0, 0};
   if (scheme == QPL_FP8R) {
     parts[0] = size_t(M) * size_t(K);
     parts[1] = size_t(4) * size_t(M);
   } else {
     parts[0] = size_t(2) * size_t(M) * size_t(K);
+    parts[1] = size_t(2) * size_t(N) * size_t(K);
     if (R > 0) {
       const int64_t rp = rank_pad(R), kl = 2 * rp;
-      parts[1] = size_t(2) * size_t(rp) * size_t(K);
-      parts[2] = size_t(2) * size_t(M) * size_t(kl);
-      parts[3] = size_t(2) * size_t(N) * size_t(kl);
+      parts[2] = size_t(2) * size_t(rp) * size_t(K);
+      parts[3] = size_t(2) * size_t(M) * size_t(kl);
+      parts[4] = size_t(2) * size_t(N) * size_t(kl);
     }
   }
   size_t o = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     L.off[i] = o;
     o += round256(parts[i]);
   }
@@ -269,15 +270,20 @@ QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint16_t* xe = reinterpret_cast<uint16_t*>(base + L.off[0]);
+  uint16_t* we = reinterpret_cast<uint16_t*>(base + L.off[1]);
   if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, xe, st)))) !=
+      QPL_OK)
+    return s;
+  // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue
+  if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st)))) !=
       QPL_OK)
     return s;
   qpl::LowRank lr;
   if (R > 0) {
     const int64_t kl = 2 * rank_pad(R);
-    uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[1]);
-    uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[2]);
-    uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[3]);
+    uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[2]);
+    uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[3]);
+    uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
     if ((s = launched(Timed(QPL_KERNEL_LOWRANK_PREP, st)(
              qpl::launch_lowrank_prep(x, lora_down, lora_up, M, K, N, R, kl, l1t, t, l2t, st)))) != QPL_OK)
       return s;
@@ -286,7 +292,7 @@ QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int
     lr.kl = kl;
   }
   return launched(Timed(R > 0 ? QPL_KERNEL_GEMM_NVFP4_LOWRANK : QPL_KERNEL_GEMM_NVFP4, st)(
-      qpl::launch_gemm_nvfp4(xe, weight, weight_scale, gscale, M, K, N, lr, y, st)));
+      qpl::launch_gemm_nvfp4(xe, we, gscale, M, K, N, lr, y, st)));
 }
 
 QPL_EXPORT qpl_status dequant_weight(qpl_scheme scheme, const uint8_t* weight, const void* weight_scale,

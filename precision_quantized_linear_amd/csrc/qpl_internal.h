@@ -33,8 +33,10 @@ struct LowRank {
   int64_t kl = 0;
 };
 
-hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint8_t* w, const uint8_t* wbs, float gscale,
-                             int64_t M, int64_t K, int64_t N, LowRank lr, uint16_t* y, hipStream_t stream);
+// xe [M,K] and we [N,K] are the bf16 expansions e2m1(code) * dec(sf) of the
+// quantized activations and weights; y = bf16(gscale * xe we^T [+ low-rank term]).
+hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
+                             LowRank lr, uint16_t* y, hipStream_t stream);
 
 hipError_t launch_lowrank_prep(const uint16_t* x, const uint16_t* l1, const uint16_t* l2, int64_t M, int64_t K,
                                int64_t N, int64_t R, int64_t kl, uint16_t* l1t, uint16_t* t, uint16_t* l2t,

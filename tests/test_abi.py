@@ -48,9 +48,9 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     M, K, N = 4608, 3072, 12288
     assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, M, K, N) == M * K + M * 4
-    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N) == 2 * M * K
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N) == 2 * M * K + 2 * N * K
     r = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, 3072, 32)
-    assert r == 2 * M * K + 2 * 32 * K + 2 * M * 64 + 2 * 3072 * 64
+    assert r == 2 * M * K + 2 * 3072 * K + 2 * 32 * K + 2 * M * 64 + 2 * 3072 * 64
     assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 24, 4) == 0      # K % 16 != 0
     assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 32, 4, 129) == 0  # rank too large
     assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, 4, 32, 4, 1) == 0     # fp8r has no low rank
