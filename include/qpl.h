@@ -70,7 +70,7 @@ qpl_status quant_act_fp8_row(const uint16_t* x, int64_t M, int64_t K,
  * Per 16-element block: sf = E4M3(bmax / (6 g)), d = dec(sf) * g (fp32),
  * codes E2M1(x / d) (signed zeros when d == 0).
  *   x              bf16 [M,K]                  input
- *   input_scale    g, finite and > 0
+ *   input_scale    g, finite and > 0, with 6 g finite in fp32 (else QPL_ERR_ARG)
  *   x_q            uint8 [M,K/2]               out: packed E2M1 codes
  *   x_block_scale  uint8 E4M3 [M,K/16]         out: block scales
  */
@@ -100,7 +100,7 @@ qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N,
  *   weight          uint8 [N,K/2]        packed E2M1
  *   weight_scale    uint8 E4M3 [N,K/16]
  *   weight_scale_2  global weight scale, finite and > 0
- *   input_scale     calibrated activation scale, finite and > 0
+ *   input_scale     calibrated activation scale, finite and > 0, 6 * input_scale finite
  *   lora_down       bf16 [K,R] (L1) or NULL when R == 0
  *   lora_up         bf16 [R,N] (L2) or NULL when R == 0
  *   R               rank, 0..128

@@ -70,6 +70,46 @@ __device__ __forceinline__ float e2m1_decode(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
+// Correctly rounded x / s from a precomputed r = RN(1 / s) (one Markstein
+// correction step: q0 = x r, e = x - s q0 exactly by fma, q = q0 + e r).  The
+// sign is copied from x so that -0 stays -0.  A quotient that overflows returns
+// the infinity of x r (the correction would turn it into NaN).  Requires
+// 2^-64 <= s <= 2^64 (r normal); the callers use the plain division outside that
+// range.  Checked on the GPU against IEEE division: identical E4M3 and E2M1 codes
+// for every finite bf16 x over 8192 divisors spanning 2^-40..2^40 (including
+// all-ones and zero mantissas).
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  const float q = __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+  return __builtin_isinf(q0) ? q0 : q;
+}
+
+// Whether s lies in the range where div_rn is exact.
+__device__ __forceinline__ bool div_rn_ok(float s) { return s >= 0x1p-64f && s <= 0x1p64f; }
+
+// E4M3 codes of two floats with the hardware OCP FP8 converter (round to nearest
+// even).  The converter turns values above 464 into NaN instead of saturating, so
+// magnitudes are clamped to 448 first; with that clamp it matched the bit-level
+// encoder on 2^28 random values including every rounding midpoint +- 1 ulp.
+// Returns the two codes in bits 7:0 and 15:8.
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+}
+
+// E2M1 codes of two floats with the hardware FP4 converter at scale 1 (round to
+// nearest even, saturating at 6; matched the bit-level encoder on 2^28 random
+// finite values including midpoints).  Inputs are clamped to +-6 first so that an
+// infinite quotient also lands on the largest code.  Returns the codes in bits 3:0
+// and 7:4.
+__device__ __forceinline__ uint32_t e2m1_pack2(float a, float b) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -6.0f, 6.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -6.0f, 6.0f);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ca, cb, 1.0f, 0) & 0xFFu;
+}
+
 // Wave-wide max of a non-negative float (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

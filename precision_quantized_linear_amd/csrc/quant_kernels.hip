@@ -22,24 +22,39 @@ __device__ __forceinline__ float pair_absmax(uint32_t p, float m) {
   return fmaxf(m, fmaxf(bf16_lo(p & 0x7FFF7FFFu), bf16_hi(p & 0x7FFF7FFFu)));
 }
 
-__device__ __forceinline__ uint32_t fp8_pair(uint32_t p, float s) {
-  uint32_t lo = e4m3_encode(bf16_lo(p) / s);
-  uint32_t hi = e4m3_encode(bf16_hi(p) / s);
-  return lo | (hi << 8);
-}
-
 // Codes of a bf16 pair in a row whose scale is 0 (every element is +-0): the sign only.
 __device__ __forceinline__ uint32_t fp8_pair_zero(uint32_t p) { return ((p >> 8) & 0x80u) | ((p >> 16) & 0x8000u); }
 
-__device__ __forceinline__ u32x2 fp8_vec(u32x4 v, float s, bool zero_row) {
+// Row quantizer state: the scale s and r = RN(1/s) for the division.
+struct RowDiv {
+  float s, r;
+  bool zero, tiny;
+};
+
+__device__ __forceinline__ RowDiv row_div(float amax) {
+  RowDiv d;
+  d.s = amax / 448.0f;
+  d.zero = !(d.s > 0.0f);
+  d.tiny = !div_rn_ok(d.s);
+  d.r = 1.0f / d.s;
+  return d;
+}
+
+__device__ __forceinline__ float qdiv(float x, const RowDiv& d) { return d.tiny ? x / d.s : div_rn(x, d.s, d.r); }
+
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t p, const RowDiv& d) {
+  return e4m3_pack2(qdiv(bf16_lo(p), d), qdiv(bf16_hi(p), d));
+}
+
+__device__ __forceinline__ u32x2 fp8_vec(u32x4 v, const RowDiv& d) {
   u32x2 o;
-  if (zero_row) {
+  if (d.zero) {
     o.x = fp8_pair_zero(v.x) | (fp8_pair_zero(v.y) << 16);
     o.y = fp8_pair_zero(v.z) | (fp8_pair_zero(v.w) << 16);
     return o;
   }
-  o.x = fp8_pair(v.x, s) | (fp8_pair(v.y, s) << 16);
-  o.y = fp8_pair(v.z, s) | (fp8_pair(v.w, s) << 16);
+  o.x = fp8_pair(v.x, d) | (fp8_pair(v.y, d) << 16);
+  o.y = fp8_pair(v.z, d) | (fp8_pair(v.w, d) << 16);
   return o;
 }
 
@@ -64,13 +79,12 @@ __global__ __launch_bounds__(256) void k_quant_fp8_row(const uint16_t* __restric
       }
     }
     amax = wave_max(amax);
-    const float s = amax / 448.0f;
-    if (lane == 0) xs[row] = s;
-    const bool zero_row = !(s > 0.0f);
+    const RowDiv d = row_div(amax);
+    if (lane == 0) xs[row] = d.s;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int64_t j = lane + 64 * i;
-      if (j < nv) qr[j] = fp8_vec(v[i], s, zero_row);
+      if (j < nv) qr[j] = fp8_vec(v[i], d);
     }
   } else {
     for (int64_t j = lane; j < nv; j += 64) {
@@ -78,10 +92,9 @@ __global__ __launch_bounds__(256) void k_quant_fp8_row(const uint16_t* __restric
       amax = pair_absmax(v.x, pair_absmax(v.y, pair_absmax(v.z, pair_absmax(v.w, amax))));
     }
     amax = wave_max(amax);
-    const float s = amax / 448.0f;
-    if (lane == 0) xs[row] = s;
-    const bool zero_row = !(s > 0.0f);
-    for (int64_t j = lane; j < nv; j += 64) qr[j] = fp8_vec(xr[j], s, zero_row);
+    const RowDiv d = row_div(amax);
+    if (lane == 0) xs[row] = d.s;
+    for (int64_t j = lane; j < nv; j += 64) qr[j] = fp8_vec(xr[j], d);
   }
 }
 
@@ -106,27 +119,33 @@ hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t
 struct Nvfp4Block {
   uint32_t sf;   // E4M3 block scale
   float d;       // dec(sf) * g
+  float rd;      // RN(1 / d)
   float dsf;     // dec(sf)
 };
 
-__device__ __forceinline__ Nvfp4Block nvfp4_block_scale(const uint32_t (&p)[8], float g, float c6g) {
+// g: global scale; c6g = 6 g (fp32) and rc6g = RN(1 / c6g), both from the host.
+__device__ __forceinline__ Nvfp4Block nvfp4_block_scale(const uint32_t (&p)[8], float g, float c6g, float rc6g) {
   float bmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) bmax = pair_absmax(p[i], bmax);
-  const float u = bmax / c6g;
+  const float u = div_rn_ok(c6g) ? div_rn(bmax, c6g, rc6g) : bmax / c6g;
   Nvfp4Block b;
-  b.sf = e4m3_mag(__float_as_uint(u));
+  b.sf = e4m3_pack2(u, 0.0f) & 0xFFu;
   b.dsf = e4m3_decode(b.sf);
   b.d = b.dsf * g;
+  b.rd = 1.0f / b.d;
   return b;
 }
 
 // E2M1 codes of the 16 values; element 2j in the low nibble of byte j.
-__device__ __forceinline__ u32x2 nvfp4_codes(const uint32_t (&p)[8], float d) {
+__device__ __forceinline__ u32x2 nvfp4_codes(const uint32_t (&p)[8], const Nvfp4Block& s) {
   uint32_t c[8];
-  if (d > 0.0f) {
+  if (div_rn_ok(s.d)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e2m1_encode(bf16_lo(p[i]) / d) | (e2m1_encode(bf16_hi(p[i]) / d) << 4);
+    for (int i = 0; i < 8; ++i) c[i] = e2m1_pack2(div_rn(bf16_lo(p[i]), s.d, s.rd), div_rn(bf16_hi(p[i]), s.d, s.rd));
+  } else if (s.d > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e2m1_pack2(bf16_lo(p[i]) / s.d, bf16_hi(p[i]) / s.d);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = ((p[i] >> 12) & 0x8u) | ((p[i] >> 24) & 0x80u);
@@ -145,35 +164,46 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
 }
 
 __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict__ x, int64_t nblocks, float g,
-                                                     float c6g, uint8_t* __restrict__ xq,
+                                                     float c6g, float rc6g, uint8_t* __restrict__ xq,
                                                      uint8_t* __restrict__ xbs) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   uint32_t p[8];
   load_block(x, b, p);
-  const Nvfp4Block s = nvfp4_block_scale(p, g, c6g);
-  reinterpret_cast<u32x2*>(xq)[b] = nvfp4_codes(p, s.d);
+  const Nvfp4Block s = nvfp4_block_scale(p, g, c6g, rc6g);
+  reinterpret_cast<u32x2*>(xq)[b] = nvfp4_codes(p, s);
   xbs[b] = (uint8_t)s.sf;
 }
 
 // Same quantization; each quantized value e2m1(code) * dec(sf) is written as bf16.
 // The product has at most 6 significant bits, so the bf16 value is exact.
+// Eight packed E2M1 codes (one dword, element 2j in the low nibble of byte j) to
+// eight bf16 values code * dsf: the FP4 converter at scale 1 gives the code values
+// exactly, the product with an E4M3 value is exact (<= 6 significant bits), and
+// the upper halves of the fp32 results are the bf16 values.
+__device__ __forceinline__ uint32_t bf16_pair_of(f32x2 v, float m) {
+  return (__float_as_uint(v[0] * m) >> 16) | (__float_as_uint(v[1] * m) & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ void expand_word(uint32_t w, float dsf, uint32_t* o) {
+  o[0] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0), dsf);
+  o[1] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), dsf);
+  o[2] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), dsf);
+  o[3] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), dsf);
+}
+
 __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __restrict__ x, int64_t nblocks,
-                                                            float g, float c6g, uint16_t* __restrict__ xe) {
+                                                            float g, float c6g, float rc6g,
+                                                            uint16_t* __restrict__ xe) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   uint32_t p[8];
   load_block(x, b, p);
-  const Nvfp4Block s = nvfp4_block_scale(p, g, c6g);
-  const u32x2 c = nvfp4_codes(p, s.d);
+  const Nvfp4Block s = nvfp4_block_scale(p, g, c6g, rc6g);
+  const u32x2 c = nvfp4_codes(p, s);
   uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t byte = ((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu;
-    const float lo = e2m1_decode(byte & 0xFu) * s.dsf;
-    const float hi = e2m1_decode(byte >> 4) * s.dsf;
-    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-  }
+  expand_word(c.x, s.dsf, o);
+  expand_word(c.y, s.dsf, o + 4);
   u32x4* dst = reinterpret_cast<u32x4*>(xe + b * 16);
   dst[0] = u32x4{o[0], o[1], o[2], o[3]};
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
@@ -182,18 +212,18 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __re
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, uint8_t* xq, uint8_t* xbs,
                               hipStream_t stream) {
   const int64_t nb = M * (K / 16);
-  const float c6g = 6.0f * g;
-  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, g, c6g, xq,
-                     xbs);
+  const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
+  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, g, c6g, rc6g,
+                     xq, xbs);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, uint16_t* xe,
                                      hipStream_t stream) {
   const int64_t nb = M * (K / 16);
-  const float c6g = 6.0f * g;
+  const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
   hipLaunchKernelGGL(k_quant_nvfp4_expand, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, g,
-                     c6g, xe);
+                     c6g, rc6g, xe);
   return hipGetLastError();
 }
 

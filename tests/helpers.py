@@ -40,4 +40,9 @@ def adversarial_rows(K, seed=0):
     rows.append((r.view(np.uint32) >> 16).astype(np.uint16))             # huge
     r = (rng.standard_normal(K) * 1e-30).astype(np.float32)
     rows.append((r.view(np.uint32) >> 16).astype(np.uint16))             # tiny (normal, near subnormal scale)
+    r = (rng.standard_normal(K) * 2.0).astype(np.float32)
+    b = (r.view(np.uint32) >> 16).astype(np.uint16)
+    b[::5] = 0x0000
+    b[2::5] = 0x8000
+    rows.append(b)                                                         # exact +-0 among normal values
     return np.stack(rows)

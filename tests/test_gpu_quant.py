@@ -113,7 +113,7 @@ def test_quant_nvfp4_weights(name):
     assert_nvfp4_equal(w, g)
 
 
-@pytest.mark.parametrize("g", [1e-4, 0.01, 0.25, 3.0, 1e6])
+@pytest.mark.parametrize("g", [1e-30, 1e-4, 0.01, 0.25, 3.0, 1e6, 1e37, 5e37])
 def test_quant_nvfp4_adversarial(g):
     # small g saturates block scales at 448; huge g underflows them to 0 (signed-zero codes)
     say("quant_act_nvfp4 adversarial", g)
