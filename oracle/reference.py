@@ -98,10 +98,19 @@ def gemm_gamma(K):
     return math.ceil(K / 16) * 2.0 ** -24
 
 
+# Share of the 2e-3 Frobenius budget left for arithmetic error once the bf16
+# rounding of a large output (about 1.66e-3 relative) is paid.
+FROB_ARITH = 2e-3 - 1.66e-3
+
+
 def check_gemm(y_bits, ref, abs_sum, K, extra_abs=None, max_ulps=4.0, frob_tol=2e-3, gamma=None):
     """Acceptance test of a bf16 GEMM output against its float64 reference.
 
-    * relative Frobenius error ||y - ref|| / ||ref|| <= frob_tol over the whole output;
+    * relative Frobenius error ||y - ref|| / ||ref|| <= max(frob_tol, frob_round +
+      FROB_ARITH) over the whole output, where frob_round is the same norm for the
+      reference itself rounded to bf16 (the error of an exactly computed output).
+      On large outputs frob_round is about 1.66e-3 and the limit is frob_tol; on a
+      handful of outputs the rounding of single values can exceed frob_tol alone;
     * per element |y - ref| <= max_ulps * ulp_bf16(ref) + gamma * sum_k |a_k w_k|
       (plus gamma * the low-rank magnitude sum when given).  ``gamma`` is the
       accumulation floor of the arithmetic under test; it defaults to the fp32
@@ -123,5 +132,9 @@ def check_gemm(y_bits, ref, abs_sum, K, extra_abs=None, max_ulps=4.0, frob_tol=2
     fails = int(np.count_nonzero(err > bound))
     only_floor = int(np.count_nonzero((err > max_ulps * ulp) & (err <= bound)))
     max_ulp_err = float(np.max(err / ulp)) if err.size else 0.0
-    ok = (frob <= frob_tol) and fails == 0 and bool(np.all(np.isfinite(y)))
-    return dict(ok=ok, frob=frob, fails=fails, only_floor=only_floor, max_ulp_err=max_ulp_err)
+    rounded = bf16_bits_to_f32(f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    frob_round = float(np.linalg.norm(rounded - ref) / den) if den > 0 else 0.0
+    frob_limit = max(frob_tol, frob_round + FROB_ARITH)
+    ok = (frob <= frob_limit) and fails == 0 and bool(np.all(np.isfinite(y)))
+    return dict(ok=ok, frob=frob, frob_round=frob_round, fails=fails, only_floor=only_floor,
+                max_ulp_err=max_ulp_err)

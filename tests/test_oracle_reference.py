@@ -148,6 +148,19 @@ def test_check_gemm_detects_planted_errors():
     assert not check_gemm(y3, ref, abs_sum * 0, 16)["ok"]
 
 
+def test_check_gemm_frobenius_on_few_outputs():
+    # One output whose own bf16 rounding costs 0.49 ulp (3.8e-3 relative, above the
+    # 2e-3 budget): the correctly rounded value and the other neighbour pass, a
+    # value 1.5 ulps away fails.
+    ulp1 = 2.0 ** -7
+    ref = np.array([[1.0 + 0.49 * ulp1]])
+    zero = np.zeros_like(ref)
+    for v, ok in ((1.0, True), (1.0 + ulp1, True), (1.0 + 2 * ulp1, False)):
+        res = check_gemm(f32_to_bf16_bits(np.array([[v]], F32)), ref, zero, 16)
+        assert res["ok"] is ok, (v, res)
+    assert abs(res["frob_round"] - 0.49 * ulp1 / ref[0, 0]) < 1e-12
+
+
 def test_gamma_floor_covers_blocked_fp32_accumulation():
     # fp32 accumulation of exact products, in blocks of 32 (one MFMA-sized chunk at a time)
     rng = np.random.default_rng(15)
