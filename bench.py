@@ -153,6 +153,9 @@ def main():
                     "tflops": round(tf, 1), f"pct_{peak}_peak": round(100 * tf / PEAK_TFLOPS[peak], 2)}
         if k != "fp8r":
             parts[k]["pct_bf16_peak"] = round(100 * tf / PEAK_TFLOPS["bf16"], 2)
+        if e["R"]:
+            lr_flops = 2.0 * e["M"] * e["R"] * (e["K"] + e["N"])
+            parts[k]["tflops_incl_lowrank"] = round((e["flops"] + lr_flops) / (ms * 1e-3) / 1e12, 1)
     kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for k, (n, t) in kern.items() if n}
 
     # ---------------------------------------------------------------- roofline (dominant kernel)

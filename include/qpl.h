@@ -160,11 +160,12 @@ typedef enum {
   QPL_KERNEL_GEMM_FP8R = 3,
   QPL_KERNEL_GEMM_NVFP4 = 4,
   QPL_KERNEL_GEMM_NVFP4_LOWRANK = 5, /* nvfp4 GEMM with the low-rank epilogue */
-  QPL_KERNEL_LOWRANK_PREP = 6,      /* x L1 and the factor transposes */
+  QPL_KERNEL_LOWRANK_PREP = 6,      /* low-rank factor transposes */
   QPL_KERNEL_DEQUANT = 7,
   QPL_KERNEL_AMAX = 8,
   QPL_KERNEL_WEIGHT_BF16 = 9,       /* nvfp4 weight expansion inside qlinear_nvfp4 */
-  QPL_KERNEL_COUNT = 10
+  QPL_KERNEL_QUANT_NVFP4_LOWRANK = 10, /* nvfp4 quantize fused with x L1 (qlinear_nvfp4, R > 0) */
+  QPL_KERNEL_COUNT = 11
 } qpl_kernel;
 
 void qpl_timing_enable(int on);

@@ -21,7 +21,7 @@ EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp
 
 # qpl_kernel order of include/qpl.h
 KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_bf16", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
-           "lowrank_prep", "dequant", "amax", "weight_bf16")
+           "lowrank_prep", "dequant", "amax", "weight_bf16", "quant_nvfp4_lowrank")
 
 _lib = None
 

@@ -33,7 +33,7 @@
 //   current slab's fragments as each one is used for the last time;
 // * operands are swapped (the MFMA computes y^T), so each lane ends with four
 //   consecutive output columns of a row and stores them as one 8-byte segment.
-#include "qpl_device.h"
+#include "qpl_dma.h"
 #include "qpl_internal.h"
 
 namespace qpl {
@@ -45,16 +45,9 @@ constexpr int SLAB = 256 * SROW;    // 16 KB per operand per stage
 constexpr int STAGE = 2 * SLAB;     // x slab then W slab
 constexpr int NST = 4;              // stages in the ring
 constexpr int DMA_PER_STAGE = 8;    // per wavefront: 4 x-slab and 4 W-slab instructions of 1 KB
-constexpr uint32_t kOutOfRange = 0x40000000u;
-constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // gfx9 buffer descriptor word 3: raw 32-bit elements
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int soff(int r, int c) { return r * SROW + ((c ^ swz(r)) << 4); }
-
-// s_waitcnt with one counter constrained (gfx9 encoding: vmcnt bits 3:0 and 15:14,
-// expcnt 6:4, lgkmcnt 11:8).
-#define QPL_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-#define QPL_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 typedef f32x16 Acc[4][4];
 
@@ -65,28 +58,11 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 }
 
-// Buffer descriptor (in scalar registers) over the tile's rows of a row-major
-// byte matrix: reads past the tile's last valid row return zero.
+// Buffer descriptor over the tile's rows of a row-major byte matrix: reads past
+// the tile's last valid row return zero.
 __device__ __forceinline__ u32x4 tile_desc(const void* base, int64_t rows_left, int64_t pitch) {
   const int64_t rows = rows_left < 256 ? rows_left : 256;
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  u32x4 d;
-  d.x = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  d.y = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  d.z = __builtin_amdgcn_readfirstlane((uint32_t)(rows * pitch));
-  d.w = kRawBufferWord3;
-  return d;
-}
-
-// 16 bytes per lane from global memory into LDS: lane l writes LDS bytes
-// [lds_addr + 16 l, + 16); an offset past the descriptor's size writes zeros.  It
-// is inline assembly so that the compiler does not wait for these loads at every
-// LDS read: the pipeline counts them itself (QPL_WAIT_VMCNT).
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, u32x4 desc, int soffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soffset)
-               : "memory");
+  return make_desc(base, rows * pitch);
 }
 
 // Operand fragments.  fp8: a 32x32x64 MFMA operand (32 K-bytes per lane, two
@@ -290,8 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   tile_coords(tiles_m, tiles_n, m0, n0);
   lscale[0][t] = m0 + t < M ? sa[m0 + t] : 0.0f;
   lscale[1][t] = n0 + t < N ? sb[n0 + t] : 0.0f;
-  const uint32_t lbase =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds));
+  const uint32_t lbase = lds_address(lds);
   Acc acc;
   zero_acc(acc);
   gemm_pass<Fp8Mma>(acc, lds, lbase, tile_desc(A + m0 * K, M - m0, K), tile_desc(B + n0 * K, N - n0, K), (int)K,
@@ -311,8 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wm = wv >> 1, wn = wv & 1;
   int64_t m0, n0;
   tile_coords(tiles_m, tiles_n, m0, n0);
-  const uint32_t lbase =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds));
+  const uint32_t lbase = lds_address(lds);
   Acc acc;
   zero_acc(acc);
   const int kb = (int)(2 * K);
@@ -332,42 +306,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   store_tile(acc, wm, wn, lane, m0, n0, M, N, Y, [&](int) { return oscale; },
              [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
-}
-
-// T = x L1 for the low-rank branch: one workgroup per 32 rows x 32 rank columns,
-// the four wavefronts split K and their partial sums meet in LDS.  T is stored
-// split into a bf16 high part and a bf16 remainder ([hi | lo], KL columns per row)
-// so the GEMM epilogue can apply it on the bf16 MFMA while keeping ~16 bits.
-__global__ __launch_bounds__(256) void k_lowrank_t(const uint16_t* __restrict__ x, const uint16_t* __restrict__ l1t,
-                                                   int64_t M, int64_t K, int64_t rpad, int64_t kl,
-                                                   uint16_t* __restrict__ t_out) {
-  __shared__ float red[4][16 * 64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.x * 32, c0 = (int64_t)blockIdx.y * 32;
-  const int64_t row = m0 + (lane & 31);
-  f32x16 acc = {};
-  const int64_t nsteps = K / 16;
-  for (int64_t s = wv; s < nsteps; s += 4) {
-    const int64_t k = s * 16 + g * 8;
-    bf16x8 a = {};
-    if (row < M) a = *reinterpret_cast<const bf16x8*>(x + row * K + k);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(l1t + (c0 + (lane & 31)) * K + k);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) red[wv][r * 64 + lane] = acc[r];
-  __syncthreads();
-  if (wv != 0) return;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float v = ((red[0][r * 64 + lane] + red[1][r * 64 + lane]) + red[2][r * 64 + lane]) + red[3][r * 64 + lane];
-    const int64_t m = m0 + (r >> 2) * 8 + g * 4 + (r & 3);
-    if (m >= M) continue;
-    const uint32_t hi = f32_to_bf16(v);
-    const uint32_t lo = f32_to_bf16(v - __uint_as_float(hi << 16));
-    t_out[m * kl + c0 + (lane & 31)] = (uint16_t)hi;
-    t_out[m * kl + rpad + c0 + (lane & 31)] = (uint16_t)lo;
-  }
 }
 
 // l1t[r][k] = L1[k][r] (zero for r >= R); l2t[n][c] = L2[c mod rpad][n] (zero past R).
@@ -409,17 +347,12 @@ hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscal
   return hipGetLastError();
 }
 
-hipError_t launch_lowrank_prep(const uint16_t* x, const uint16_t* l1, const uint16_t* l2, int64_t M, int64_t K,
-                               int64_t N, int64_t R, int64_t kl, uint16_t* l1t, uint16_t* t, uint16_t* l2t,
-                               hipStream_t stream) {
+hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,
+                               uint16_t* l1t, uint16_t* l2t, hipStream_t stream) {
   const int64_t rpad = kl / 2;
   const int64_t ntr = rpad * K + N * kl;
   hipLaunchKernelGGL(k_lowrank_transpose, dim3((unsigned)((ntr + 255) / 256)), dim3(256), 0, stream, l1, l2, K, N, R,
                      rpad, kl, l1t, l2t);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_lowrank_t, dim3((unsigned)((M + 31) / 32), (unsigned)(rpad / 32)), dim3(256), 0, stream, x,
-                     l1t, M, K, rpad, kl, t);
   return hipGetLastError();
 }
 

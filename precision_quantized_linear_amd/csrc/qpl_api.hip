@@ -271,26 +271,30 @@ QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint16_t* xe = reinterpret_cast<uint16_t*>(base + L.off[0]);
   uint16_t* we = reinterpret_cast<uint16_t*>(base + L.off[1]);
-  if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, xe, st)))) !=
-      QPL_OK)
-    return s;
-  // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue
-  if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st)))) !=
-      QPL_OK)
-    return s;
   qpl::LowRank lr;
   if (R > 0) {
+    // SVDQuant branch: factor layouts, then the activation quantize fused with T = x L1
     const int64_t kl = 2 * rank_pad(R);
     uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[2]);
     uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[3]);
     uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
     if ((s = launched(Timed(QPL_KERNEL_LOWRANK_PREP, st)(
-             qpl::launch_lowrank_prep(x, lora_down, lora_up, M, K, N, R, kl, l1t, t, l2t, st)))) != QPL_OK)
+             qpl::launch_lowrank_prep(lora_down, lora_up, K, N, R, kl, l1t, l2t, st)))) != QPL_OK)
+      return s;
+    if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
+             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, l1t, kl, xe, t, st)))) != QPL_OK)
       return s;
     lr.t = t;
     lr.l2t = l2t;
     lr.kl = kl;
+  } else if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(
+                  qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, xe, st)))) != QPL_OK) {
+    return s;
   }
+  // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue
+  if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st)))) !=
+      QPL_OK)
+    return s;
   return launched(Timed(R > 0 ? QPL_KERNEL_GEMM_NVFP4_LOWRANK : QPL_KERNEL_GEMM_NVFP4, st)(
       qpl::launch_gemm_nvfp4(xe, we, gscale, M, K, N, lr, y, st)));
 }

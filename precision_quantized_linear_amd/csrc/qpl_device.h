@@ -18,6 +18,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
@@ -85,6 +86,13 @@ __device__ __forceinline__ float div_rn(float x, float s, float r) {
   return __builtin_isinf(q0) ? q0 : q;
 }
 
+// div_rn for quotients known to stay below 2^127 in magnitude (no overflow check).
+__device__ __forceinline__ float div_rn_finite(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+}
+
 // Whether s lies in the range where div_rn is exact.
 __device__ __forceinline__ bool div_rn_ok(float s) { return s >= 0x1p-64f && s <= 0x1p64f; }
 
@@ -99,6 +107,12 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
 }
 
+// e4m3_pack2 for magnitudes below 464, which the converter rounds like the
+// saturating encoder (nothing above 448 but below 464 is a different code).
+__device__ __forceinline__ uint32_t e4m3_pack2_small(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
 // E2M1 codes of two floats with the hardware FP4 converter at scale 1 (round to
 // nearest even, saturating at 6; matched the bit-level encoder on 2^28 random
 // finite values including midpoints).  Inputs are clamped to +-6 first so that an
@@ -108,6 +122,41 @@ __device__ __forceinline__ uint32_t e2m1_pack2(float a, float b) {
   const float ca = __builtin_amdgcn_fmed3f(a, -6.0f, 6.0f);
   const float cb = __builtin_amdgcn_fmed3f(b, -6.0f, 6.0f);
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ca, cb, 1.0f, 0) & 0xFFu;
+}
+
+// e2m1_pack2 for finite inputs (the converter saturates them by itself).
+__device__ __forceinline__ uint32_t e2m1_pack2_finite(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+// div_rn without the sign fix: the quotient of a zero is +0 whatever the sign of x
+// (for values whose sign of zero does not matter).  Same range conditions.
+__device__ __forceinline__ float div_rn_nosign(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_fmaf(e, r, q0);
+}
+
+// Running maximum of bf16 magnitudes kept as two 16-bit integers: non-negative
+// floats order like their bit patterns, so an integer max of |x| bits is a float max.
+__device__ __forceinline__ uint32_t absmax_acc(uint32_t m, uint32_t pair) {
+  const u16x2 a = __builtin_bit_cast(u16x2, pair & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, m)));
+}
+
+// The float value of the larger half of an absmax_acc accumulator.
+__device__ __forceinline__ float absmax_value(uint32_t m) {
+  const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+  return __uint_as_float((lo > hi ? lo : hi) << 16);
+}
+
+// Eight E2M1 codes (finite inputs, pairs in order) packed into one word with the
+// converter's byte select: pair i lands in byte i, first value in the low nibble.
+__device__ __forceinline__ uint32_t e2m1_pack8_finite(const float (&q)[8]) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
 }
 
 // Wave-wide max of a non-negative float (64 lanes).

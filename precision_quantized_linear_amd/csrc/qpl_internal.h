@@ -8,6 +8,15 @@
 
 namespace qpl {
 
+// Per block-scale code sf (E4M3, 0..127): d = dec(sf) * g and RN(1 / d) in fp32,
+// computed on the host for one global scale g and passed by value to the nvfp4
+// quantizers.
+struct Nvfp4ScaleTable {
+  float d[128];
+  float rd[128];
+};
+Nvfp4ScaleTable nvfp4_scale_table(float g);
+
 hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                                 hipStream_t stream);
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, uint8_t* xq,
@@ -16,6 +25,11 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, 
 // (exact: at most 6 significant bits) instead of packed codes.
 hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, uint16_t* xe,
                                      hipStream_t stream);
+// The same, fused with the low-rank down-projection: t [M, kl] bf16 receives
+// T = x L1 as [hi | lo] halves of kl / 2 columns each; l1t [kl / 2, K] is L1
+// transposed (zero past R); kl / 2 is a multiple of 32, at most 128.
+hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const uint16_t* l1t,
+                                             int64_t kl, uint16_t* xe, uint16_t* t, hipStream_t stream);
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
                                hipStream_t stream);
@@ -38,8 +52,9 @@ struct LowRank {
 hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
                              LowRank lr, uint16_t* y, hipStream_t stream);
 
-hipError_t launch_lowrank_prep(const uint16_t* x, const uint16_t* l1, const uint16_t* l2, int64_t M, int64_t K,
-                               int64_t N, int64_t R, int64_t kl, uint16_t* l1t, uint16_t* t, uint16_t* l2t,
-                               hipStream_t stream);
+// Factor layouts for the low-rank branch: l1t [kl / 2, K] = L1^T and l2t [N, kl] =
+// [L2^T | L2^T], both zero past R.
+hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,
+                               uint16_t* l1t, uint16_t* l2t, hipStream_t stream);
 
 }  // namespace qpl

@@ -6,9 +6,11 @@
 // Numerics follow the schemes of the Diffusers guide "BFL (fp8r / nvfp4)" (intro
 // bullets) as read in qpl.h: fp8r s = amax / 448, codes E4M3(x / s); nvfp4
 // sf = E4M3(bmax / (6 g)), d = dec(sf) * g, codes E2M1(x / d).  Divisions are
-// IEEE correctly rounded (the library is built with correctly rounded fp32
-// division and without contraction), so codes match an fp32 reference bit for bit.
-#include "qpl_device.h"
+// correctly rounded (a reciprocal with one fma correction, or IEEE division where
+// that is not exact), so codes match an fp32 reference bit for bit.
+#include <cmath>
+
+#include "qpl_dma.h"
 #include "qpl_internal.h"
 
 namespace qpl {
@@ -18,8 +20,8 @@ namespace qpl {
 // vectors per lane stay in registers between the amax pass and the encode pass;
 // VPT == 0 streams the row twice (rows longer than 64 * 8 * 24 elements).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float pair_absmax(uint32_t p, float m) {
-  return fmaxf(m, fmaxf(bf16_lo(p & 0x7FFF7FFFu), bf16_hi(p & 0x7FFF7FFFu)));
+__device__ __forceinline__ uint32_t vec_absmax(const u32x4& v, uint32_t m) {
+  return absmax_acc(absmax_acc(absmax_acc(absmax_acc(m, v.x), v.y), v.z), v.w);
 }
 
 // Codes of a bf16 pair in a row whose scale is 0 (every element is +-0): the sign only.
@@ -40,10 +42,17 @@ __device__ __forceinline__ RowDiv row_div(float amax) {
   return d;
 }
 
-__device__ __forceinline__ float qdiv(float x, const RowDiv& d) { return d.tiny ? x / d.s : div_rn(x, d.s, d.r); }
+// |x| <= amax, so |x / s| stays at 448 up to rounding: no overflow, and no clamp
+// needed before the converter.
+__device__ __forceinline__ float qdiv(float x, const RowDiv& d) {
+  return d.tiny ? x / d.s : div_rn_finite(x, d.s, d.r);
+}
 
-__device__ __forceinline__ uint32_t fp8_pair(uint32_t p, const RowDiv& d) {
-  return e4m3_pack2(qdiv(bf16_lo(p), d), qdiv(bf16_hi(p), d));
+// E4M3 codes of two bf16 pairs: pair a in bits 15:0, pair b in bits 31:16 (the
+// converter's word select fills the halves; no clamp, see qdiv).
+__device__ __forceinline__ uint32_t fp8_word(uint32_t a, uint32_t b, const RowDiv& d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(qdiv(bf16_lo(a), d), qdiv(bf16_hi(a), d), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qdiv(bf16_lo(b), d), qdiv(bf16_hi(b), d), lo, true);
 }
 
 __device__ __forceinline__ u32x2 fp8_vec(u32x4 v, const RowDiv& d) {
@@ -53,8 +62,8 @@ __device__ __forceinline__ u32x2 fp8_vec(u32x4 v, const RowDiv& d) {
     o.y = fp8_pair_zero(v.z) | (fp8_pair_zero(v.w) << 16);
     return o;
   }
-  o.x = fp8_pair(v.x, d) | (fp8_pair(v.y, d) << 16);
-  o.y = fp8_pair(v.z, d) | (fp8_pair(v.w, d) << 16);
+  o.x = fp8_word(v.x, v.y, d);
+  o.y = fp8_word(v.z, v.w, d);
   return o;
 }
 
@@ -67,7 +76,8 @@ __global__ __launch_bounds__(256) void k_quant_fp8_row(const uint16_t* __restric
   const int64_t nv = K >> 3;
   const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * K);
   u32x2* qr = reinterpret_cast<u32x2*>(xq + row * K);
-  float amax = 0.0f;
+  uint32_t am = 0;
+  float amax;
   if constexpr (VPT > 0) {
     u32x4 v[VPT];
 #pragma unroll
@@ -75,10 +85,10 @@ __global__ __launch_bounds__(256) void k_quant_fp8_row(const uint16_t* __restric
       const int64_t j = lane + 64 * i;
       if (j < nv) {
         v[i] = __builtin_nontemporal_load(xr + j);
-        amax = pair_absmax(v[i].x, pair_absmax(v[i].y, pair_absmax(v[i].z, pair_absmax(v[i].w, amax))));
+        am = vec_absmax(v[i], am);
       }
     }
-    amax = wave_max(amax);
+    amax = wave_max(absmax_value(am));
     const RowDiv d = row_div(amax);
     if (lane == 0) xs[row] = d.s;
 #pragma unroll
@@ -87,11 +97,8 @@ __global__ __launch_bounds__(256) void k_quant_fp8_row(const uint16_t* __restric
       if (j < nv) qr[j] = fp8_vec(v[i], d);
     }
   } else {
-    for (int64_t j = lane; j < nv; j += 64) {
-      u32x4 v = xr[j];
-      amax = pair_absmax(v.x, pair_absmax(v.y, pair_absmax(v.z, pair_absmax(v.w, amax))));
-    }
-    amax = wave_max(amax);
+    for (int64_t j = lane; j < nv; j += 64) am = vec_absmax(xr[j], am);
+    amax = wave_max(absmax_value(am));
     const RowDiv d = row_div(amax);
     if (lane == 0) xs[row] = d.s;
     for (int64_t j = lane; j < nv; j += 64) qr[j] = fp8_vec(xr[j], d);
@@ -121,39 +128,61 @@ struct Nvfp4Block {
   float d;       // dec(sf) * g
   float rd;      // RN(1 / d)
   float dsf;     // dec(sf)
+  bool fast;     // d in div_rn's range and every |x / d| finite
 };
 
-// g: global scale; c6g = 6 g (fp32) and rc6g = RN(1 / c6g), both from the host.
-__device__ __forceinline__ Nvfp4Block nvfp4_block_scale(const uint32_t (&p)[8], float g, float c6g, float rc6g) {
-  float bmax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) bmax = pair_absmax(p[i], bmax);
+// Block scale from the block's largest magnitude.  c6g = 6 g (fp32) and
+// rc6g = RN(1 / c6g) come from the host, and so does the table of
+// d = dec(sf) * g and RN(1 / d) for every block-scale code (tab_d, tab_rd in LDS).
+__device__ __forceinline__ Nvfp4Block nvfp4_scale(float bmax, float c6g, float rc6g, const float* tab_d,
+                                                  const float* tab_rd) {
   const float u = div_rn_ok(c6g) ? div_rn(bmax, c6g, rc6g) : bmax / c6g;
   Nvfp4Block b;
   b.sf = e4m3_pack2(u, 0.0f) & 0xFFu;
   b.dsf = e4m3_decode(b.sf);
-  b.d = b.dsf * g;
-  b.rd = 1.0f / b.d;
+  b.d = tab_d[b.sf];
+  b.rd = tab_rd[b.sf];
+  b.fast = div_rn_ok(b.d) && bmax * b.rd < 0x1p126f;
   return b;
 }
 
-// E2M1 codes of the 16 values; element 2j in the low nibble of byte j.
-__device__ __forceinline__ u32x2 nvfp4_codes(const uint32_t (&p)[8], const Nvfp4Block& s) {
-  uint32_t c[8];
-  if (div_rn_ok(s.d)) {
+// E2M1 codes of eight values (four bf16 pairs) under block scale s: byte i holds
+// pair i, first value in the low nibble.  SIGNED_ZERO: a zero keeps its sign in
+// the code (the codes are an output); otherwise the sign of a zero may be lost
+// (the codes are only expanded to values, where +-0 are the same).
+template <bool SIGNED_ZERO>
+__device__ __forceinline__ uint32_t nvfp4_word(const uint32_t* p, const Nvfp4Block& s) {
+  float q[8];
+  if (s.fast) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e2m1_pack2(div_rn(bf16_lo(p[i]), s.d, s.rd), div_rn(bf16_hi(p[i]), s.d, s.rd));
-  } else if (s.d > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e2m1_pack2(bf16_lo(p[i]) / s.d, bf16_hi(p[i]) / s.d);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = ((p[i] >> 12) & 0x8u) | ((p[i] >> 24) & 0x80u);
+    for (int i = 0; i < 4; ++i) {
+      q[2 * i] = SIGNED_ZERO ? div_rn_finite(bf16_lo(p[i]), s.d, s.rd) : div_rn_nosign(bf16_lo(p[i]), s.d, s.rd);
+      q[2 * i + 1] = SIGNED_ZERO ? div_rn_finite(bf16_hi(p[i]), s.d, s.rd) : div_rn_nosign(bf16_hi(p[i]), s.d, s.rd);
+    }
+    return e2m1_pack8_finite(q);
   }
-  u32x2 o;
-  o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-  return o;
+  if (s.d > 0.0f) {
+    // d outside div_rn's range or quotients that may overflow: IEEE division, clamped
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[2 * i] = __builtin_amdgcn_fmed3f(bf16_lo(p[i]) / s.d, -6.0f, 6.0f);
+      q[2 * i + 1] = __builtin_amdgcn_fmed3f(bf16_hi(p[i]) / s.d, -6.0f, 6.0f);
+    }
+    return e2m1_pack8_finite(q);
+  }
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w |= (((p[i] >> 12) & 0x8u) | ((p[i] >> 24) & 0x80u)) << (8 * i);
+  return w;
+}
+
+// Copy the per-code table from the kernel arguments into LDS (whole workgroup).
+__device__ __forceinline__ void load_scale_table(const Nvfp4ScaleTable& t, float* tab_d, float* tab_rd) {
+  for (int i = threadIdx.x; i < 128; i += blockDim.x) {
+    tab_d[i] = t.d[i];
+    tab_rd[i] = t.rd[i];
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t b, uint32_t (&p)[8]) {
@@ -163,15 +192,23 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
   p[4] = v1.x; p[5] = v1.y; p[6] = v1.z; p[7] = v1.w;
 }
 
-__global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict__ x, int64_t nblocks, float g,
-                                                     float c6g, float rc6g, uint8_t* __restrict__ xq,
-                                                     uint8_t* __restrict__ xbs) {
+__device__ __forceinline__ float block_absmax(const uint32_t* p, int n) {
+  uint32_t m = 0;
+  for (int i = 0; i < n; ++i) m = absmax_acc(m, p[i]);
+  return absmax_value(m);
+}
+
+__global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                     float c6g, float rc6g, Nvfp4ScaleTable tab,
+                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xbs) {
+  __shared__ float tab_d[128], tab_rd[128];
+  load_scale_table(tab, tab_d, tab_rd);
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   uint32_t p[8];
   load_block(x, b, p);
-  const Nvfp4Block s = nvfp4_block_scale(p, g, c6g, rc6g);
-  reinterpret_cast<u32x2*>(xq)[b] = nvfp4_codes(p, s);
+  const Nvfp4Block s = nvfp4_scale(block_absmax(p, 8), c6g, rc6g, tab_d, tab_rd);
+  reinterpret_cast<u32x2*>(xq)[b] = u32x2{nvfp4_word<true>(p, s), nvfp4_word<true>(p + 4, s)};
   xbs[b] = (uint8_t)s.sf;
 }
 
@@ -193,28 +230,236 @@ __device__ __forceinline__ void expand_word(uint32_t w, float dsf, uint32_t* o) 
 }
 
 __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __restrict__ x, int64_t nblocks,
-                                                            float g, float c6g, float rc6g,
+                                                            float c6g, float rc6g, Nvfp4ScaleTable tab,
                                                             uint16_t* __restrict__ xe) {
+  __shared__ float tab_d[128], tab_rd[128];
+  load_scale_table(tab, tab_d, tab_rd);
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   uint32_t p[8];
   load_block(x, b, p);
-  const Nvfp4Block s = nvfp4_block_scale(p, g, c6g, rc6g);
-  const u32x2 c = nvfp4_codes(p, s);
+  const Nvfp4Block s = nvfp4_scale(block_absmax(p, 8), c6g, rc6g, tab_d, tab_rd);
   uint32_t o[8];
-  expand_word(c.x, s.dsf, o);
-  expand_word(c.y, s.dsf, o + 4);
+  expand_word(nvfp4_word<false>(p, s), s.dsf, o);
+  expand_word(nvfp4_word<false>(p + 4, s), s.dsf, o + 4);
   u32x4* dst = reinterpret_cast<u32x4*>(xe + b * 16);
   dst[0] = u32x4{o[0], o[1], o[2], o[3]};
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// nvfp4 quantize-and-expand fused with the SVDQuant low-rank down-projection
+// T = x L1 (the pages fuse the down-projection into the quantization kernel so
+// that the 16-bit branch does not read x a second time: "Bringing Nunchaku 4-bit
+// Diffusion Inference to Diffusers", section "Background: SVDQuant and
+// Nunchaku").  The branch takes the unquantized x.
+//
+// A workgroup (eight wavefronts) owns rpw <= 32 consecutive rows, rpw chosen so that
+// there is about one workgroup per CU, and walks K in tiles of TK columns.  Each tile of x
+// (32 x TK bf16) and of L1^T (rpad x TK) moves global -> LDS without register
+// staging, S - 1 tiles ahead; a load instruction covers whole 512- or 256-byte row
+// segments, so HBM sees full lines.  Per tile, the wavefronts
+//   1. quantize their eighth of the x tile from LDS (lane l holds eight values,
+//      lanes l and l ^ 1 one 16-element block) and store the bf16 expansion
+//      straight to global memory, again as whole row segments;
+//   2. run the bf16 MFMA 32x32x16 over their eighth of the tile's k range,
+//      reading both operands from LDS, into per-wave partial sums of T.
+// Two wavefronts per SIMD keep the quantizer's arithmetic busy.  The eight partial
+// sums meet in LDS at the end, in a fixed order; T is stored as [hi | lo] bf16
+// halves (row stride kl = 2 rpad) for the GEMM epilogue.
+//
+// LDS layout: 16-byte chunk c of tile row r sits at chunk slot c ^ (r & 15) of
+// the row, so the MFMA operand reads (16 rows, one chunk) hit 16 different bank
+// groups; the load instructions fill slots in order and fetch the chunk each slot
+// holds.
+template <int NCT>
+struct LrTile {
+  static constexpr int TK = NCT <= 2 ? 256 : 128;  // k per tile
+  static constexpr int CPR = TK / 8;                // 16-byte chunks per tile row
+  static constexpr int XB = 32 * TK * 2;            // x tile bytes
+  static constexpr int LB = 32 * NCT * TK * 2;      // L1^T tile bytes
+  static constexpr int SB = XB + LB;                // stage bytes
+  static constexpr int S = (NCT == 1 || NCT == 3) ? 4 : 3;  // stages in the ring (<= 128 KB, 144 KB for NCT 2)
+  static constexpr int NW = 8;                      // wavefronts
+  static constexpr int XI = XB / 1024 / NW;         // x loads (and xe stores) per wave per tile, 1 KB each
+  static constexpr int LI = LB / 1024 / NW;         // L1^T loads per wave per tile
+  static constexpr int DW = XI + LI;
+};
+
+template <int NCT>
+__global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                               float c6g, float rc6g, Nvfp4ScaleTable tab,
+                                                               const uint16_t* __restrict__ l1t, int64_t kl,
+                                                               int rpw, uint16_t* __restrict__ xe,
+                                                               uint16_t* __restrict__ t_out) {
+  using C = LrTile<NCT>;
+  constexpr int TK = C::TK, CPR = C::CPR, S = C::S, XI = C::XI, LI = C::LI, NW = C::NW;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S * C::SB];
+  __shared__ float tab_d[128], tab_rd[128];
+  load_scale_table(tab, tab_d, tab_rd);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t m0 = (int64_t)blockIdx.x * rpw;
+  const int64_t rows = M - m0 < rpw ? M - m0 : rpw;
+  const uint32_t pitch = (uint32_t)(K * 2);
+  const u32x4 dx = make_desc(x + m0 * K, rows * pitch);
+  const u32x4 dl = make_desc(l1t, (int64_t)32 * NCT * pitch);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(xe + m0 * K, (short)0, (int)(rows * pitch),
+                                                                      (int)kRawBufferWord3);
+  const uint32_t lbase = lds_address(lds);
+  const int ntiles = (int)((K + TK - 1) / TK);
+
+  // Geometry of this lane's slot in load instruction j of the wave (the same for
+  // every tile): tile row, chunk held, byte offset within the tile.
+  auto slot_row = [&](int j, int per) { return ((wv * per + j) * 64 + lane) / CPR; };
+  auto slot_chunk = [&](int j, int per) {
+    const int sl = (wv * per + j) * 64 + lane;
+    return (sl % CPR) ^ ((sl / CPR) & 15);
+  };
+  // Offsets valid for tile kt: chunks past K read zero (rows past M do through dx).
+  auto voff = [&](int r, int c, int kt) -> uint32_t {
+    return (int64_t)kt * TK + 8 * c < K ? (uint32_t)r * pitch + 16u * (uint32_t)c : kOutOfRange;
+  };
+  auto issue = [&](int kt) {
+    const uint32_t st = lbase + (uint32_t)((kt % S) * C::SB);
+    const int soff = kt * TK * 2;
+#pragma unroll
+    for (int j = 0; j < XI; ++j)
+      dma16(st + (uint32_t)((wv * XI + j) * 1024), voff(slot_row(j, XI), slot_chunk(j, XI), kt), dx, soff);
+#pragma unroll
+    for (int j = 0; j < LI; ++j)
+      dma16(st + C::XB + (uint32_t)((wv * LI + j) * 1024), voff(slot_row(j, LI), slot_chunk(j, LI), kt), dl, soff);
+  };
+
+  f32x16 acc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
+
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue(t);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    // tile kt has landed: loads and stores retire in order, and the ones issued
+    // after tile kt's loads are the later tiles' loads and this wave's stores
+    const int after = kt < S - 1 ? kt : S - 1;
+    switch (after) {
+      case 0: QPL_WAIT_VMCNT((S - 2) * C::DW); break;
+      case 1: QPL_WAIT_VMCNT((S - 2) * C::DW + XI); break;
+      case 2: QPL_WAIT_VMCNT((S - 2) * C::DW + 2 * XI); break;
+      default: QPL_WAIT_VMCNT((S - 2) * C::DW + 3 * XI); break;
+    }
+    QPL_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();  // every wave's part of tile kt is in LDS; tile kt - 1's buffer is free
+    issue(kt + S - 1);             // past the end: out-of-range offsets, zeros into an unused buffer
+    const uint8_t* xt = lds + (kt % S) * C::SB;
+    const uint8_t* lt = xt + C::XB;
+
+    // 1. quantize and expand this wave's part of the x tile
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+      const int r = slot_row(j, XI), c = slot_chunk(j, XI);
+      if ((wv * XI + j) * 64 / CPR >= rows) {
+        // rows past the workgroup's: no work, but the store is still issued (and
+        // dropped) so that every wave retires the same number of operations
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, re, (int)kOutOfRange, 0, 0);
+        continue;
+      }
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xt + ((wv * XI + j) * 64 + lane) * 16);
+      const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = absmax_acc(m, p[i]);
+      // the other half of the block is in lane l ^ 1 (chunk c ^ 1 of the same row)
+      m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+      const Nvfp4Block sc = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
+      uint32_t o[4];
+      expand_word(nvfp4_word<false>(p, sc), sc.dsf, o);
+      const uint32_t so = voff(r, c, kt);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, re,
+                                             so == kOutOfRange ? (int)kOutOfRange : (int)(so + (uint32_t)kt * TK * 2),
+                                             0, 0);
+    }
+
+    // 2. T += x_tile L1t_tile^T over this wave's part of the k range
+#pragma unroll
+    for (int ks = 0; ks < TK / 16 / NW; ++ks) {
+      const int ch = wv * (CPR / NW) + 2 * ks + (lane >> 5);  // chunk of the 32x32x16 operand
+      const int r = lane & 31;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(xt + (r * CPR + (ch ^ (r & 15))) * 16);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const int rb = 32 * c + r;
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(lt + (rb * CPR + (ch ^ (rb & 15))) * 16);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      }
+    }
+  }
+  QPL_WAIT_VMCNT(0);
+  __syncthreads();
+
+  // partial sums of the eight waves -> T: p_w = acc_w + acc_(w+4), then ((p0 + p1) + p2) + p3
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [4][c][4][64]
+  if (wv >= 4) {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        red[(((wv - 4) * NCT + c) * 4 + q) * 64 + lane] =
+            f32x4{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]};
+  }
+  __syncthreads();
+  if (wv < 4) {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4& r = red[((wv * NCT + c) * 4 + q) * 64 + lane];
+        r = f32x4{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]} + r;
+      }
+  }
+  __syncthreads();
+  // acc[c][r] is T[m0 + (r / 4) * 8 + (lane / 32) * 4 + r % 4][32 c + lane % 32]
+  const int64_t rpad = kl / 2;
+  for (int e = threadIdx.x; e < NCT * 4 * 64; e += 64 * NW) {
+    const int c = e / 256, q = (e / 64) % 4, l = e % 64;
+    f32x4 v = red[((0 * NCT + c) * 4 + q) * 64 + l];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v = v + red[((w * NCT + c) * 4 + q) * 64 + l];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mr = q * 8 + (l >> 5) * 4 + i;
+      if (mr >= rows) continue;
+      const int64_t m = m0 + mr;
+      const uint32_t hi = f32_to_bf16(v[i]);
+      const uint32_t lo = f32_to_bf16(v[i] - __uint_as_float(hi << 16));
+      t_out[m * kl + 32 * c + (l & 31)] = (uint16_t)hi;
+      t_out[m * kl + rpad + 32 * c + (l & 31)] = (uint16_t)lo;
+    }
+  }
+}
+
+// Host side of the nvfp4 scale rule: d = dec(sf) * g and RN(1 / d) for every
+// block-scale code, in fp32 as on the device (the host build does not contract or
+// flush either).  Code 0x7F (NaN) is never produced.
+static float e4m3_value_host(uint32_t c) {
+  const int e = (int)((c >> 3) & 15u), m = (int)(c & 7u);
+  return e ? std::ldexp(1.0f + (float)m / 8.0f, e - 7) : std::ldexp((float)m / 8.0f, -6);
+}
+
+Nvfp4ScaleTable nvfp4_scale_table(float g) {
+  Nvfp4ScaleTable t;
+  for (uint32_t c = 0; c < 128; ++c) {
+    const float d = c == 0x7Fu ? 0.0f : e4m3_value_host(c) * g;
+    t.d[c] = d;
+    t.rd[c] = 1.0f / d;
+  }
+  return t;
 }
 
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, uint8_t* xq, uint8_t* xbs,
                               hipStream_t stream) {
   const int64_t nb = M * (K / 16);
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, g, c6g, rc6g,
-                     xq, xbs);
+  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, c6g, rc6g,
+                     nvfp4_scale_table(g), xq, xbs);
   return hipGetLastError();
 }
 
@@ -222,8 +467,37 @@ hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, fl
                                      hipStream_t stream) {
   const int64_t nb = M * (K / 16);
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  hipLaunchKernelGGL(k_quant_nvfp4_expand, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, g,
-                     c6g, rc6g, xe);
+  hipLaunchKernelGGL(k_quant_nvfp4_expand, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, c6g,
+                     rc6g, nvfp4_scale_table(g), xe);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const uint16_t* l1t,
+                                             int64_t kl, uint16_t* xe, uint16_t* t, hipStream_t stream) {
+  // buffer offsets are 32-bit: the L1^T tile rows (at most 128) times the pitch
+  if (K > (int64_t{1} << 21)) return hipErrorInvalidValue;
+  const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
+  const Nvfp4ScaleTable tab = nvfp4_scale_table(g);
+  // about one workgroup per CU (256 on MI355X), at most 32 rows each
+  const int64_t rpw64 = (M + 255) / 256;
+  const int rpw = (int)(rpw64 < 32 ? rpw64 : 32);
+  const dim3 grid((unsigned)((M + rpw - 1) / rpw)), block(512);
+  switch (kl / 64) {  // rpad / 32
+    case 1:
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<1>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<2>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      break;
+    case 3:
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<3>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      break;
+    case 4:
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<4>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -236,15 +510,13 @@ __global__ __launch_bounds__(256) void k_amax_bf16(const uint16_t* __restrict__ 
                                                    float* __restrict__ amax) {
   __shared__ float part[4];
   const int64_t nv = n >> 3;
-  float m = 0.0f;
+  uint32_t am = 0;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nv; j += (int64_t)gridDim.x * 256) {
-    const u32x4 v = xv[j];
-    m = pair_absmax(v.x, pair_absmax(v.y, pair_absmax(v.z, pair_absmax(v.w, m))));
-  }
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nv; j += (int64_t)gridDim.x * 256)
+    am = vec_absmax(xv[j], am);
   if (blockIdx.x == 0 && threadIdx.x == 0)
-    for (int64_t i = nv * 8; i < n; ++i) m = fmaxf(m, bf16_lo(x[i] & 0x7FFFu));
-  m = wave_max(m);
+    for (int64_t i = nv * 8; i < n; ++i) am = absmax_acc(am, x[i]);
+  float m = wave_max(absmax_value(am));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {

@@ -116,6 +116,8 @@ NVFP4_SHAPES = [
     ("nvfp4_mlp_down_cfg", 257, 1024, 300),
     ("svdq_w4a4", 300, 448, 264),               # low-rank branch, ragged
     ("svdq_w4a4", 256, 512, 256),
+    ("svdq_w4a4", 37, 272, 72),                 # K % 32 == 16: half a k step in the fused x L1
+    ("svdq_w4a4", 1, 16, 1),                    # one block, one row
 ]
 
 
@@ -138,15 +140,17 @@ def test_qlinear_nvfp4_full(name):
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("R", [1, 20, 64, 100])
-def test_qlinear_nvfp4_lowrank_ranks(R):
-    d = make("svdq_w4a4", M=130, K=256, N=200)
+@pytest.mark.parametrize("R,M,K", [(1, 130, 256), (20, 130, 256), (64, 130, 256), (100, 130, 256), (128, 45, 208),
+                                   (33, 17, 48)])
+def test_qlinear_nvfp4_lowrank_ranks(R, M, K):
+    # every padded rank width (32, 64, 96, 128 columns of T), ragged M and K % 32 == 16
+    d = make("svdq_w4a4", M=M, K=K, N=200)
     rng = np.random.default_rng(R)
     from synthetic import bf16_round
-    d["l1"] = bf16_round((rng.standard_normal((256, R)) * 0.05).astype(np.float32))
+    d["l1"] = bf16_round((rng.standard_normal((K, R)) * 0.05).astype(np.float32))
     d["l2"] = bf16_round((rng.standard_normal((R, 200)) * 0.05).astype(np.float32))
-    say("qlinear_nvfp4 rank", R)
-    r = nvfp4_case(d, np.arange(130), np.float32(0.01))
+    say("qlinear_nvfp4 rank", R, M, K)
+    r = nvfp4_case(d, np.arange(M), np.float32(0.01))
     assert r["ok"], r
 
 
