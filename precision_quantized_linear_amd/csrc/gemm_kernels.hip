@@ -15,7 +15,8 @@
 // (V_MFMA_F32_32X32X16_BF16).  The global factor input_scale * weight_scale_2
 // and the optional SVDQuant low-rank term (Nunchaku post, "Background: SVDQuant
 // and Nunchaku": the up-projection fused into the GEMM) are applied to the fp32
-// accumulators before the single bf16 rounding.
+// accumulators before the single bf16 rounding; the low-rank pass accumulates
+// (T / gscale) L2 into the same accumulators, and the epilogue scales by gscale.
 //
 // Pipeline (both GEMMs):
 // * a 256-thread workgroup (4 wavefronts, 2 x 2) owns a 256 x 256 output tile; a
@@ -33,6 +34,8 @@
 //   current slab's fragments as each one is used for the last time;
 // * operands are swapped (the MFMA computes y^T), so each lane ends with four
 //   consecutive output columns of a row and stores them as one 8-byte segment.
+#include <type_traits>
+
 #include "qpl_dma.h"
 #include "qpl_internal.h"
 
@@ -57,6 +60,10 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 }
+
+// Rows of a 256-row tile that lie inside the matrix (rows_left = rows from the
+// tile's first row to the matrix end).
+__device__ __forceinline__ int64_t M_rows(int64_t rows_left) { return rows_left < 256 ? rows_left : 256; }
 
 // Buffer descriptor over the tile's rows of a row-major byte matrix: reads past
 // the tile's last valid row return zero.
@@ -94,95 +101,26 @@ struct Bf16Mma {
   }
 };
 
-// One pass of the pipeline over K: acc += W_tile x_tile^T in the D^T layout
-// (acc[i][j] row index = W row, column index = x row).  dx / dw are descriptors
-// over the tile's x rows and W rows (same pitch, kbytes valid bytes per row).
-// Ends with every load drained and all waves past a barrier, so LDS is free.
-template <class T>
-__device__ __forceinline__ void gemm_pass(Acc& acc, uint8_t* lds, uint32_t lbase, u32x4 dx, u32x4 dw, int pitch,
-                                          int kbytes, int wv, int wm, int wn, int lane) {
-  uint32_t vbase[4];
-  int cb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // instruction q of this wave covers slab rows 16 (4 wv + q) .. + 15; lane l
-    // fills physical chunk l % 4 of row ... + l / 4, i.e. logical chunk (l % 4) ^ swz
-    const int row = 16 * (4 * wv + q) + (lane >> 2);
-    cb[q] = ((lane & 3) ^ swz(row)) * 16;
-    vbase[q] = (uint32_t)(row * pitch + cb[q]);
-  }
-  const int nk = (kbytes + SROW - 1) / SROW;
-  auto voff = [&](int s, int q) -> uint32_t { return (s < nk && s * SROW + cb[q] < kbytes) ? vbase[q] : kOutOfRange; };
-  auto dma = [&](int s, int q, bool w_slab) {
-    const uint32_t dst = lbase + (s % NST) * STAGE + (w_slab ? SLAB : 0) + (4 * wv + q) * 1024;
-    dma16(dst, voff(s, q), w_slab ? dw : dx, s * SROW);
-  };
-#pragma unroll
-  for (int s = 0; s < NST; ++s)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      dma(s, q, false);
-      dma(s, q, true);
-    }
-  QPL_WAIT_VMCNT((NST - 1) * DMA_PER_STAGE);
-  __builtin_amdgcn_s_barrier();
-  typename T::Frag fw[T::SUB][4], fx[T::SUB][4];
-#pragma unroll
-  for (int u = 0; u < T::SUB; ++u)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fw[u][i] = T::read(lds + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
-      fx[u][i] = T::read(lds, wm * 128 + i * 32 + (lane & 31), u, lane);
-    }
-  constexpr int NMMA = 16 * T::SUB;
-  for (int kt = 0; kt < nk; ++kt) {
-    // slab kt + 1 has landed for every wave, and every wave is done with step kt - 1
-    QPL_WAIT_LGKM0();
-    QPL_WAIT_VMCNT((NST - 2) * DMA_PER_STAGE);
-    __builtin_amdgcn_s_barrier();
-    const uint8_t* nx = lds + ((kt + 1) % NST) * STAGE;
-    const int sref = kt + NST;  // refill the buffer slab kt used with slab kt + NST
-#pragma unroll
-    for (int u = 0; u < T::SUB; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = T::mma(fw[u][i], fx[u][j], acc[i][j]);
-          const int k = 16 * u + 4 * i + j;
-          if (i == 3) fx[u][j] = T::read(nx, wm * 128 + j * 32 + (lane & 31), u, lane);
-          if (j == 3) fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
-          // spread this step's 8 refill loads over its MFMAs
-          constexpr int every = NMMA / DMA_PER_STAGE;
-          if (k % every == every - 1) {
-            const int d = k / every;
-            dma(sref, d & 3, d >= 4);
-          }
-        }
-  }
-  QPL_WAIT_VMCNT(0);
-  QPL_WAIT_LGKM0();
-  __builtin_amdgcn_s_barrier();
-}
-
-// Tile order.  Workgroups are dispatched round-robin over the 8 XCDs and each XCD
-// has its own L2, so each XCD gets a contiguous run of the tile sequence; the
-// sequence walks groups of GROUP_M tile-rows column by column, so the ~32 tiles an
-// XCD runs at once form a 4 x 8 block that shares 4 activation slabs and 8 weight
-// slabs in that XCD's L2.
+// Tile order.  The tile sequence walks groups of GROUP_M tile-rows column by column.
+// Workgroups are dispatched round-robin over the 8 XCDs and each XCD has its own
+// L2, so in every round of the persistent loop the 32 workgroups of one XCD take a
+// contiguous run of 32 tiles of the sequence: a 4 x 8 block that shares 4
+// activation slabs and 8 weight slabs in that XCD's L2.
 constexpr int GROUP_M = 4;
 
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
-  const int T = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
+__device__ __forceinline__ void tile_coords(int s, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
   const int per_group = GROUP_M * tiles_n;
-  const int g = b / per_group;
+  const int g = s / per_group;
   const int first_m = g * GROUP_M;
   const int gm = min(tiles_m - first_m, GROUP_M);
-  const int r = b - g * per_group;
+  const int r = s - g * per_group;
   m0 = (int64_t)(first_m + r % gm) * 256;
   n0 = (int64_t)(r / gm) * 256;
+}
+
+// Position in the tile sequence of workgroup b's i-th tile (nwg workgroups).
+__device__ __forceinline__ int tile_seq(int i, int b, int nwg) {
+  return (nwg & 7) == 0 ? i * nwg + (b & 7) * (nwg >> 3) + (b >> 3) : i * nwg + b;
 }
 
 // Two floats to packed bf16, round to nearest even (V_CVT_PK_BF16_F32; checked
@@ -196,116 +134,278 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return u;
 }
 
-// Store the tile: y[m][n .. n+3] = bf16((acc * rs(m)) * cs(n .. n+3)) as 8-byte
-// segments.  Interior tiles (and N % 4 == 0) take a path without per-element
-// checks; edge tiles check rows and columns and fall back to element stores.
+// What the GEMM kernels multiply.  Pass 1: rows of x (a) and of W (w), pitch1
+// bytes apart, kbytes1 valid bytes each.  Pass 2 (the low-rank up-projection):
+// rows of [T_hi | T_lo] and [L2^T | L2^T].
+struct GemmArgs {
+  const uint8_t* a;
+  const uint8_t* w;
+  const uint8_t* a2;
+  const uint8_t* w2;
+  int64_t M, N;
+  int pitch1, kbytes1, pitch2, kbytes2;
+  int tiles_m, tiles_n, ntiles, nwg;
+};
+
+constexpr int NSTORE = 32;           // 16-byte output stores per wave per tile (fast path)
+constexpr int SCALE_BUF = 2048;      // per tile parity: s_x of the tile's 256 rows, then s_w of its 256 columns
+
+// Epilogue of one tile: y = bf16((acc * rs(m)) * cs(n)).  acc[i][j] holds y^T: its
+// element r at lane l is row m = m0 + 128 wm + 32 j + l % 32, column
+// n = n0 + 128 wn + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4.  Lanes l and l + 32
+// exchange halves (V_PERMLANE32_SWAP) so that each lane holds eight consecutive
+// columns of one row and stores them as one 16-byte segment.  Returns the number
+// of store instructions left in flight: NSTORE on the interior path, 0 on the
+// edge path (which checks every element and drains its stores).
 template <class RowScale, class ColScale>
-__device__ __forceinline__ void store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
-                                           int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
-                                           const ColScale& cs) {
-  float fr[4];
-  f32x4 fc[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fr[j] = rs(wm * 128 + j * 32 + (lane & 31));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) fc[i][g] = cs(wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4);
-  auto seg = [&](int i, int j, int g) {
-    const f32x16& a = acc[i][j];
-    u32x2 o;
-    o.x = pack_bf16((a[g * 4 + 0] * fr[j]) * fc[i][g][0], (a[g * 4 + 1] * fr[j]) * fc[i][g][1]);
-    o.y = pack_bf16((a[g * 4 + 2] * fr[j]) * fc[i][g][2], (a[g * 4 + 3] * fr[j]) * fc[i][g][3]);
-    return o;
-  };
-  const int64_t mb = m0 + wm * 128 + (lane & 31), nb = n0 + wn * 128 + (lane >> 5) * 4;
-  if (m0 + 256 <= M && n0 + 256 <= N && (N & 3) == 0) {
-    uint16_t* yb = y + mb * N + nb;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<u32x2*>(yb + (int64_t)(j * 32) * N + i * 32 + g * 8) = seg(i, j, g);
-    return;
-  }
-  const bool vec = (N & 3) == 0;
+__device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
+                                          int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
+                                          const ColScale& cs) {
+  const bool fast = m0 + 256 <= M && n0 + 256 <= N && (N & 7) == 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t m = mb + j * 32;
-    if (m >= M) continue;
+    const int mr = wm * 128 + j * 32 + (lane & 31);
+    const float fr = rs(mr);
+    const int64_t m = m0 + mr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t n = nb + i * 32 + g * 8;
-        const u32x2 o = seg(i, j, g);
-        if (vec && n < N) {
-          *reinterpret_cast<u32x2*>(y + m * N + n) = o;
-        } else {
-          const uint32_t w[2] = {o.x, o.y};
+      for (int gp = 0; gp < 2; ++gp) {
+        uint32_t w[2][2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) y[m * N + n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        for (int h = 0; h < 2; ++h) {
+          const int g = 2 * gp + h;
+          const f32x4 fc = cs(wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4);
+          const f32x16& a = acc[i][j];
+          w[h][0] = pack_bf16((a[g * 4 + 0] * fr) * fc[0], (a[g * 4 + 1] * fr) * fc[1]);
+          w[h][1] = pack_bf16((a[g * 4 + 2] * fr) * fc[2], (a[g * 4 + 3] * fr) * fc[3]);
+        }
+        const auto r0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+        const u32x4 v = u32x4{r0[0], r1[0], r0[1], r1[1]};
+        const int64_t n = n0 + wn * 128 + i * 32 + (2 * gp + (lane >> 5)) * 8;
+        if (fast) {
+          *reinterpret_cast<u32x4*>(y + m * N + n) = v;
+        } else if (m < M) {
+          const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+          if ((N & 7) == 0 && n + 8 <= N) {
+            *reinterpret_cast<u32x4*>(y + m * N + n) = v;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+              if (n + c < N) y[m * N + n + c] = (uint16_t)(e[c >> 1] >> (16 * (c & 1)));
+          }
         }
       }
   }
+  if (fast) return NSTORE;
+  QPL_WAIT_VMCNT(0);
+  return 0;
+}
+
+// Persistent GEMM: workgroup b walks its tiles (tile_seq) one after the other,
+// and the slabs of all of them form one stream through the LDS ring: the loads
+// for the next tile's first slabs are issued while the current tile's last slabs
+// are multiplied, and the current tile's output stores drain while the next
+// tile's MFMAs run.
+//
+// Wait accounting (vector memory operations of a wave retire in issue order): at
+// the top of iteration g, slab g + 1 must have landed; issued after its loads are
+// the loads of slabs g + 2 and g + 3 (2 D) and the output stores of the
+// epilogues that ran after iterations g - 3 .. g - 1.
+//
+// ROWCOL: fp8r output scales s_x[m] s_w[n], moved into LDS by two extra dword
+// loads per wave per slab (real for a tile's first slab, out of range otherwise).
+// Otherwise the output scale is gscale.  LOWRANK: pass 2 continues the same
+// accumulation with T / gscale and L2 (the quantizer stores T divided by gscale),
+// so y = bf16(gscale (x_q w_q^T + (T / gscale) L2)).
+template <class T, bool ROWCOL, bool LOWRANK>
+__device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* __restrict__ sa,
+                                                const float* __restrict__ sb, float gscale,
+                                                uint16_t* __restrict__ Y) {
+  constexpr int D = ROWCOL ? 10 : 8;  // loads per wave per slab
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[ROWCOL ? 3 * SCALE_BUF : 16];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wv >> 1, wn = wv & 1;
+  const int b = blockIdx.x;
+  const uint32_t lbase = lds_address(lds);
+  const uint32_t sbase = lds_address(lsc);
+
+  int nt = 0;
+  while (tile_seq(nt, b, p.nwg) < p.ntiles) ++nt;
+  const int nk1 = (p.kbytes1 + SROW - 1) / SROW;
+  const int nk2 = LOWRANK ? (p.kbytes2 + SROW - 1) / SROW : 0;
+  const int nk = nk1 + nk2;
+
+  // lane geometry of the slab loads: instruction q of this wave fills slab rows
+  // 16 (4 wv + q) .. + 15; lane l writes physical chunk l % 4 of row + l / 4,
+  // which holds logical chunk (l % 4) ^ swz(row)
+  int lrow[4], cb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lrow[q] = 16 * (4 * wv + q) + (lane >> 2);
+    cb[q] = ((lane & 3) ^ swz(lrow[q])) * 16;
+  }
+
+  // The load stream: slab ks of the workgroup's tile ti, advanced one slab per
+  // call of next_src (tile coordinates recomputed at tile boundaries only).
+  struct SlabSrc {
+    u32x4 dx, dw, ds;
+    int pitch, kb, koff, stage, tpar;
+    bool first, valid;
+  };
+  int s_ti = 0, s_ks = 0, s_stage = 0;
+  int64_t s_m0 = 0, s_n0 = 0;
+  if (nt > 0) tile_coords(tile_seq(0, b, p.nwg), p.tiles_m, p.tiles_n, s_m0, s_n0);
+  auto next_src = [&]() {
+    SlabSrc r;
+    r.valid = s_ti < nt;
+    r.stage = s_stage;
+    r.first = s_ks == 0;
+    r.tpar = s_ti & 1;
+    const bool pass2 = LOWRANK && s_ks >= nk1;
+    r.pitch = pass2 ? p.pitch2 : p.pitch1;
+    r.kb = r.valid ? (pass2 ? p.kbytes2 : p.kbytes1) : 0;
+    r.koff = (pass2 ? s_ks - nk1 : s_ks) * SROW;
+    const int64_t rm = M_rows(p.M - s_m0), rn = M_rows(p.N - s_n0);
+    r.dx = make_desc((pass2 ? p.a2 : p.a) + s_m0 * r.pitch, rm * r.pitch);
+    r.dw = make_desc((pass2 ? p.w2 : p.w) + s_n0 * r.pitch, rn * r.pitch);
+    if constexpr (ROWCOL) {
+      const bool row = wv < 2;
+      r.ds = make_desc(row ? sa + s_m0 : sb + s_n0, (row ? rm : rn) * 4);
+    }
+    s_stage = s_stage == NST - 1 ? 0 : s_stage + 1;
+    if (++s_ks == nk) {
+      s_ks = 0;
+      ++s_ti;
+      if (s_ti < nt) tile_coords(tile_seq(s_ti, b, p.nwg), p.tiles_m, p.tiles_n, s_m0, s_n0);
+    }
+    return r;
+  };
+  auto issue = [&](const SlabSrc& s, int d) {
+    if (d < 8) {
+      const int q = d & 3;
+      const bool wslab = d >= 4;
+      const uint32_t dst = lbase + s.stage * STAGE + (wslab ? SLAB : 0) + (4 * wv + q) * 1024;
+      const uint32_t vo = s.koff + cb[q] < s.kb ? (uint32_t)(lrow[q] * s.pitch + cb[q]) : kOutOfRange;
+      dma16(dst, vo, wslab ? s.dw : s.dx, s.koff);
+    } else {
+      // scale vectors of a tile: wave w moves 128 floats of s_x (w = 0, 1) or s_w
+      // (w = 2, 3), 64 per instruction; other slabs load nothing into a spare area
+      const int h = d - 8;
+      const bool real = s.valid && s.first;
+      const uint32_t dst = sbase + (real ? s.tpar * SCALE_BUF : 2 * SCALE_BUF) + wv * 512 + h * 256;
+      const uint32_t vo = real ? (uint32_t)(((wv & 1) * 128 + h * 64 + lane) * 4) : kOutOfRange;
+      dma4(dst, vo, s.ds, 0);
+    }
+  };
+
+  // prologue: the first NST slabs of the stream, then slab 0's fragments
+#pragma unroll
+  for (int s0 = 0; s0 < NST; ++s0) {
+    const SlabSrc src = next_src();
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(src, d);
+  }
+  QPL_WAIT_VMCNT((NST - 1) * D);
+  __builtin_amdgcn_s_barrier();
+  typename T::Frag fw[T::SUB][4], fx[T::SUB][4];
+#pragma unroll
+  for (int u = 0; u < T::SUB; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fw[u][i] = T::read(lds + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
+      fx[u][i] = T::read(lds, wm * 128 + i * 32 + (lane & 31), u, lane);
+    }
+
+  int st1 = 0, st2 = 0, st3 = 0;  // stores left in flight after iterations g - 1, g - 2, g - 3
+  int cur = 0;                     // stage of the slab being multiplied
+  constexpr int NMMA = 16 * T::SUB;
+  // One slab: wait for the next slab, multiply this one while reading the next
+  // one's fragments (FRAGS) and issuing the loads of slab + NST.  Before the
+  // epilogue (and the low-rank rescale) the next fragments are read afterwards
+  // instead (read_frags), so that they do not occupy registers meanwhile.
+  auto read_frags = [&]() {
+    const uint8_t* nx = lds + cur * STAGE;
+#pragma unroll
+    for (int u = 0; u < T::SUB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
+        fx[u][i] = T::read(nx, wm * 128 + i * 32 + (lane & 31), u, lane);
+      }
+  };
+  auto step = [&](Acc& acc, auto frags) {
+    constexpr bool FRAGS = decltype(frags)::value;
+    QPL_WAIT_LGKM0();
+    const int extra = st1 + st2 + st3;
+    if (extra == 0) {
+      QPL_WAIT_VMCNT((NST - 2) * D);
+    } else if (extra == NSTORE) {
+      QPL_WAIT_VMCNT((NST - 2) * D + NSTORE);
+    } else {
+      QPL_WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_barrier();  // the next slab is in LDS for every wave; the previous slab's stage is free
+    const SlabSrc src = next_src();
+    cur = cur == NST - 1 ? 0 : cur + 1;
+    const uint8_t* nx = lds + cur * STAGE;
+#pragma unroll
+    for (int u = 0; u < T::SUB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = T::mma(fw[u][i], fx[u][j], acc[i][j]);
+          const int k = 16 * u + 4 * i + j;
+          if (FRAGS && i == 3) fx[u][j] = T::read(nx, wm * 128 + j * 32 + (lane & 31), u, lane);
+          if (FRAGS && j == 3) fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
+          // spread the D loads of slab + NST over this slab's MFMAs
+#pragma unroll
+          for (int d = 0; d < D; ++d)
+            if (k == (d * NMMA) / D) issue(src, d);
+        }
+    st3 = st2;
+    st2 = st1;
+    st1 = 0;
+  };
+
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  for (int ti = 0; ti < nt; ++ti) {
+    Acc acc;
+    zero_acc(acc);
+    for (int kt = 0; kt < nk - 1; ++kt) step(acc, Yes{});
+    step(acc, No{});
+    int64_t m0, n0;
+    tile_coords(tile_seq(ti, b, p.nwg), p.tiles_m, p.tiles_n, m0, n0);
+    if constexpr (ROWCOL) {
+      const float* ls = reinterpret_cast<const float*>(lsc + (ti & 1) * SCALE_BUF);
+      st1 = store_tile(
+          acc, wm, wn, lane, m0, n0, p.M, p.N, Y, [&](int r) { return ls[r]; },
+          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); });
+    } else {
+      st1 = store_tile(acc, wm, wn, lane, m0, n0, p.M, p.N, Y, [&](int) { return gscale; },
+                       [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
+    }
+    if (st1 == 0) st2 = st3 = 0;
+    read_frags();
+  }
+  QPL_WAIT_VMCNT(0);
+  QPL_WAIT_LGKM0();
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_fp8r(
-    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
-    const float* __restrict__ sb, int64_t M, int64_t K, int64_t N, uint16_t* __restrict__ Y, int tiles_m,
-    int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
-  __shared__ __attribute__((aligned(16))) float lscale[2][256];  // the tile's row scales and column scales
-  const int t = threadIdx.x, lane = t & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
-  int64_t m0, n0;
-  tile_coords(tiles_m, tiles_n, m0, n0);
-  lscale[0][t] = m0 + t < M ? sa[m0 + t] : 0.0f;
-  lscale[1][t] = n0 + t < N ? sb[n0 + t] : 0.0f;
-  const uint32_t lbase = lds_address(lds);
-  Acc acc;
-  zero_acc(acc);
-  gemm_pass<Fp8Mma>(acc, lds, lbase, tile_desc(A + m0 * K, M - m0, K), tile_desc(B + n0 * K, N - n0, K), (int)K,
-                    (int)K, wv, wm, wn, lane);
-  store_tile(acc, wm, wn, lane, m0, n0, M, N, Y, [&](int r) { return lscale[0][r]; },
-             [&](int c) { return *reinterpret_cast<const f32x4*>(&lscale[1][c]); });
+    GemmArgs p, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ Y) {
+  gemm_persistent<Fp8Mma, true, false>(p, sa, sb, 1.0f, Y);
 }
 
 template <bool LOWRANK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, float gscale, int64_t M, int64_t K, int64_t N,
-    const uint16_t* __restrict__ T, const uint16_t* __restrict__ L2t, int64_t KL, uint16_t* __restrict__ Y,
-    int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
-  const int t = threadIdx.x, lane = t & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
-  int64_t m0, n0;
-  tile_coords(tiles_m, tiles_n, m0, n0);
-  const uint32_t lbase = lds_address(lds);
-  Acc acc;
-  zero_acc(acc);
-  const int kb = (int)(2 * K);
-  gemm_pass<Bf16Mma>(acc, lds, lbase, tile_desc(A + m0 * K, M - m0, kb), tile_desc(W + n0 * K, N - n0, kb), kb, kb,
-                     wv, wm, wn, lane);
-  float oscale = gscale;
-  if constexpr (LOWRANK) {
-    // SVDQuant up-projection: acc = g * acc + [T_hi | T_lo] [L2^T | L2^T]^T, in fp32
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] *= gscale;
-    const int lb = (int)(2 * KL);
-    gemm_pass<Bf16Mma>(acc, lds, lbase, tile_desc(T + m0 * KL, M - m0, lb), tile_desc(L2t + n0 * KL, N - n0, lb), lb,
-                       lb, wv, wm, wn, lane);
-    oscale = 1.0f;
-  }
-  store_tile(acc, wm, wn, lane, m0, n0, M, N, Y, [&](int) { return oscale; },
-             [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
+    GemmArgs p, float gscale, uint16_t* __restrict__ Y) {
+  gemm_persistent<Bf16Mma, false, LOWRANK>(p, nullptr, nullptr, gscale, Y);
 }
 
 // l1t[r][k] = L1[k][r] (zero for r >= R); l2t[n][c] = L2[c mod rpad][n] (zero past R).
@@ -326,24 +426,53 @@ __global__ __launch_bounds__(256) void k_lowrank_transpose(const uint16_t* __res
 
 }  // namespace
 
+// Persistent workgroups: one per CU while every slab stream is at least NST
+// slabs per tile (the ring and the scale buffers assume it); one per tile otherwise.
+static int gemm_workgroups(int ntiles, int nk) { return nk >= NST ? (ntiles < 256 ? ntiles : 256) : ntiles; }
+
 hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws, int64_t M,
                             int64_t K, int64_t N, uint16_t* y, hipStream_t stream) {
-  const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
-  hipLaunchKernelGGL(k_gemm_fp8r, dim3((unsigned)(tm * tn)), dim3(256), 0, stream, xq, xs, w, ws, M, K, N, y, tm,
-                     tn);
+  GemmArgs p{};
+  p.a = xq;
+  p.w = w;
+  p.M = M;
+  p.N = N;
+  p.pitch1 = (int)K;
+  p.kbytes1 = (int)K;
+  p.tiles_m = (int)((M + 255) / 256);
+  p.tiles_n = (int)((N + 255) / 256);
+  p.ntiles = p.tiles_m * p.tiles_n;
+  p.nwg = gemm_workgroups(p.ntiles, (p.kbytes1 + SROW - 1) / SROW);
+  hipLaunchKernelGGL(k_gemm_fp8r, dim3((unsigned)p.nwg), dim3(256), 0, stream, p, xs, ws, y);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
                              LowRank lr, uint16_t* y, hipStream_t stream) {
-  const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
-  const dim3 grid((unsigned)(tm * tn)), block(256);
+  GemmArgs p{};
+  p.a = reinterpret_cast<const uint8_t*>(xe);
+  p.w = reinterpret_cast<const uint8_t*>(we);
+  p.M = M;
+  p.N = N;
+  p.pitch1 = (int)(2 * K);
+  p.kbytes1 = (int)(2 * K);
+  int nk = (p.kbytes1 + SROW - 1) / SROW;
+  if (lr.kl > 0) {
+    p.a2 = reinterpret_cast<const uint8_t*>(lr.t);
+    p.w2 = reinterpret_cast<const uint8_t*>(lr.l2t);
+    p.pitch2 = (int)(2 * lr.kl);
+    p.kbytes2 = (int)(2 * lr.kl);
+    nk += (p.kbytes2 + SROW - 1) / SROW;
+  }
+  p.tiles_m = (int)((M + 255) / 256);
+  p.tiles_n = (int)((N + 255) / 256);
+  p.ntiles = p.tiles_m * p.tiles_n;
+  p.nwg = gemm_workgroups(p.ntiles, nk);
+  const dim3 grid((unsigned)p.nwg), block(256);
   if (lr.kl > 0)
-    hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, block, 0, stream, xe, we, gscale, M, K, N, lr.t, lr.l2t, lr.kl, y,
-                       tm, tn);
+    hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, block, 0, stream, p, gscale, y);
   else
-    hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, block, 0, stream, xe, we, gscale, M, K, N, lr.t, lr.l2t, lr.kl, y,
-                       tm, tn);
+    hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, block, 0, stream, p, gscale, y);
   return hipGetLastError();
 }
 

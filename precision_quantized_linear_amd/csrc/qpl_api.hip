@@ -282,7 +282,7 @@ QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int
              qpl::launch_lowrank_prep(lora_down, lora_up, K, N, R, kl, l1t, l2t, st)))) != QPL_OK)
       return s;
     if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
-             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, l1t, kl, xe, t, st)))) != QPL_OK)
+             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, l1t, kl, gscale, xe, t, st)))) != QPL_OK)
       return s;
     lr.t = t;
     lr.l2t = l2t;

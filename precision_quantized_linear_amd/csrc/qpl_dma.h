@@ -40,6 +40,16 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, u32x4 de
                : "memory");
 }
 
+// 4 bytes per lane from global memory into LDS: lane l writes LDS bytes
+// [lds_addr + 4 l, + 4); each dword is checked against the descriptor's size on
+// its own (zero past it).
+__device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, u32x4 desc, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soffset)
+               : "memory");
+}
+
 // LDS byte address of a __shared__ array, as a wave-uniform value.
 template <class T>
 __device__ __forceinline__ uint32_t lds_address(T* p) {

@@ -26,10 +26,11 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, 
 hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, uint16_t* xe,
                                      hipStream_t stream);
 // The same, fused with the low-rank down-projection: t [M, kl] bf16 receives
-// T = x L1 as [hi | lo] halves of kl / 2 columns each; l1t [kl / 2, K] is L1
-// transposed (zero past R); kl / 2 is a multiple of 32, at most 128.
+// T / tdiv (T = x L1, fp32, one correctly rounded division) as [hi | lo] halves of
+// kl / 2 columns each; l1t [kl / 2, K] is L1 transposed (zero past R); kl / 2 is
+// a multiple of 32, at most 128.
 hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const uint16_t* l1t,
-                                             int64_t kl, uint16_t* xe, uint16_t* t, hipStream_t stream);
+                                             int64_t kl, float tdiv, uint16_t* xe, uint16_t* t, hipStream_t stream);
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
                                hipStream_t stream);

@@ -264,8 +264,9 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __re
 //   2. run the bf16 MFMA 32x32x16 over their eighth of the tile's k range,
 //      reading both operands from LDS, into per-wave partial sums of T.
 // Two wavefronts per SIMD keep the quantizer's arithmetic busy.  The eight partial
-// sums meet in LDS at the end, in a fixed order; T is stored as [hi | lo] bf16
-// halves (row stride kl = 2 rpad) for the GEMM epilogue.
+// sums meet in LDS at the end, in a fixed order; T / tdiv is stored as [hi | lo]
+// bf16 halves (row stride kl = 2 rpad) for the GEMM's low-rank pass (tdiv is the
+// GEMM's output scale, which the pass's result is multiplied by again).
 //
 // LDS layout: 16-byte chunk c of tile row r sits at chunk slot c ^ (r & 15) of
 // the row, so the MFMA operand reads (16 rows, one chunk) hit 16 different bank
@@ -289,7 +290,7 @@ template <int NCT>
 __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                                float c6g, float rc6g, Nvfp4ScaleTable tab,
                                                                const uint16_t* __restrict__ l1t, int64_t kl,
-                                                               int rpw, uint16_t* __restrict__ xe,
+                                                               int rpw, float tdiv, uint16_t* __restrict__ xe,
                                                                uint16_t* __restrict__ t_out) {
   using C = LrTile<NCT>;
   constexpr int TK = C::TK, CPR = C::CPR, S = C::S, XI = C::XI, LI = C::LI, NW = C::NW;
@@ -428,8 +429,9 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
       const int mr = q * 8 + (l >> 5) * 4 + i;
       if (mr >= rows) continue;
       const int64_t m = m0 + mr;
-      const uint32_t hi = f32_to_bf16(v[i]);
-      const uint32_t lo = f32_to_bf16(v[i] - __uint_as_float(hi << 16));
+      const float tv = v[i] / tdiv;
+      const uint32_t hi = f32_to_bf16(tv);
+      const uint32_t lo = f32_to_bf16(tv - __uint_as_float(hi << 16));
       t_out[m * kl + 32 * c + (l & 31)] = (uint16_t)hi;
       t_out[m * kl + rpad + 32 * c + (l & 31)] = (uint16_t)lo;
     }
@@ -473,7 +475,7 @@ hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, fl
 }
 
 hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const uint16_t* l1t,
-                                             int64_t kl, uint16_t* xe, uint16_t* t, hipStream_t stream) {
+                                             int64_t kl, float tdiv, uint16_t* xe, uint16_t* t, hipStream_t stream) {
   // buffer offsets are 32-bit: the L1^T tile rows (at most 128) times the pitch
   if (K > (int64_t{1} << 21)) return hipErrorInvalidValue;
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
@@ -484,16 +486,16 @@ hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64
   const dim3 grid((unsigned)((M + rpw - 1) / rpw)), block(512);
   switch (kl / 64) {  // rpad / 32
     case 1:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<1>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<1>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
       break;
     case 2:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<2>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<2>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
       break;
     case 3:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<3>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<3>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
       break;
     case 4:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<4>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, xe, t);
+      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<4>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
       break;
     default:
       return hipErrorInvalidValue;
