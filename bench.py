@@ -34,7 +34,11 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 HBM_GBS = 8000.0
 METRIC = "qlinear TFLOP/s (act-quant+GEMM) and % of FP8/FP4 MFMA peak, M=4608"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_4608x3072x12288.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_4608x3072x12288.md")
+# sources of the kernel the traffic counters were taken on; a changed source voids them
+TRAFFIC_SOURCES = ("precision_quantized_linear_amd/csrc/gemm_kernels.hip", "precision_quantized_linear_amd/csrc/qpl_dma.h",
+                   "precision_quantized_linear_amd/csrc/qpl_device.h")
+COPY_PROBE_BYTES = 256 << 20
 
 
 def parse():
@@ -43,7 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="activation rows per linear in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="activation rows per linear in the CPU sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 256 MiB device copy (the reference kernel for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -105,6 +111,14 @@ def main():
         e["flops"] = 2.0 * e["M"] * e["N"] * e["K"]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
+    if args.copy_probe:
+        src = torch.empty((COPY_PROBE_BYTES,), dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: {COPY_PROBE_BYTES} bytes read and written")
 
     def run(key):
         e = lin[key]
@@ -163,11 +177,7 @@ def main():
     avg_s = t_g / n_g * 1e-3
     e = lin["nvfp4"]
     achieved = e["flops"] / avg_s / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        traffic = tr.get("hbm_bytes_per_launch")
+    traffic = measured_traffic()
     roofline = {"kernel": "gemm_nvfp4 (bf16 MFMA, 4608x3072x12288)", "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                 "traffic": traffic, "avg_us": round(avg_s * 1e6, 2),
@@ -195,6 +205,35 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the nvfp4 GEMM from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factors), or None when the
+    summary is missing or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                fields[k.strip("`")] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(lin, rows):
