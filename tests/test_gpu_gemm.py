@@ -140,6 +140,26 @@ def test_qlinear_nvfp4_full(name):
     assert r["ok"], r
 
 
+@pytest.mark.parametrize("scheme", ["fp8r", "nvfp4"])
+def test_last_round_tiles(scheme):
+    # 4608 x 12288 outputs = 864 tiles of 256 x 256 over 256 persistent workgroups:
+    # the 96 tiles of the fourth round (rows 4096..4607) and the band above them,
+    # every column, at a short K
+    M, K, N = 4608, 256, 12288
+    rows = np.arange(3840, M)
+    if scheme == "fp8r":
+        d = make("fp8r_dit_n12288", M=M, K=K, N=N)
+        say("last round fp8r", M, K, N)
+        r = fp8r_case(d, rows)
+    else:
+        d = make("nvfp4_dit", M=M, K=K, N=N)
+        g_in = calibrate_input_scale(calibration_batches("nvfp4_dit", M=64, K=K))
+        say("last round nvfp4", M, K, N)
+        r = nvfp4_case(d, rows, g_in)
+    say(r)
+    assert r["ok"], r
+
+
 @pytest.mark.parametrize("R,M,K", [(1, 130, 256), (20, 130, 256), (64, 130, 256), (100, 130, 256), (128, 45, 208),
                                    (33, 17, 48)])
 def test_qlinear_nvfp4_lowrank_ranks(R, M, K):
