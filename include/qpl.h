@@ -169,6 +169,9 @@ typedef enum {
 } qpl_kernel;
 
 void qpl_timing_enable(int on);
+/* Time only the kernel kinds whose bit (1 << kind) is set in `kinds` (0 = off);
+ * an event pair costs a few microseconds of stream time per timed launch. */
+void qpl_timing_select(uint32_t kinds);
 qpl_status qpl_timing_collect(int64_t* launches, double* total_ms);
 
 /* Static description of a status code. */

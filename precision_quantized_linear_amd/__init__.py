@@ -4,4 +4,4 @@ is its thin Python binding."""
 from ._binding import (EXPORTS, KERNELS, LIB_PATH, QPL_FP8R, QPL_NVFP4, QPLError, amax_bf16,  # noqa: F401
                        dequant_weight, load, nvfp4_global_scale, qlinear_fp8r, qlinear_nvfp4,
                        qlinear_workspace_bytes, quant_act_fp8_row, quant_act_nvfp4, timing_collect,
-                       timing_enable)
+                       timing_enable, timing_select)

@@ -17,7 +17,7 @@ QPL_NVFP4 = 1
 
 EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp4", "dequant_weight",
            "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
-           "qpl_timing_enable", "qpl_timing_collect")
+           "qpl_timing_enable", "qpl_timing_select", "qpl_timing_collect")
 
 # qpl_kernel order of include/qpl.h
 KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_bf16", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
@@ -61,6 +61,8 @@ def load():
     lib.qpl_status_str.restype = ctypes.c_char_p
     lib.qpl_timing_enable.argtypes = [ctypes.c_int]
     lib.qpl_timing_enable.restype = None
+    lib.qpl_timing_select.argtypes = [ctypes.c_uint32]
+    lib.qpl_timing_select.restype = None
     lib.qpl_timing_collect.argtypes = [P, P]
     lib.qpl_timing_collect.restype = ctypes.c_int
     _lib = lib
@@ -186,6 +188,14 @@ def nvfp4_global_scale(amax):
 def timing_enable(on=True):
     """Bracket every library kernel launch with HIP events (profiling aid)."""
     load().qpl_timing_enable(1 if on else 0)
+
+
+def timing_select(kinds):
+    """Time only the named kernel kinds (names from KERNELS); an empty list turns timing off."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNELS.index(k)
+    load().qpl_timing_select(mask)
 
 
 def timing_collect():

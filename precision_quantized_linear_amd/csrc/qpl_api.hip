@@ -95,7 +95,7 @@ Layout layout(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R) {
 }
 
 // ---- per-kernel timing -------------------------------------------------------
-std::atomic<bool> g_timing{false};
+std::atomic<uint32_t> g_timing{0u};  // bit k: time launches of kernel kind k
 std::mutex g_tmu;
 struct TimingRec {
   int kind;
@@ -122,7 +122,7 @@ hipEvent_t take_event() {
 class Timed {
  public:
   Timed(qpl_kernel kind, hipStream_t s) : kind_(kind), s_(s) {
-    if (!g_timing.load(std::memory_order_relaxed)) return;
+    if (!((g_timing.load(std::memory_order_relaxed) >> int(kind)) & 1u)) return;
     std::lock_guard<std::mutex> lk(g_tmu);
     start_ = take_event();
     if (start_ && hipEventRecord(start_, s_) != hipSuccess) {
@@ -154,7 +154,9 @@ class Timed {
 
 }  // namespace
 
-QPL_EXPORT void qpl_timing_enable(int on) { g_timing.store(on != 0); }
+QPL_EXPORT void qpl_timing_enable(int on) { g_timing.store(on ? (1u << QPL_KERNEL_COUNT) - 1u : 0u); }
+
+QPL_EXPORT void qpl_timing_select(uint32_t kinds) { g_timing.store(kinds & ((1u << QPL_KERNEL_COUNT) - 1u)); }
 
 QPL_EXPORT qpl_status qpl_timing_collect(int64_t* launches, double* total_ms) {
   if (!launches || !total_ms) return QPL_ERR_NULL;
