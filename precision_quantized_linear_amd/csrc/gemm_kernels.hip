@@ -137,6 +137,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // What the GEMM kernels multiply.  Pass 1: rows of x (a) and of W (w), pitch1
 // bytes apart, kbytes1 valid bytes each.  Pass 2 (the low-rank up-projection):
 // rows of [T_hi | T_lo] and [L2^T | L2^T].
+// Tile sequence positions [0, nfull) are computed whole; each of the ntail tiles
+// after them is computed as two 128-row halves by workgroups 2j and 2j + 1.
 struct GemmArgs {
   const uint8_t* a;
   const uint8_t* w;
@@ -144,7 +146,7 @@ struct GemmArgs {
   const uint8_t* w2;
   int64_t M, N;
   int pitch1, kbytes1, pitch2, kbytes2;
-  int tiles_m, tiles_n, ntiles, nwg;
+  int tiles_m, tiles_n, ntiles, nwg, nfull, ntail;
 };
 
 constexpr int NSTORE = 32;           // 16-byte output stores per wave per tile (fast path)
@@ -154,17 +156,19 @@ constexpr int SCALE_BUF = 2048;      // per tile parity: s_x of the tile's 256 r
 // element r at lane l is row m = m0 + 128 wm + 32 j + l % 32, column
 // n = n0 + 128 wn + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4.  Lanes l and l + 32
 // exchange halves (V_PERMLANE32_SWAP) so that each lane holds eight consecutive
-// columns of one row and stores them as one 16-byte segment.  Returns the number
-// of store instructions left in flight: NSTORE on the interior path, 0 on the
-// edge path (which checks every element and drains its stores).
-template <class RowScale, class ColScale>
+// columns of one row and stores them as one 16-byte segment.  NJ: 32-row blocks
+// per wavefront (4 for a 256-row tile, 2 for a 128-row half tile, whose rows are
+// m0 + 64 wm + 32 j + l % 32).  Returns the number of store instructions left in
+// flight: 8 NJ on the interior path, 0 on the edge path (which checks every
+// element and drains its stores).
+template <int NJ, class RowScale, class ColScale>
 __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
                                           int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
                                           const ColScale& cs) {
-  const bool fast = m0 + 256 <= M && n0 + 256 <= N && (N & 7) == 0;
+  const bool fast = m0 + 64 * NJ <= M && n0 + 256 <= N && (N & 7) == 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int mr = wm * 128 + j * 32 + (lane & 31);
+  for (int j = 0; j < NJ; ++j) {
+    const int mr = wm * 32 * NJ + j * 32 + (lane & 31);
     const float fr = rs(mr);
     const int64_t m = m0 + mr;
 #pragma unroll
@@ -198,7 +202,7 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
         }
       }
   }
-  if (fast) return NSTORE;
+  if (fast) return 8 * NJ;
   QPL_WAIT_VMCNT(0);
   return 0;
 }
@@ -233,11 +237,32 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
   const uint32_t lbase = lds_address(lds);
   const uint32_t sbase = lds_address(lsc);
 
+  // Units of work: whole tiles at tile sequence positions tile_seq(0..nt - 1), then
+  // (has_half) half u of the tail: rows 128 (u % 2) .. + 127 of tile nfull + u / 2.
   int nt = 0;
-  while (tile_seq(nt, b, p.nwg) < p.ntiles) ++nt;
+  while (tile_seq(nt, b, p.nwg) < p.nfull) ++nt;
+  const int hu = tile_seq(nt, b, p.nwg) - p.nfull;
+  const bool has_half = hu < 2 * p.ntail;
+  const int nu = nt + (has_half ? 1 : 0);
   const int nk1 = (p.kbytes1 + SROW - 1) / SROW;
   const int nk2 = LOWRANK ? (p.kbytes2 + SROW - 1) / SROW : 0;
   const int nk = nk1 + nk2;
+  struct Unit {
+    int64_t m0, n0;
+    int rows;
+  };
+  auto unit = [&](int ti) {
+    Unit r;
+    if (ti < nt) {
+      tile_coords(tile_seq(ti, b, p.nwg), p.tiles_m, p.tiles_n, r.m0, r.n0);
+      r.rows = 256;
+    } else {
+      tile_coords(p.nfull + (hu >> 1), p.tiles_m, p.tiles_n, r.m0, r.n0);
+      r.m0 += 128 * (hu & 1);
+      r.rows = 128;
+    }
+    return r;
+  };
 
   // lane geometry of the slab loads: instruction q of this wave fills slab rows
   // 16 (4 wv + q) .. + 15; lane l writes physical chunk l % 4 of row + l / 4,
@@ -249,19 +274,20 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
     cb[q] = ((lane & 3) ^ swz(lrow[q])) * 16;
   }
 
-  // The load stream: slab ks of the workgroup's tile ti, advanced one slab per
-  // call of next_src (tile coordinates recomputed at tile boundaries only).
+  // The load stream: slab ks of the workgroup's unit ti, advanced one slab per
+  // call of next_src (unit coordinates recomputed at unit boundaries only).  A half
+  // unit's x slab rows 128 .. 255 lie outside its descriptor and load zeros.
   struct SlabSrc {
     u32x4 dx, dw, ds;
     int pitch, kb, koff, stage, tpar;
     bool first, valid;
   };
   int s_ti = 0, s_ks = 0, s_stage = 0;
-  int64_t s_m0 = 0, s_n0 = 0;
-  if (nt > 0) tile_coords(tile_seq(0, b, p.nwg), p.tiles_m, p.tiles_n, s_m0, s_n0);
+  Unit s_u{0, 0, 256};
+  if (nu > 0) s_u = unit(0);
   auto next_src = [&]() {
     SlabSrc r;
-    r.valid = s_ti < nt;
+    r.valid = s_ti < nu;
     r.stage = s_stage;
     r.first = s_ks == 0;
     r.tpar = s_ti & 1;
@@ -269,18 +295,20 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
     r.pitch = pass2 ? p.pitch2 : p.pitch1;
     r.kb = r.valid ? (pass2 ? p.kbytes2 : p.kbytes1) : 0;
     r.koff = (pass2 ? s_ks - nk1 : s_ks) * SROW;
-    const int64_t rm = M_rows(p.M - s_m0), rn = M_rows(p.N - s_n0);
-    r.dx = make_desc((pass2 ? p.a2 : p.a) + s_m0 * r.pitch, rm * r.pitch);
-    r.dw = make_desc((pass2 ? p.w2 : p.w) + s_n0 * r.pitch, rn * r.pitch);
+    const int64_t left = p.M - s_u.m0;
+    const int64_t rm = left < 0 ? 0 : (left < s_u.rows ? left : s_u.rows);
+    const int64_t rn = M_rows(p.N - s_u.n0);
+    r.dx = make_desc((pass2 ? p.a2 : p.a) + s_u.m0 * r.pitch, rm * r.pitch);
+    r.dw = make_desc((pass2 ? p.w2 : p.w) + s_u.n0 * r.pitch, rn * r.pitch);
     if constexpr (ROWCOL) {
       const bool row = wv < 2;
-      r.ds = make_desc(row ? sa + s_m0 : sb + s_n0, (row ? rm : rn) * 4);
+      r.ds = make_desc(row ? sa + s_u.m0 : sb + s_u.n0, (row ? rm : rn) * 4);
     }
     s_stage = s_stage == NST - 1 ? 0 : s_stage + 1;
     if (++s_ks == nk) {
       s_ks = 0;
       ++s_ti;
-      if (s_ti < nt) tile_coords(tile_seq(s_ti, b, p.nwg), p.tiles_m, p.tiles_n, s_m0, s_n0);
+      if (s_ti < nu) s_u = unit(s_ti);
     }
     return r;
   };
@@ -292,7 +320,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
       const uint32_t vo = s.koff + cb[q] < s.kb ? (uint32_t)(lrow[q] * s.pitch + cb[q]) : kOutOfRange;
       dma16(dst, vo, wslab ? s.dw : s.dx, s.koff);
     } else {
-      // scale vectors of a tile: wave w moves 128 floats of s_x (w = 0, 1) or s_w
+      // scale vectors of a unit: wave w moves 128 floats of s_x (w = 0, 1) or s_w
       // (w = 2, 3), 64 per instruction; other slabs load nothing into a spare area
       const int h = d - 8;
       const bool real = s.valid && s.first;
@@ -312,33 +340,29 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
   QPL_WAIT_VMCNT((NST - 1) * D);
   __builtin_amdgcn_s_barrier();
   typename T::Frag fw[T::SUB][4], fx[T::SUB][4];
-#pragma unroll
-  for (int u = 0; u < T::SUB; ++u)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fw[u][i] = T::read(lds + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
-      fx[u][i] = T::read(lds, wm * 128 + i * 32 + (lane & 31), u, lane);
-    }
 
   int st1 = 0, st2 = 0, st3 = 0;  // stores left in flight after iterations g - 1, g - 2, g - 3
   int cur = 0;                     // stage of the slab being multiplied
-  constexpr int NMMA = 16 * T::SUB;
+  // NJ: 32-row blocks of x per wavefront in the current unit (4 whole, 2 half).
   // One slab: wait for the next slab, multiply this one while reading the next
   // one's fragments (FRAGS) and issuing the loads of slab + NST.  Before the
   // epilogue (and the low-rank rescale) the next fragments are read afterwards
   // instead (read_frags), so that they do not occupy registers meanwhile.
-  auto read_frags = [&]() {
+  auto read_frags = [&](auto nj) {
+    constexpr int NJ = decltype(nj)::value;
     const uint8_t* nx = lds + cur * STAGE;
 #pragma unroll
     for (int u = 0; u < T::SUB; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
-        fx[u][i] = T::read(nx, wm * 128 + i * 32 + (lane & 31), u, lane);
+        if (i < NJ) fx[u][i] = T::read(nx, wm * 32 * NJ + i * 32 + (lane & 31), u, lane);
       }
   };
-  auto step = [&](Acc& acc, auto frags) {
+  auto step = [&](Acc& acc, auto frags, auto nj) {
     constexpr bool FRAGS = decltype(frags)::value;
+    constexpr int NJ = decltype(nj)::value;
+    constexpr int NMMA = 4 * NJ * T::SUB;
     QPL_WAIT_LGKM0();
     const int extra = st1 + st2 + st3;
     if (extra == 0) {
@@ -357,11 +381,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           acc[i][j] = T::mma(fw[u][i], fx[u][j], acc[i][j]);
-          const int k = 16 * u + 4 * i + j;
-          if (FRAGS && i == 3) fx[u][j] = T::read(nx, wm * 128 + j * 32 + (lane & 31), u, lane);
-          if (FRAGS && j == 3) fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
+          const int k = 4 * NJ * u + NJ * i + j;
+          if (FRAGS && i == 3) fx[u][j] = T::read(nx, wm * 32 * NJ + j * 32 + (lane & 31), u, lane);
+          if (FRAGS && j == NJ - 1) fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
           // spread the D loads of slab + NST over this slab's MFMAs
 #pragma unroll
           for (int d = 0; d < D; ++d)
@@ -374,24 +398,45 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
 
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
+  using Whole = std::integral_constant<int, 4>;
+  using Half = std::integral_constant<int, 2>;
+  auto epilogue = [&](const Acc& acc, int ti, auto nj) {
+    constexpr int NJ = decltype(nj)::value;
+    const Unit un = unit(ti);
+    if constexpr (ROWCOL) {
+      const float* ls = reinterpret_cast<const float*>(lsc + (ti & 1) * SCALE_BUF);
+      st1 = store_tile<NJ>(
+          acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int r) { return ls[r]; },
+          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); });
+    } else {
+      st1 = store_tile<NJ>(
+          acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return gscale; },
+          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
+    }
+    if (st1 == 0) st2 = st3 = 0;
+  };
+
+  if (nt > 0)
+    read_frags(Whole{});
+  else
+    read_frags(Half{});
   for (int ti = 0; ti < nt; ++ti) {
     Acc acc;
     zero_acc(acc);
-    for (int kt = 0; kt < nk - 1; ++kt) step(acc, Yes{});
-    step(acc, No{});
-    int64_t m0, n0;
-    tile_coords(tile_seq(ti, b, p.nwg), p.tiles_m, p.tiles_n, m0, n0);
-    if constexpr (ROWCOL) {
-      const float* ls = reinterpret_cast<const float*>(lsc + (ti & 1) * SCALE_BUF);
-      st1 = store_tile(
-          acc, wm, wn, lane, m0, n0, p.M, p.N, Y, [&](int r) { return ls[r]; },
-          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); });
-    } else {
-      st1 = store_tile(acc, wm, wn, lane, m0, n0, p.M, p.N, Y, [&](int) { return gscale; },
-                       [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
-    }
-    if (st1 == 0) st2 = st3 = 0;
-    read_frags();
+    for (int kt = 0; kt < nk - 1; ++kt) step(acc, Yes{}, Whole{});
+    step(acc, No{}, Whole{});
+    epilogue(acc, ti, Whole{});
+    if (ti + 1 < nt)
+      read_frags(Whole{});
+    else
+      read_frags(Half{});
+  }
+  if (has_half) {
+    Acc acc;
+    zero_acc(acc);
+    for (int kt = 0; kt < nk - 1; ++kt) step(acc, Yes{}, Half{});
+    step(acc, No{}, Half{});
+    epilogue(acc, nt, Half{});
   }
   QPL_WAIT_VMCNT(0);
   QPL_WAIT_LGKM0();
@@ -430,6 +475,18 @@ __global__ __launch_bounds__(256) void k_lowrank_transpose(const uint16_t* __res
 // slabs per tile (the ring and the scale buffers assume it); one per tile otherwise.
 static int gemm_workgroups(int ntiles, int nk) { return nk >= NST ? (ntiles < 256 ? ntiles : 256) : ntiles; }
 
+// Workgroup count and the split of the last round.  With 256 persistent
+// workgroups and ntiles % 256 <= 128 leftover tiles, the leftover tiles are
+// computed as 2 (ntiles % 256) half tiles, one per workgroup, so the last round
+// takes half a tile's time instead of a whole one.
+static void gemm_plan(GemmArgs& p, int nk) {
+  p.nwg = gemm_workgroups(p.ntiles, nk);
+  const int tail = p.ntiles % 256;
+  const bool split = p.nwg == 256 && p.ntiles > 256 && tail > 0 && tail <= 128;
+  p.nfull = split ? p.ntiles - tail : p.ntiles;
+  p.ntail = split ? tail : 0;
+}
+
 hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws, int64_t M,
                             int64_t K, int64_t N, uint16_t* y, hipStream_t stream) {
   GemmArgs p{};
@@ -442,7 +499,7 @@ hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w
   p.tiles_m = (int)((M + 255) / 256);
   p.tiles_n = (int)((N + 255) / 256);
   p.ntiles = p.tiles_m * p.tiles_n;
-  p.nwg = gemm_workgroups(p.ntiles, (p.kbytes1 + SROW - 1) / SROW);
+  gemm_plan(p, (p.kbytes1 + SROW - 1) / SROW);
   hipLaunchKernelGGL(k_gemm_fp8r, dim3((unsigned)p.nwg), dim3(256), 0, stream, p, xs, ws, y);
   return hipGetLastError();
 }
@@ -467,7 +524,7 @@ hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscal
   p.tiles_m = (int)((M + 255) / 256);
   p.tiles_n = (int)((N + 255) / 256);
   p.ntiles = p.tiles_m * p.tiles_n;
-  p.nwg = gemm_workgroups(p.ntiles, nk);
+  gemm_plan(p, nk);
   const dim3 grid((unsigned)p.nwg), block(256);
   if (lr.kl > 0)
     hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, block, 0, stream, p, gscale, y);

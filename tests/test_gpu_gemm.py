@@ -140,21 +140,28 @@ def test_qlinear_nvfp4_full(name):
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("scheme", ["fp8r", "nvfp4"])
-def test_last_round_tiles(scheme):
-    # 4608 x 12288 outputs = 864 tiles of 256 x 256 over 256 persistent workgroups:
-    # the 96 tiles of the fourth round (rows 4096..4607) and the band above them,
-    # every column, at a short K
-    M, K, N = 4608, 256, 12288
+@pytest.mark.parametrize("scheme,M,N", [("fp8r", 4608, 12288), ("nvfp4", 4608, 12288), ("fp8r", 4500, 12200),
+                                         ("nvfp4", 4400, 12288), ("svdq", 4500, 12288), ("fp8r", 4608, 16384),
+                                         ("nvfp4", 4500, 16384), ("fp8r", 4608, 16640)])
+def test_last_round_tiles(scheme, M, N):
+    # 18 x 48 = 864 tiles of 256 x 256 over 256 persistent workgroups: the 96
+    # tiles left for a fourth round (tile rows 16 and 17) are computed as 192 half
+    # tiles of 128 x 256.  Checked: those rows and the band above them, every
+    # column, at a short K.  M = 4500 leaves 20 rows in the second half of the
+    # last tile row, M = 4400 none; N = 12200 is ragged.  18 x 64 = 1152 tiles
+    # leave 128 (every workgroup takes a half tile); 18 x 65 = 1170 leave 146,
+    # which are computed whole.
+    K = 256
     rows = np.arange(3840, M)
     if scheme == "fp8r":
         d = make("fp8r_dit_n12288", M=M, K=K, N=N)
         say("last round fp8r", M, K, N)
         r = fp8r_case(d, rows)
     else:
-        d = make("nvfp4_dit", M=M, K=K, N=N)
-        g_in = calibrate_input_scale(calibration_batches("nvfp4_dit", M=64, K=K))
-        say("last round nvfp4", M, K, N)
+        name = "nvfp4_dit" if scheme == "nvfp4" else "svdq_w4a4"
+        d = make(name, M=M, K=K, N=N)
+        g_in = calibrate_input_scale(calibration_batches(name, M=64, K=K))
+        say("last round", name, M, K, N, "R", d.get("R", 0))
         r = nvfp4_case(d, rows, g_in)
     say(r)
     assert r["ok"], r
