@@ -21,10 +21,15 @@ design notes):
   ``input_scale`` uses the largest amax over the calibration batches.
 * Packing: byte j of a row holds element 2j in its low nibble and 2j+1 in its
   high nibble; block scales are row-major ``[rows, K/16]``.
+* SVDQuant smoothing (Nunchaku post, "Background: SVDQuant and Nunchaku": the
+  activation outliers are moved into the weights): the layer divides input
+  channel k by a positive factor ``smooth[k]`` (the weight's column k carries the
+  factor instead), ``x_hat = bf16(x / smooth[k])`` with a correctly rounded fp32
+  division, and both the 4-bit path and the low-rank branch take ``x_hat``.
 """
 import numpy as np
 
-from .formats import (bf16_bits_to_f32, e2m1_encode, e4m3_decode, e4m3_encode)
+from .formats import (bf16_bits_to_f32, e2m1_encode, e4m3_decode, e4m3_encode, f32_to_bf16_bits)
 
 F32 = np.float32
 
@@ -101,3 +106,17 @@ def quant_nvfp4(x_bits, g):
     codes[nz] = e2m1_encode(q)
     codes[~nz] = np.where(np.signbit(xb[~nz]), 0x8, 0x0).astype(np.uint8)
     return pack_e2m1(codes.reshape(R, K)), sf
+
+
+def smooth_bf16(x_bits, smooth):
+    """SVDQuant smoothing of a bf16 [R, K] activation by per-channel factors.
+
+    x_hat[r, k] = bf16_RNE(fp32(x[r, k]) / smooth[k]): one correctly rounded fp32
+    division, then the round to bf16 that makes x_hat the 16-bit activation both
+    branches of the layer read.  ``smooth`` is float32 [K], positive and finite.
+    Returns bf16 bit patterns [R, K].
+    """
+    x = bf16_bits_to_f32(x_bits)
+    lam = np.asarray(smooth, dtype=F32)
+    assert lam.shape == (x.shape[1],)
+    return f32_to_bf16_bits((x / lam[None, :]).astype(F32))

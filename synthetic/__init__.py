@@ -3,4 +3,4 @@
 Holds random draws and input shaping only: no quantization, scale or GEMM
 arithmetic of the method lives here.
 """
-from .workloads import WORKLOADS, make, calibration_batches, bf16_round  # noqa: F401
+from .workloads import WORKLOADS, make, calibration_batches, bf16_round, smooth_factors  # noqa: F401

@@ -12,10 +12,12 @@ checkpoint or dataset is used.  Recipe (all draws float32 from
 * the SVDQuant workload stores the residual weight W - (L1 L2)^T (rounded to bf16),
   as an SVDQuant checkpoint stores the residual beside its low-rank factors;
 * calibration batches: further draws with the activation recipe and the same
-  outlier channels.
+  outlier channels;
+* smoothing factors [K] (float32, for the SVDQuant smoothing step):
+  exp(N(0, 0.25^2)), times sqrt(mult) on the outlier channels.
 
 Seeds for workload number c: X 100c, W 100c+1, outlier channels 100c+2,
-L1 100c+3, L2 100c+4, calibration batch i 100c+10+i.
+L1 100c+3, L2 100c+4, smoothing factors 100c+5, calibration batch i 100c+10+i.
 """
 import numpy as np
 
@@ -112,3 +114,15 @@ def calibration_batches(name, M=None, K=None):
     ch = _outlier_channels(spec, K)
     for i in range(spec.get("n_cal", 0)):
         yield _activation(spec, 100 * spec["c"] + 10 + i, M, K, ch)
+
+
+def smooth_factors(name, K=None):
+    """Positive per-channel smoothing factors float32 [K] for workload ``name``."""
+    spec = WORKLOADS[name]
+    K = spec["K"] if K is None else K
+    lam = np.exp(_rng(100 * spec["c"] + 5).standard_normal(K, dtype=np.float32) * np.float32(0.25))
+    lam = lam.astype(np.float32)
+    ch = _outlier_channels(spec, K)
+    if len(ch):
+        lam[ch] *= np.float32(np.sqrt(spec["mult"]))
+    return lam

@@ -1,10 +1,13 @@
 """Pins for oracle.quant: scale invariants, error bounds, constructed exact ties,
-saturation, zero rows/blocks, nibble order and the global-scale rule."""
+saturation, zero rows/blocks, nibble order, the global-scale rule and the
+SVDQuant smoothing division."""
+from fractions import Fraction
+
 import numpy as np
 
 from oracle.formats import e2m1_decode, e4m3_decode, e4m3_encode, bf16_bits_to_f32
 from oracle.quant import (amax_bf16, calibrate_input_scale, global_scale, pack_e2m1,
-                          quant_fp8_row, quant_nvfp4, unpack_e2m1)
+                          quant_fp8_row, quant_nvfp4, smooth_bf16, unpack_e2m1)
 from synthetic import bf16_round, make, calibration_batches
 
 F32 = np.float32
@@ -164,3 +167,91 @@ def test_nvfp4_weight_global_scale_saturates_nothing():
     assert int(sf.max()) <= 0x7E
     # the tensor maximum sits in a block whose scale is 448 (code 0x7E) or just below
     assert e4m3_decode(sf).max() >= 416.0
+
+
+# ---------------------------------------------------------------- smoothing
+
+def test_smooth_unit_factor_is_identity():
+    x = rand_bf16((8, 64), 11, 3.0)
+    x[0, :4] = [0x0000, 0x8000, 0x0001, 0x8001]  # signed zeros and bf16 subnormals
+    assert np.array_equal(smooth_bf16(x, np.ones(64, F32)), x)
+
+
+def test_smooth_power_of_two_shifts_the_exponent():
+    # x / 2^j is exact; on bf16 bit patterns it subtracts j from the exponent field
+    rng = np.random.default_rng(12)
+    x = rand_bf16((16, 48), 12, 1.0)
+    x[x & 0x7F80 == 0] = 0x3F80  # keep every value normal and away from the edges
+    j = rng.integers(-8, 9, size=48)
+    lam = np.ldexp(np.ones(48), j).astype(F32)
+    expect = (x.astype(np.int64) - (j[None, :] << 7)).astype(np.uint16)
+    assert np.array_equal(smooth_bf16(x, lam), expect)
+
+
+def _round_rne(q, p):
+    """Nearest value with p significant bits to the nonzero rational q, ties to even
+    (normal range only)."""
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    unit = Fraction(2) ** (e - p + 1)
+    n = a // unit
+    rem = a - n * unit
+    if rem > unit / 2 or (rem == unit / 2 and n % 2 == 1):
+        n += 1
+    v = n * unit
+    return v if q > 0 else -v
+
+
+def test_smooth_is_fp32_division_then_bf16_rounding():
+    # brute force from exact rationals: round x / lam to 24 significant bits, then to 8
+    rng = np.random.default_rng(13)
+    x = rand_bf16((1, 400), 13, 4.0)[0]
+    x[x & 0x7F80 == 0] = 0xC0A0
+    lam = np.exp(rng.uniform(-6, 6, size=400)).astype(F32)
+    lam[:40] = np.nextafter(np.ldexp(F32(1), rng.integers(-5, 6, size=40)).astype(F32), F32(0))  # 1.11..1 x 2^e
+    lam[40:80] = (F32(1) + F32(2.0 ** -23) * rng.integers(1, 64, size=40)).astype(F32)
+    # factors whose quotient lies just off a bf16 midpoint: there the two roundings
+    # differ from one rounding of the exact quotient
+    xs, ls = [], []
+    for _ in range(64):
+        xb = int(rng.integers(0x3F80, 0x4000))
+        xf = float(np.array([xb << 16], np.uint32).view(F32)[0])
+        m = Fraction(1) + Fraction(2 * int(rng.integers(0, 128)) + 1, 256)
+        c = F32(float(Fraction(xf) / m))
+        xs += [xb] * 3
+        ls += [c, np.nextafter(c, F32(0)), np.nextafter(c, F32(10))]
+    x = np.concatenate([x, np.array(xs, np.uint16)])
+    lam = np.concatenate([lam, np.array(ls, F32)])
+    got = smooth_bf16(x[None, :], lam)[0]
+    xv = bf16_bits_to_f32(x)
+    double = 0
+    for i in range(x.size):
+        q = Fraction(float(xv[i])) / Fraction(float(lam[i]))
+        q8 = _round_rne(_round_rne(q, 24), 8)
+        double += q8 != _round_rne(q, 8)
+        assert Fraction(float(bf16_bits_to_f32(got[i:i + 1])[0])) == q8, (i, xv[i], lam[i])
+    assert double >= 4
+
+
+def test_smooth_divides_and_the_weight_multiplies():
+    # SVDQuant moves a channel's range from x into W: (x / lam) (W lam)^T = x W^T.
+    # With power-of-two factors every step is exact, so the identity holds exactly;
+    # a multiplication by lam in place of the division fails it.
+    rng = np.random.default_rng(14)
+    xi = rng.integers(-8, 9, size=(6, 32)).astype(F32)
+    wi = rng.integers(-8, 9, size=(5, 32)).astype(np.float64)
+    lam = np.ldexp(np.ones(32), rng.integers(-3, 4, size=32)).astype(F32)
+    x_bits = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    xh = bf16_bits_to_f32(smooth_bf16(x_bits, lam)).astype(np.float64)
+    assert np.array_equal(xh @ (wi * lam.astype(np.float64)[None, :]).T, xi.astype(np.float64) @ wi.T)
+    assert not np.array_equal(xh, xi.astype(np.float64))
+
+
+def test_smooth_keeps_signs():
+    x = np.array([[0x8000, 0x0000, 0xBF80, 0x3F80]], np.uint16)
+    got = smooth_bf16(x, np.array([3.0, 3.0, 7.0, 7.0], F32))
+    assert got[0, 0] == 0x8000 and got[0, 1] == 0x0000
+    assert got[0, 2] & 0x8000 and not got[0, 3] & 0x8000
+    assert got[0, 2] == got[0, 3] | 0x8000
