@@ -20,7 +20,8 @@ The roofline object covers the dominant kernel (the nvfp4 GEMM at 4608 x 3072 x
 timed region (the library's event timing, limited to that kernel).  `parts` and
 `kernels` come from a second pass of the same steps with every launch timed.  The
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
-(rank 0, one GPU only).
+(rank 0, one GPU only).  `extras` times what lies beyond the step: the svdq linear
+with SVDQuant smoothing factors.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -71,7 +72,7 @@ def main():
     import torch
 
     import precision_quantized_linear_amd as qpl
-    from synthetic import calibration_batches, make
+    from synthetic import calibration_batches, make, smooth_factors
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -200,6 +201,41 @@ def main():
     qbytes = 3.0 * lin["fp8r"]["M"] * lin["fp8r"]["K"] + 4.0 * lin["fp8r"]["M"]
     quant_gbs = qbytes / (tq / nq * 1e-3) / 1e9
 
+    # ---------------------------------------------------------------- beyond the step: SVDQuant smoothing
+    # The svdq linear again with per-channel smoothing factors (quantize fused with
+    # x L1 now divides x by them first); same shapes, timed on its own.
+    e = lin["svdq"]
+    lam = torch.from_numpy(smooth_factors("svdq_w4a4")).to(dev)
+
+    def run_smooth():
+        qpl.qlinear_nvfp4(e["x"], e["wq"], e["wbs"], e["g_w"], e["g_in"], y=e["y"], workspace=e["ws_buf"],
+                          lora_down=e["l1"], lora_up=e["l2"], smooth=lam)
+
+    for _ in range(args.warmup):
+        run_smooth()
+    torch.cuda.synchronize()
+    qpl.timing_collect()
+    qpl.timing_select(["quant_nvfp4_lowrank"])
+    evs = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run_smooth()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    qpl.timing_select([])
+    ns, ts = qpl.timing_collect()["quant_nvfp4_lowrank"]
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    kl = 2 * 32 * ((e["R"] + 31) // 32)
+    qlr_bytes = 4.0 * e["M"] * e["K"] + 2.0 * e["M"] * kl + 4.0 * e["K"]  # x in, expanded x out, T out, factors
+    extras = {"svdq_smooth": {"shape": [e["M"], e["K"], e["N"], e["R"]], "ms": round(ms, 4),
+                              "tflops": round(e["flops"] / (ms * 1e-3) / 1e12, 1),
+                              "quant_nvfp4_lowrank_smooth_us": round(1e3 * ts / ns, 2),
+                              "quant_nvfp4_lowrank_smooth_gbs": round(qlr_bytes / (ts / ns * 1e-3) / 1e9, 1)}}
+    nl, tl = kern["quant_nvfp4_lowrank"]
+    extras["quant_nvfp4_lowrank_gbs"] = round((qlr_bytes - 4.0 * e["K"]) / (tl / nl * 1e-3) / 1e9, 1)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -216,6 +252,7 @@ def main():
         "parts": parts,
         "kernels": kernels,
         "quant_fp8_row_gbs": round(quant_gbs, 1),
+        "extras": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

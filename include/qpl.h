@@ -71,11 +71,20 @@ qpl_status quant_act_fp8_row(const uint16_t* x, int64_t M, int64_t K,
  * codes E2M1(x / d) (signed zeros when d == 0).
  *   x              bf16 [M,K]                  input
  *   input_scale    g, finite and > 0, with 6 g finite in fp32 (else QPL_ERR_ARG)
+ *   smooth         float [K] or NULL: SVDQuant smoothing factors (Nunchaku post,
+ *                  "Background: SVDQuant and Nunchaku": activation outliers move
+ *                  into the weights, whose column k carries smooth[k]).  When
+ *                  given, the quantized activation is x_hat[m,k] =
+ *                  bf16_rne(x[m,k] / smooth[k]) (correctly rounded fp32
+ *                  division).  The factors are device data the call does not
+ *                  check: they must be positive and finite and every x / smooth
+ *                  finite in bf16; otherwise the codes are unspecified.
  *   x_q            uint8 [M,K/2]               out: packed E2M1 codes
  *   x_block_scale  uint8 E4M3 [M,K/16]         out: block scales
+ * All pointers 16-byte aligned (smooth too when not NULL).
  */
 qpl_status quant_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, float input_scale,
-                           uint8_t* x_q, uint8_t* x_block_scale, void* stream);
+                           const float* smooth, uint8_t* x_q, uint8_t* x_block_scale, void* stream);
 
 /*
  * fp8r linear (guide, "Kernels" table, fp8r row: a row-wise scaled FP8 GEMM):
@@ -95,12 +104,15 @@ qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N,
  * by a block-scaled FP4 GEMM), optionally with the SVDQuant low-rank branch:
  *   y = bf16_rne( input_scale * weight_scale_2 *
  *                 sum_b sx[m,b] sw[n,b] sum_{k in b} e2m1(xq) e2m1(w)  +  (x L1) L2 )
- * where xq, sx come from quant_act_nvfp4(x, input_scale) and the low-rank term is
- * accumulated in fp32 before the single rounding to bf16.
+ * where xq, sx come from quant_act_nvfp4(x, input_scale, smooth) and the low-rank
+ * term is accumulated in fp32 before the single rounding to bf16.  With smooth,
+ * x in both terms is the smoothed x_hat that quant_act_nvfp4 defines (the
+ * weight and L1 of such a layer were built for x_hat).
  *   weight          uint8 [N,K/2]        packed E2M1
  *   weight_scale    uint8 E4M3 [N,K/16]
  *   weight_scale_2  global weight scale, finite and > 0
  *   input_scale     calibrated activation scale, finite and > 0, 6 * input_scale finite
+ *   smooth          float [K] smoothing factors or NULL (as in quant_act_nvfp4)
  *   lora_down       bf16 [K,R] (L1) or NULL when R == 0
  *   lora_up         bf16 [R,N] (L2) or NULL when R == 0
  *   R               rank, 0..128
@@ -109,7 +121,7 @@ qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N,
  */
 qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                          const uint8_t* weight, const uint8_t* weight_scale,
-                         float weight_scale_2, float input_scale,
+                         float weight_scale_2, float input_scale, const float* smooth,
                          const uint16_t* lora_down, const uint16_t* lora_up, int64_t R,
                          uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 

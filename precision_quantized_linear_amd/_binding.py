@@ -43,9 +43,9 @@ def load():
     P, I64, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "quant_act_fp8_row": [P, I64, I64, P, P, P],
-        "quant_act_nvfp4": [P, I64, I64, F, P, P, P],
+        "quant_act_nvfp4": [P, I64, I64, F, P, P, P, P],
         "qlinear_fp8r": [P, I64, I64, I64, P, P, P, P, SZ, P],
-        "qlinear_nvfp4": [P, I64, I64, I64, P, P, F, F, P, P, I64, P, P, SZ, P],
+        "qlinear_nvfp4": [P, I64, I64, I64, P, P, F, F, P, P, P, I64, P, P, SZ, P],
         "dequant_weight": [ctypes.c_int, P, P, F, I64, I64, P, P],
         "qpl_amax_bf16": [P, I64, P, P],
     }
@@ -104,14 +104,17 @@ def quant_act_fp8_row(x, x_q=None, x_scale=None, stream=None):
     return x_q, x_scale
 
 
-def quant_act_nvfp4(x, input_scale, x_q=None, x_block_scale=None, stream=None):
-    """bf16 [M,K] -> (packed E2M1 uint8 [M,K/2], E4M3 block scales uint8 [M,K/16])."""
+def quant_act_nvfp4(x, input_scale, smooth=None, x_q=None, x_block_scale=None, stream=None):
+    """bf16 [M,K] -> (packed E2M1 uint8 [M,K/2], E4M3 block scales uint8 [M,K/16]);
+    with smooth (float32 [K]) the quantized activation is bf16(x / smooth)."""
     M, K = x.shape
     _expect(x, torch.bfloat16, (M, K), "x")
+    if smooth is not None:
+        _expect(smooth, torch.float32, (K,), "smooth")
     x_q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device) if x_q is None else x_q
     x_block_scale = (torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
                      if x_block_scale is None else x_block_scale)
-    _check("quant_act_nvfp4", load().quant_act_nvfp4(_ptr(x), M, K, float(input_scale), _ptr(x_q),
+    _check("quant_act_nvfp4", load().quant_act_nvfp4(_ptr(x), M, K, float(input_scale), _ptr(smooth), _ptr(x_q),
                                                       _ptr(x_block_scale), _stream(stream)))
     return x_q, x_block_scale
 
@@ -142,11 +145,14 @@ def qlinear_fp8r(x, weight, weight_scale, y=None, workspace=None, stream=None):
 
 
 def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_down=None, lora_up=None, y=None,
-                  workspace=None, stream=None):
-    """y[M,N] bf16 = nvfp4 linear (+ (x L1) L2 when lora_down [K,R] / lora_up [R,N] are given)."""
+                  workspace=None, stream=None, smooth=None):
+    """y[M,N] bf16 = nvfp4 linear (+ (x L1) L2 when lora_down [K,R] / lora_up [R,N] are given);
+    with smooth (float32 [K]) both terms take the smoothed activation bf16(x / smooth)."""
     M, K = x.shape
     N = weight.shape[0]
     _expect(x, torch.bfloat16, (M, K), "x")
+    if smooth is not None:
+        _expect(smooth, torch.float32, (K,), "smooth")
     _expect(weight, torch.uint8, (N, K // 2), "weight")
     _expect(weight_scale, torch.uint8, (N, K // 16), "weight_scale")
     R = 0
@@ -157,7 +163,8 @@ def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_dow
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
     ws, nbytes = _workspace(QPL_NVFP4, M, K, N, R, workspace, x.device)
     _check("qlinear_nvfp4", load().qlinear_nvfp4(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale),
-                                                 float(weight_scale_2), float(input_scale), _ptr(lora_down),
+                                                 float(weight_scale_2), float(input_scale), _ptr(smooth),
+                                                 _ptr(lora_down),
                                                  _ptr(lora_up), R, _ptr(y), _ptr(ws), nbytes, _stream(stream)))
     return y
 

@@ -216,17 +216,17 @@ QPL_EXPORT qpl_status quant_act_fp8_row(const uint16_t* x, int64_t M, int64_t K,
   return launched(Timed(QPL_KERNEL_QUANT_FP8_ROW, st)(qpl::launch_quant_fp8_row(x, M, K, x_q, x_scale, st)));
 }
 
-QPL_EXPORT qpl_status quant_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, float input_scale, uint8_t* x_q,
-                                      uint8_t* x_block_scale, void* stream) {
+QPL_EXPORT qpl_status quant_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, float input_scale,
+                                      const float* smooth, uint8_t* x_q, uint8_t* x_block_scale, void* stream) {
   if (!x || !x_q || !x_block_scale) return QPL_ERR_NULL;
-  if (!aligned16(x) || !aligned16(x_q) || !aligned16(x_block_scale)) return QPL_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(x_q) || !aligned16(x_block_scale) || !aligned16(smooth)) return QPL_ERR_ALIGN;
   qpl_status s = check_dims(M, K);
   if (s != QPL_OK) return s;
   if (!positive_finite(input_scale) || !positive_finite(6.0f * input_scale)) return QPL_ERR_ARG;
   if ((s = check_device()) != QPL_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return launched(
-      Timed(QPL_KERNEL_QUANT_NVFP4, st)(qpl::launch_quant_nvfp4(x, M, K, input_scale, x_q, x_block_scale, st)));
+      Timed(QPL_KERNEL_QUANT_NVFP4, st)(qpl::launch_quant_nvfp4(x, M, K, input_scale, smooth, x_q, x_block_scale, st)));
 }
 
 QPL_EXPORT qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
@@ -251,10 +251,11 @@ QPL_EXPORT qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int6
 
 QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
                                     const uint8_t* weight_scale, float weight_scale_2, float input_scale,
-                                    const uint16_t* lora_down, const uint16_t* lora_up, int64_t R, uint16_t* y,
-                                    void* ws, size_t ws_bytes, void* stream) {
+                                    const float* smooth, const uint16_t* lora_down, const uint16_t* lora_up,
+                                    int64_t R, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !weight || !weight_scale || !y || !ws) return QPL_ERR_NULL;
-  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws))
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws) ||
+      !aligned16(smooth))
     return QPL_ERR_ALIGN;
   qpl_status s = check_gemm_dims(M, K, N);
   if (s != QPL_OK) return s;
@@ -284,13 +285,13 @@ QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int
              qpl::launch_lowrank_prep(lora_down, lora_up, K, N, R, kl, l1t, l2t, st)))) != QPL_OK)
       return s;
     if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
-             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, l1t, kl, gscale, xe, t, st)))) != QPL_OK)
+             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, smooth, l1t, kl, gscale, xe, t, st)))) != QPL_OK)
       return s;
     lr.t = t;
     lr.l2t = l2t;
     lr.kl = kl;
   } else if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(
-                  qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, xe, st)))) != QPL_OK) {
+                  qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, smooth, xe, st)))) != QPL_OK) {
     return s;
   }
   // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue

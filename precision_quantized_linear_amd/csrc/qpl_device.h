@@ -29,6 +29,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// SVDQuant smoothing of a bf16 pair (Nunchaku post, "Background: SVDQuant and
+// Nunchaku": activation outliers move into the weights, so input channel k is
+// divided by its factor): bf16_rne(x / l) per half, with the correctly rounded
+// fp32 division of this build.  l0 divides the low half, l1 the high half.
+__device__ __forceinline__ uint32_t smooth_pair(uint32_t pair, float l0, float l1) {
+  return f32_to_bf16(bf16_lo(pair) / l0) | (f32_to_bf16(bf16_hi(pair) / l1) << 16);
+}
+
 // |v| (as raw fp32 bits without sign) -> E4M3 magnitude code.
 //   below 2^-6: the subnormal grid of step 2^-9, code = rint(|v| * 2^9) (0..8);
 //   otherwise: round the fp32 mantissa to 3 bits (ties to even) and rebias the

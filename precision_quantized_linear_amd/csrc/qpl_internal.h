@@ -19,18 +19,21 @@ Nvfp4ScaleTable nvfp4_scale_table(float g);
 
 hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                                 hipStream_t stream);
-hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, uint8_t* xq,
+// lam: SVDQuant smoothing factors [K] (x is divided by them first) or nullptr.
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
                               uint8_t* xbs, hipStream_t stream);
 // nvfp4 quantization that writes each quantized value e2m1(q) * dec(sf) as bf16
 // (exact: at most 6 significant bits) instead of packed codes.
-hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, uint16_t* xe,
-                                     hipStream_t stream);
+hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                     uint16_t* xe, hipStream_t stream);
 // The same, fused with the low-rank down-projection: t [M, kl] bf16 receives
 // T / tdiv (T = x L1, fp32, one correctly rounded division) as [hi | lo] halves of
 // kl / 2 columns each; l1t [kl / 2, K] is L1 transposed (zero past R); kl / 2 is
-// a multiple of 32, at most 128.
-hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const uint16_t* l1t,
-                                             int64_t kl, float tdiv, uint16_t* xe, uint16_t* t, hipStream_t stream);
+// a multiple of 32, at most 128.  With lam, both the quantized values and T are
+// computed from the smoothed activation.
+hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                             const uint16_t* l1t, int64_t kl, float tdiv, uint16_t* xe, uint16_t* t,
+                                             hipStream_t stream);
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
                                hipStream_t stream);

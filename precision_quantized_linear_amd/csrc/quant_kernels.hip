@@ -192,14 +192,33 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
   p[4] = v1.x; p[5] = v1.y; p[6] = v1.z; p[7] = v1.w;
 }
 
+// Smoothing of one 16-element block (b-th block of the tensor, kb blocks per row):
+// element k of the row is divided by lam[k].  p[j] holds elements 2j and 2j + 1.
+template <bool SMOOTH>
+__device__ __forceinline__ void smooth_block(uint32_t (&p)[8], const float* __restrict__ lam, int64_t b,
+                                             int64_t kb) {
+  if constexpr (SMOOTH) {
+    const f32x4* l = reinterpret_cast<const f32x4*>(lam + (b % kb) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = l[i];
+      p[2 * i] = smooth_pair(p[2 * i], v[0], v[1]);
+      p[2 * i + 1] = smooth_pair(p[2 * i + 1], v[2], v[3]);
+    }
+  }
+}
+
 __device__ __forceinline__ float block_absmax(const uint32_t* p, int n) {
   uint32_t m = 0;
   for (int i = 0; i < n; ++i) m = absmax_acc(m, p[i]);
   return absmax_value(m);
 }
 
+// SMOOTH: the block is first smoothed by lam (kb = K / 16 blocks per row).
+template <bool SMOOTH>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict__ x, int64_t nblocks,
                                                      float c6g, float rc6g, Nvfp4ScaleTable tab,
+                                                     const float* __restrict__ lam, int64_t kb,
                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xbs) {
   __shared__ float tab_d[128], tab_rd[128];
   load_scale_table(tab, tab_d, tab_rd);
@@ -207,6 +226,7 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict_
   if (b >= nblocks) return;
   uint32_t p[8];
   load_block(x, b, p);
+  smooth_block<SMOOTH>(p, lam, b, kb);
   const Nvfp4Block s = nvfp4_scale(block_absmax(p, 8), c6g, rc6g, tab_d, tab_rd);
   reinterpret_cast<u32x2*>(xq)[b] = u32x2{nvfp4_word<true>(p, s), nvfp4_word<true>(p + 4, s)};
   xbs[b] = (uint8_t)s.sf;
@@ -229,8 +249,10 @@ __device__ __forceinline__ void expand_word(uint32_t w, float dsf, uint32_t* o) 
   o[3] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), dsf);
 }
 
+template <bool SMOOTH>
 __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __restrict__ x, int64_t nblocks,
                                                             float c6g, float rc6g, Nvfp4ScaleTable tab,
+                                                            const float* __restrict__ lam, int64_t kb,
                                                             uint16_t* __restrict__ xe) {
   __shared__ float tab_d[128], tab_rd[128];
   load_scale_table(tab, tab_d, tab_rd);
@@ -238,6 +260,7 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __re
   if (b >= nblocks) return;
   uint32_t p[8];
   load_block(x, b, p);
+  smooth_block<SMOOTH>(p, lam, b, kb);
   const Nvfp4Block s = nvfp4_scale(block_absmax(p, 8), c6g, rc6g, tab_d, tab_rd);
   uint32_t o[8];
   expand_word(nvfp4_word<false>(p, s), s.dsf, o);
@@ -272,27 +295,35 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __re
 // the row, so the MFMA operand reads (16 rows, one chunk) hit 16 different bank
 // groups; the load instructions fill slots in order and fetch the chunk each slot
 // holds.
-template <int NCT>
+//
+// SMOOTH (SVDQuant smoothing): each stage also holds the tile's TK smoothing
+// factors (one dword load per wavefront: wave w moves factors 64 w .. 64 w + 63,
+// zeros past TK or K).  Step 1 divides its values by them, quantizes the smoothed
+// bf16 values and writes them back over the tile, and step 2 waits for every
+// wave's write-back, so that both branches read the same smoothed activation.
+template <int NCT, bool SMOOTH>
 struct LrTile {
   static constexpr int TK = NCT <= 2 ? 256 : 128;  // k per tile
   static constexpr int CPR = TK / 8;                // 16-byte chunks per tile row
   static constexpr int XB = 32 * TK * 2;            // x tile bytes
   static constexpr int LB = 32 * NCT * TK * 2;      // L1^T tile bytes
-  static constexpr int SB = XB + LB;                // stage bytes
+  static constexpr int FB = SMOOTH ? 8 * 256 : 0;  // smoothing factor bytes (one 256-byte slot per wave)
+  static constexpr int SB = XB + LB + FB;           // stage bytes
   static constexpr int S = (NCT == 1 || NCT == 3) ? 4 : 3;  // stages in the ring (<= 128 KB, 144 KB for NCT 2)
   static constexpr int NW = 8;                      // wavefronts
   static constexpr int XI = XB / 1024 / NW;         // x loads (and xe stores) per wave per tile, 1 KB each
   static constexpr int LI = LB / 1024 / NW;         // L1^T loads per wave per tile
-  static constexpr int DW = XI + LI;
+  static constexpr int DW = XI + LI + (SMOOTH ? 1 : 0);  // loads per wave per tile
 };
 
-template <int NCT>
+template <int NCT, bool SMOOTH>
 __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                                float c6g, float rc6g, Nvfp4ScaleTable tab,
                                                                const uint16_t* __restrict__ l1t, int64_t kl,
-                                                               int rpw, float tdiv, uint16_t* __restrict__ xe,
+                                                               const float* __restrict__ lam, int rpw, float tdiv,
+                                                               uint16_t* __restrict__ xe,
                                                                uint16_t* __restrict__ t_out) {
-  using C = LrTile<NCT>;
+  using C = LrTile<NCT, SMOOTH>;
   constexpr int TK = C::TK, CPR = C::CPR, S = C::S, XI = C::XI, LI = C::LI, NW = C::NW;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S * C::SB];
   __shared__ float tab_d[128], tab_rd[128];
@@ -304,6 +335,7 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
   const uint32_t pitch = (uint32_t)(K * 2);
   const u32x4 dx = make_desc(x + m0 * K, rows * pitch);
   const u32x4 dl = make_desc(l1t, (int64_t)32 * NCT * pitch);
+  const u32x4 df = make_desc(lam, SMOOTH ? K * 4 : 0);
   const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(xe + m0 * K, (short)0, (int)(rows * pitch),
                                                                       (int)kRawBufferWord3);
   const uint32_t lbase = lds_address(lds);
@@ -329,6 +361,11 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
 #pragma unroll
     for (int j = 0; j < LI; ++j)
       dma16(st + C::XB + (uint32_t)((wv * LI + j) * 1024), voff(slot_row(j, LI), slot_chunk(j, LI), kt), dl, soff);
+    if constexpr (SMOOTH) {
+      const int64_t k = (int64_t)kt * TK + wv * 64 + lane;
+      dma4(st + C::XB + C::LB + (uint32_t)(wv * 256),
+           wv * 64 < TK && k < K ? (uint32_t)(k * 4) : kOutOfRange, df, 0);
+    }
   };
 
   f32x16 acc[NCT];
@@ -350,7 +387,7 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
     QPL_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();  // every wave's part of tile kt is in LDS; tile kt - 1's buffer is free
     issue(kt + S - 1);             // past the end: out-of-range offsets, zeros into an unused buffer
-    const uint8_t* xt = lds + (kt % S) * C::SB;
+    uint8_t* xt = lds + (kt % S) * C::SB;
     const uint8_t* lt = xt + C::XB;
 
     // 1. quantize and expand this wave's part of the x tile
@@ -363,8 +400,20 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, re, (int)kOutOfRange, 0, 0);
         continue;
       }
-      const u32x4 v = *reinterpret_cast<const u32x4*>(xt + ((wv * XI + j) * 64 + lane) * 16);
-      const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+      u32x4* slot = reinterpret_cast<u32x4*>(xt + ((wv * XI + j) * 64 + lane) * 16);
+      const u32x4 v = *slot;
+      uint32_t p[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (SMOOTH) {
+        if ((int64_t)kt * TK + 8 * c < K) {  // chunks past K hold zeros and no factors
+          const f32x4* f = reinterpret_cast<const f32x4*>(xt + C::XB + C::LB + 32 * c);
+          const f32x4 f0 = f[0], f1 = f[1];
+          p[0] = smooth_pair(p[0], f0[0], f0[1]);
+          p[1] = smooth_pair(p[1], f0[2], f0[3]);
+          p[2] = smooth_pair(p[2], f1[0], f1[1]);
+          p[3] = smooth_pair(p[3], f1[2], f1[3]);
+          *slot = u32x4{p[0], p[1], p[2], p[3]};
+        }
+      }
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = absmax_acc(m, p[i]);
@@ -377,6 +426,11 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, re,
                                              so == kOutOfRange ? (int)kOutOfRange : (int)(so + (uint32_t)kt * TK * 2),
                                              0, 0);
+    }
+
+    if constexpr (SMOOTH) {
+      QPL_WAIT_LGKM0();
+      __builtin_amdgcn_s_barrier();  // every wave's smoothed values are in the tile
     }
 
     // 2. T += x_tile L1t_tile^T over this wave's part of the k range
@@ -456,26 +510,55 @@ Nvfp4ScaleTable nvfp4_scale_table(float g) {
   return t;
 }
 
-hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, uint8_t* xq, uint8_t* xbs,
-                              hipStream_t stream) {
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
+                              uint8_t* xbs, hipStream_t stream) {
   const int64_t nb = M * (K / 16);
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, c6g, rc6g,
-                     nvfp4_scale_table(g), xq, xbs);
+  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  if (lam)
+    hipLaunchKernelGGL(k_quant_nvfp4<true>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g), lam,
+                       K / 16, xq, xbs);
+  else
+    hipLaunchKernelGGL(k_quant_nvfp4<false>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g), lam,
+                       K / 16, xq, xbs);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, uint16_t* xe,
-                                     hipStream_t stream) {
+hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                     uint16_t* xe, hipStream_t stream) {
   const int64_t nb = M * (K / 16);
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  hipLaunchKernelGGL(k_quant_nvfp4_expand, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, x, nb, c6g,
-                     rc6g, nvfp4_scale_table(g), xe);
+  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  if (lam)
+    hipLaunchKernelGGL(k_quant_nvfp4_expand<true>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
+                       lam, K / 16, xe);
+  else
+    hipLaunchKernelGGL(k_quant_nvfp4_expand<false>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
+                       lam, K / 16, xe);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const uint16_t* l1t,
-                                             int64_t kl, float tdiv, uint16_t* xe, uint16_t* t, hipStream_t stream) {
+template <int NCT, bool SMOOTH>
+static void launch_expand_lr(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K, float c6g,
+                             float rc6g, const Nvfp4ScaleTable& tab, const uint16_t* l1t, int64_t kl,
+                             const float* lam, int rpw, float tdiv, uint16_t* xe, uint16_t* t) {
+  hipLaunchKernelGGL((k_quant_nvfp4_expand_lr<NCT, SMOOTH>), grid, dim3(512), 0, stream, x, M, K, c6g, rc6g, tab,
+                     l1t, kl, lam, rpw, tdiv, xe, t);
+}
+
+template <int NCT>
+static void launch_expand_lr(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K, float c6g,
+                             float rc6g, const Nvfp4ScaleTable& tab, const uint16_t* l1t, int64_t kl,
+                             const float* lam, int rpw, float tdiv, uint16_t* xe, uint16_t* t) {
+  if (lam)
+    launch_expand_lr<NCT, true>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t);
+  else
+    launch_expand_lr<NCT, false>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t);
+}
+
+hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                             const uint16_t* l1t, int64_t kl, float tdiv, uint16_t* xe, uint16_t* t,
+                                             hipStream_t stream) {
   // buffer offsets are 32-bit: the L1^T tile rows (at most 128) times the pitch
   if (K > (int64_t{1} << 21)) return hipErrorInvalidValue;
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
@@ -483,22 +566,13 @@ hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64
   // about one workgroup per CU (256 on MI355X), at most 32 rows each
   const int64_t rpw64 = (M + 255) / 256;
   const int rpw = (int)(rpw64 < 32 ? rpw64 : 32);
-  const dim3 grid((unsigned)((M + rpw - 1) / rpw)), block(512);
+  const dim3 grid((unsigned)((M + rpw - 1) / rpw));
   switch (kl / 64) {  // rpad / 32
-    case 1:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<1>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
-      break;
-    case 2:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<2>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
-      break;
-    case 3:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<3>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
-      break;
-    case 4:
-      hipLaunchKernelGGL(k_quant_nvfp4_expand_lr<4>, grid, block, 0, stream, x, M, K, c6g, rc6g, tab, l1t, kl, rpw, tdiv, xe, t);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 1: launch_expand_lr<1>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
+    case 2: launch_expand_lr<2>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
+    case 3: launch_expand_lr<3>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
+    case 4: launch_expand_lr<4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -69,9 +69,10 @@ def test_quant_validation(lib):
     assert lib.quant_act_fp8_row(A, 0, 16, B, C, None) == SHAPE
     assert lib.quant_act_fp8_row(A, 4, 24, B, C, None) == SHAPE
     assert lib.quant_act_fp8_row(A, 4, 0, B, C, None) == SHAPE
-    assert lib.quant_act_nvfp4(A, 4, 32, 1.0, None, C, None) == NULL
+    assert lib.quant_act_nvfp4(A, 4, 32, 1.0, None, None, C, None) == NULL
     for bad in (0.0, -1.0, float("inf"), float("nan"), 1e38):
-        assert lib.quant_act_nvfp4(A, 4, 32, bad, B, C, None) == ARG, bad
+        assert lib.quant_act_nvfp4(A, 4, 32, bad, None, B, C, None) == ARG, bad
+    assert lib.quant_act_nvfp4(A, 4, 32, 1.0, MIS, B, C, None) == ALIGN  # smoothing factors
 
 
 def test_qlinear_validation(lib):
@@ -81,13 +82,14 @@ def test_qlinear_validation(lib):
     assert lib.qlinear_fp8r(A, 4, 32, 8, B, C, D, A, 10, None) == WORKSPACE
     assert lib.qlinear_fp8r(A, 4, 32, 8, B, MIS, D, A, ws, None) == ALIGN
     args = (A, 4, 32, 8, B, C)
-    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, None, 0, D, A, 10, None) == WORKSPACE
-    assert lib.qlinear_nvfp4(*args, 0.0, 1.0, None, None, 0, D, A, ws, None) == ARG
-    assert lib.qlinear_nvfp4(*args, 1.0, float("nan"), None, None, 0, D, A, ws, None) == ARG
-    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, A, None, 4, D, A, ws, None) == NULL
-    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, A, B, 0, D, A, ws, None) == ARG
-    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, A, B, 200, D, A, ws, None) == SHAPE
-    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, MIS, B, 4, D, A, ws, None) == ALIGN
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, None, None, 0, D, A, 10, None) == WORKSPACE
+    assert lib.qlinear_nvfp4(*args, 0.0, 1.0, None, None, None, 0, D, A, ws, None) == ARG
+    assert lib.qlinear_nvfp4(*args, 1.0, float("nan"), None, None, None, 0, D, A, ws, None) == ARG
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, A, None, 4, D, A, ws, None) == NULL
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, A, B, 0, D, A, ws, None) == ARG
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, A, B, 200, D, A, ws, None) == SHAPE
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, MIS, B, 4, D, A, ws, None) == ALIGN
+    assert lib.qlinear_nvfp4(*args, 1.0, 1.0, MIS, None, None, 0, D, A, ws, None) == ALIGN  # smoothing factors
     assert lib.dequant_weight(5, A, B, 1.0, 4, 32, C, None) == ARG
     assert lib.dequant_weight(1, A, B, -1.0, 4, 32, C, None) == ARG
     assert lib.dequant_weight(0, A, None, 1.0, 4, 32, C, None) == NULL
@@ -98,7 +100,7 @@ def test_qlinear_validation(lib):
 @pytest.mark.skipif(torch.cuda.is_available(), reason="forces the no-device status; a GPU is present")
 def test_no_device_status(lib):
     assert lib.quant_act_fp8_row(A, 4, 16, B, C, None) == DEVICE
-    assert lib.qlinear_nvfp4(A, 4, 32, 8, B, C, 1.0, 1.0, None, None, 0, D, A, 1 << 30, None) == DEVICE
+    assert lib.qlinear_nvfp4(A, 4, 32, 8, B, C, 1.0, 1.0, None, None, None, 0, D, A, 1 << 30, None) == DEVICE
 
 
 def test_timing_collect_empty(lib):

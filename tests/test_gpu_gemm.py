@@ -26,9 +26,10 @@ import torch
 import precision_quantized_linear_amd as qpl
 from helpers import bf16_bits, to_dev, to_dev_bf16
 from oracle.formats import bf16_bits_to_f32
-from oracle.quant import amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4
+from oracle.quant import (amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4,
+                          smooth_bf16)
 from oracle.reference import (check_gemm, dequant_fp8r, dequant_nvfp4, lowrank_abs, lowrank_ref)
-from synthetic import calibration_batches, make
+from synthetic import calibration_batches, make, smooth_factors
 
 pytestmark = pytest.mark.gpu
 
@@ -64,20 +65,24 @@ def fp8r_case(d, rows):
     return check_gemm(bf16_bits(y)[rows], ref, absum, K, gamma=fp8_gamma(K))
 
 
-def nvfp4_case(d, rows, g_in):
+def nvfp4_case(d, rows, g_in, lam=None):
+    # lam: SVDQuant smoothing factors; the reference then starts from bf16(x / lam)
     x, w = d["x"], d["w"]
     K = x.shape[1]
     g_w = global_scale(amax_bf16(w))
-    xp, xb = quant_nvfp4(x[rows], g_in)
+    xr = x[rows] if lam is None else smooth_bf16(x[rows], lam)
+    xp, xb = quant_nvfp4(xr, g_in)
     wp, wb = quant_nvfp4(w, g_w)
     a, b = dequant_nvfp4(xp, xb, g_in), dequant_nvfp4(wp, wb, g_w)
     ref, absum = a @ b.T, np.abs(a) @ np.abs(b).T
     extra = None
     lora = {}
     if "l1" in d:
-        ref = ref + lowrank_ref(x[rows], d["l1"], d["l2"])
-        extra = lowrank_abs(x[rows], d["l1"], d["l2"])
+        ref = ref + lowrank_ref(xr, d["l1"], d["l2"])
+        extra = lowrank_abs(xr, d["l1"], d["l2"])
         lora = dict(lora_down=to_dev_bf16(d["l1"]), lora_up=to_dev_bf16(d["l2"]))
+    if lam is not None:
+        lora["smooth"] = to_dev(lam)
     y = qpl.qlinear_nvfp4(to_dev_bf16(x), to_dev(wp), to_dev(wb), g_w, g_in, **lora)
     torch.cuda.synchronize()
     return check_gemm(bf16_bits(y)[rows], ref, absum, K, extra_abs=extra)
@@ -163,6 +168,36 @@ def test_last_round_tiles(scheme, M, N):
         g_in = calibrate_input_scale(calibration_batches(name, M=64, K=K))
         say("last round", name, M, K, N, "R", d.get("R", 0))
         r = nvfp4_case(d, rows, g_in)
+    say(r)
+    assert r["ok"], r
+
+
+def smoothed_scale(name, lam, K):
+    return calibrate_input_scale(smooth_bf16(b, lam) for b in calibration_batches(name, M=64, K=K))
+
+
+@pytest.mark.parametrize("name,M,K,N,R", [
+    ("svdq_w4a4", None, None, None, None),      # full size, sampled rows
+    ("svdq_w4a4", 300, 448, 264, None),         # ragged
+    ("svdq_w4a4", 37, 272, 72, None),           # K % 32 == 16
+    ("svdq_w4a4", 1, 16, 1, None),
+    ("svdq_w4a4", 130, 256, 200, 64),           # two 32-column groups of T
+    ("svdq_w4a4", 45, 208, 200, 100),           # four groups, TK = 128
+    ("svdq_w4a4", 70, 320, 96, 80),             # three groups
+    ("nvfp4_dit", 300, 400, 520, 0),            # smoothing without the low-rank branch
+])
+def test_qlinear_nvfp4_smoothed(name, M, K, N, R):
+    d = make(name, M=M, K=K, N=N)
+    if R:
+        rng = np.random.default_rng(R)
+        from synthetic import bf16_round
+        d["l1"] = bf16_round((rng.standard_normal((d["K"], R)) * 0.05).astype(np.float32))
+        d["l2"] = bf16_round((rng.standard_normal((R, d["N"])) * 0.05).astype(np.float32))
+    lam = smooth_factors(name, K=d["K"])
+    g_in = smoothed_scale(name, lam, d["K"])
+    rows = sample_rows(d["M"]) if M is None else np.arange(d["M"])
+    say("qlinear_nvfp4 smoothed", name, d["M"], d["K"], d["N"], "R", d["l1"].shape[1] if "l1" in d else 0)
+    r = nvfp4_case(d, rows, g_in, lam)
     say(r)
     assert r["ok"], r
 

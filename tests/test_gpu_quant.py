@@ -7,9 +7,10 @@ import torch
 import precision_quantized_linear_amd as qpl
 from helpers import adversarial_rows, bf16_bits, host, to_dev, to_dev_bf16
 from oracle.formats import bf16_bits_to_f32
-from oracle.quant import amax_bf16, global_scale, quant_fp8_row, quant_nvfp4
+from oracle.quant import (amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4,
+                          smooth_bf16)
 from oracle.reference import dequant_weight_fp8r, dequant_weight_nvfp4
-from synthetic import bf16_round, make
+from synthetic import bf16_round, calibration_batches, make, smooth_factors
 
 pytestmark = pytest.mark.gpu
 
@@ -126,6 +127,49 @@ def test_quant_nvfp4_exact_ties():
     bits = np.tile(bf16_round(row), (4, 4))
     say("quant_act_nvfp4 ties")
     assert_nvfp4_equal(bits, np.float32(0.25))
+
+
+def assert_nvfp4_smoothed_equal(bits, g, lam):
+    cq, cs = quant_nvfp4(smooth_bf16(bits, lam), g)
+    q, sc = qpl.quant_act_nvfp4(to_dev_bf16(bits), g, smooth=to_dev(lam))
+    torch.cuda.synchronize()
+    gq, gs = host(q), host(sc)
+    assert np.array_equal(gs, cs), f"{np.count_nonzero(gs != cs)} block scales differ"
+    bad = np.argwhere(gq != cq)
+    assert bad.size == 0, f"{len(bad)} code bytes differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("M,K", [(None, None), (300, 400), (37, 272), (1, 16)])
+def test_quant_nvfp4_smoothed(M, K):
+    # SVDQuant smoothing: codes of bf16(x / smooth), input_scale calibrated on smoothed batches
+    d = make("svdq_w4a4", M=M, K=K)
+    lam = smooth_factors("svdq_w4a4", K=d["K"])
+    g = calibrate_input_scale(smooth_bf16(b, lam) for b in calibration_batches("svdq_w4a4", M=64, K=d["K"]))
+    say("quant_act_nvfp4 smoothed", d["x"].shape, g)
+    assert_nvfp4_smoothed_equal(d["x"], g, lam)
+
+
+def test_quant_nvfp4_smoothed_adversarial():
+    # factors that are powers of two, all-ones mantissas, tiny (x / smooth near the
+    # top of bf16) and huge (quotients in the fp32 and bf16 subnormal range), over
+    # rows with signed zeros and subnormal inputs
+    K = 256
+    x = adversarial_rows(K, seed=5)
+    rng = np.random.default_rng(6)
+    lam = np.exp(rng.uniform(-4, 4, size=K)).astype(np.float32)
+    lam[0:16] = np.ldexp(1.0, rng.integers(-20, 21, size=16)).astype(np.float32)
+    lam[16:32] = np.nextafter(np.ldexp(np.float32(1), rng.integers(-5, 6, size=16)).astype(np.float32),
+                              np.float32(0))
+    lam[32:48] = np.float32(1e-30)
+    lam[48:64] = np.float32(3e37)
+    lam[64:80] = np.float32(1e38)
+    # quotients that overflow bf16 are outside the contract: those inputs become 1.0
+    with np.errstate(over="ignore"):
+        x[~np.isfinite(bf16_bits_to_f32(smooth_bf16(x, lam)))] = 0x3F80
+    assert np.all(np.isfinite(bf16_bits_to_f32(smooth_bf16(x, lam))))
+    for g in (1e-30, 0.01, 1e6):
+        say("quant_act_nvfp4 smoothed adversarial", g)
+        assert_nvfp4_smoothed_equal(x, g, lam)
 
 
 def test_dequant_weight_fp8r():
