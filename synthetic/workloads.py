@@ -45,6 +45,10 @@ WORKLOADS = {
     "nvfp4_mlp_down_cfg": dict(c=4, scheme="nvfp4", M=9216, K=12288, N=3072, dist="t4", frac_out=0.01, mult=10.0, n_cal=8),
     # SVDQuant-style W4A4: nvfp4 residual + rank-32 bf16 branch
     "svdq_w4a4": dict(c=5, scheme="nvfp4", M=4608, K=3072, N=3072, dist="normal", frac_out=0.01, mult=10.0, n_cal=8, R=32),
+    # weight-only 4-bit modulation projections (one conditioning vector per image):
+    # FLUX adanorm_zero 3072 -> 6 x 3072 and adanorm_single 3072 -> 3 x 3072, group 64
+    "awq_adanorm_zero": dict(c=6, scheme="w4a16", M=1, K=3072, N=18432, dist="normal", frac_out=0.0, mult=1.0, G=64),
+    "awq_adanorm_single": dict(c=7, scheme="w4a16", M=1, K=3072, N=9216, dist="normal", frac_out=0.0, mult=1.0, G=64),
 }
 
 
