@@ -21,7 +21,8 @@ timed region (the library's event timing, limited to that kernel).  `parts` and
 `kernels` come from a second pass of the same steps with every launch timed.  The
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
 (rank 0, one GPU only).  `extras` times what lies beyond the step: the svdq linear
-with SVDQuant smoothing factors.
+with SVDQuant smoothing factors, and the weight-only 4-bit (awq_w4a16) GEMV at the
+FLUX modulation shapes.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -235,6 +236,33 @@ def main():
                               "quant_nvfp4_lowrank_smooth_gbs": round(qlr_bytes / (ts / ns * 1e-3) / 1e9, 1)}}
     nl, tl = kern["quant_nvfp4_lowrank"]
     extras["quant_nvfp4_lowrank_gbs"] = round((qlr_bytes - 4.0 * e["K"]) / (tl / nl * 1e-3) / 1e9, 1)
+
+    # ---------------------------------------------------------------- beyond the step: weight-only 4-bit
+    # FLUX modulation projections (awq_w4a16) at one and two conditioning rows,
+    # weights quantized by the library's quantizer; HBM-bound, so bytes per launch
+    # (codes + scales + zero points + x + y) over the kernel's event time.
+    for name, M in (("awq_adanorm_zero", 1), ("awq_adanorm_zero", 2), ("awq_adanorm_single", 1)):
+        d = make(name, M=M)
+        G, K, N = d["spec"]["G"], d["K"], d["N"]
+        xa = bf16(d["x"])
+        wa = bf16(d["w"])
+        wq, wsc, wz = qpl.quant_weight_awq(wa, G)
+        del wa
+        ya = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup):
+            qpl.qlinear_awq_w4a16(xa, wq, wsc, wz, G, y=ya)
+        torch.cuda.synchronize()
+        qpl.timing_collect()
+        qpl.timing_select(["gemv_w4a16"])
+        for _ in range(4 * args.steps):
+            qpl.qlinear_awq_w4a16(xa, wq, wsc, wz, G, y=ya)
+        torch.cuda.synchronize()
+        qpl.timing_select([])
+        na, ta = qpl.timing_collect()["gemv_w4a16"]
+        nbytes = N * K / 2 + 3.0 * N * (K // G) + 2.0 * M * K + 2.0 * M * N
+        gbs = nbytes / (ta / na * 1e-3) / 1e9
+        extras[f"{name}_m{M}"] = {"shape": [M, K, N, G], "us": round(1e3 * ta / na, 2), "gbs": round(gbs, 1),
+                                  "frac_hbm": round(gbs / HBM_GBS, 4)}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

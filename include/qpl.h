@@ -126,6 +126,35 @@ qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                          uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Weight-only 4-bit linear with bf16 activations (Nunchaku post, "Introducing
+ * Nunchaku Lite": the awq_w4a16 layer, 4-bit weights and 16-bit activations for
+ * the memory-bound adaptive-normalization and modulation projections).  The post
+ * gives no format; this library's:
+ *   weight        uint8 [N,K/2]     codes q in 0..15, channel 2j in the low nibble of byte j
+ *   weight_scale  bf16 [N,K/group]  one scale s per group of `group` input channels
+ *   weight_zero   uint8 [N,K/group] one zero point z in 0..15 per group
+ *   group         32, 64 or 128; K % group == 0 (else QPL_ERR_ARG / QPL_ERR_SHAPE)
+ * The weight value is (q - z) * s, exact in fp32.
+ *
+ * quant_weight_awq: quantize a bf16 weight w [N,K] into that format.  Per group:
+ *   hi = max(max w, 0), lo = min(min w, 0), s = bf16_rne(fp32((hi - lo) / 15)),
+ *   z = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15)
+ *   (fp32, correctly rounded divisions, ties to even); s == 0 gives q = z = 0.
+ *   Activation-aware channel scaling, if any, is applied to w beforehand.
+ *   The group spans (hi - lo) must be finite in fp32.
+ *
+ * qlinear_awq_w4a16: y[m,n] = bf16_rne( sum_k x[m,k] (q[n,k] - z[n,g]) s[n,g] ),
+ *   g = k / group, fp32 accumulation.  x bf16 [M,K], y bf16 [M,N].  Built for
+ *   small M (one row per image): the weight is streamed once per two rows of x.
+ * All pointers 16-byte aligned.  No workspace.
+ */
+qpl_status quant_weight_awq(const uint16_t* w, int64_t N, int64_t K, int64_t group,
+                            uint8_t* w_q, uint16_t* w_scale, uint8_t* w_zero, void* stream);
+qpl_status qlinear_awq_w4a16(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                             const uint8_t* weight, const uint16_t* weight_scale,
+                             const uint8_t* weight_zero, int64_t group, uint16_t* y, void* stream);
+
+/*
  * Dequantize a weight to bf16 (guide, "Kernels" section, last paragraph: on other
  * devices the weight is dequantized to compute_dtype on every forward and the
  * layer runs as a regular linear; that linear is the caller's).
@@ -177,7 +206,9 @@ typedef enum {
   QPL_KERNEL_AMAX = 8,
   QPL_KERNEL_WEIGHT_BF16 = 9,       /* nvfp4 weight expansion inside qlinear_nvfp4 */
   QPL_KERNEL_QUANT_NVFP4_LOWRANK = 10, /* nvfp4 quantize fused with x L1 (qlinear_nvfp4, R > 0) */
-  QPL_KERNEL_COUNT = 11
+  QPL_KERNEL_QUANT_W4G = 11,        /* quant_weight_awq */
+  QPL_KERNEL_GEMV_W4A16 = 12,       /* qlinear_awq_w4a16 */
+  QPL_KERNEL_COUNT = 13
 } qpl_kernel;
 
 void qpl_timing_enable(int on);

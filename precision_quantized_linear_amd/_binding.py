@@ -16,12 +16,12 @@ QPL_FP8R = 0
 QPL_NVFP4 = 1
 
 EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp4", "dequant_weight",
-           "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
+           "quant_weight_awq", "qlinear_awq_w4a16", "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
            "qpl_timing_enable", "qpl_timing_select", "qpl_timing_collect")
 
 # qpl_kernel order of include/qpl.h
 KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_bf16", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
-           "lowrank_prep", "dequant", "amax", "weight_bf16", "quant_nvfp4_lowrank")
+           "lowrank_prep", "dequant", "amax", "weight_bf16", "quant_nvfp4_lowrank", "quant_w4g", "gemv_w4a16")
 
 _lib = None
 
@@ -47,6 +47,8 @@ def load():
         "qlinear_fp8r": [P, I64, I64, I64, P, P, P, P, SZ, P],
         "qlinear_nvfp4": [P, I64, I64, I64, P, P, F, F, P, P, P, I64, P, P, SZ, P],
         "dequant_weight": [ctypes.c_int, P, P, F, I64, I64, P, P],
+        "quant_weight_awq": [P, I64, I64, I64, P, P, P, P],
+        "qlinear_awq_w4a16": [P, I64, I64, I64, P, P, P, I64, P, P],
         "qpl_amax_bf16": [P, I64, P, P],
     }
     for name, args in sig.items():
@@ -166,6 +168,33 @@ def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_dow
                                                  float(weight_scale_2), float(input_scale), _ptr(smooth),
                                                  _ptr(lora_down),
                                                  _ptr(lora_up), R, _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def quant_weight_awq(w, group=64, w_q=None, w_scale=None, w_zero=None, stream=None):
+    """bf16 weight [N,K] -> (codes uint8 [N,K/2], scales bf16 [N,K/group], zero points uint8 [N,K/group])."""
+    N, K = w.shape
+    _expect(w, torch.bfloat16, (N, K), "w")
+    G = K // group
+    w_q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device) if w_q is None else w_q
+    w_scale = torch.empty((N, G), dtype=torch.bfloat16, device=w.device) if w_scale is None else w_scale
+    w_zero = torch.empty((N, G), dtype=torch.uint8, device=w.device) if w_zero is None else w_zero
+    _check("quant_weight_awq", load().quant_weight_awq(_ptr(w), N, K, group, _ptr(w_q), _ptr(w_scale), _ptr(w_zero),
+                                                        _stream(stream)))
+    return w_q, w_scale, w_zero
+
+
+def qlinear_awq_w4a16(x, weight, weight_scale, weight_zero, group=64, y=None, stream=None):
+    """y[M,N] bf16 = x [M,K] (bf16) times the group-wise 4-bit weight, dequantized as (q - z) s."""
+    M, K = x.shape
+    N = weight.shape[0]
+    _expect(x, torch.bfloat16, (M, K), "x")
+    _expect(weight, torch.uint8, (N, K // 2), "weight")
+    _expect(weight_scale, torch.bfloat16, (N, K // group), "weight_scale")
+    _expect(weight_zero, torch.uint8, (N, K // group), "weight_zero")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _check("qlinear_awq_w4a16", load().qlinear_awq_w4a16(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale),
+                                                          _ptr(weight_zero), group, _ptr(y), _stream(stream)))
     return y
 
 

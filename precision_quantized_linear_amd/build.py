@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqpl.so")
-SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "qpl_api.hip"]
+SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "w4a16_kernels.hip", "qpl_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

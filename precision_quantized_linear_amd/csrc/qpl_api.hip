@@ -302,6 +302,35 @@ QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int
       qpl::launch_gemm_nvfp4(xe, we, gscale, M, K, N, lr, y, st)));
 }
 
+QPL_EXPORT qpl_status quant_weight_awq(const uint16_t* w, int64_t N, int64_t K, int64_t group, uint8_t* w_q,
+                                       uint16_t* w_scale, uint8_t* w_zero, void* stream) {
+  if (!w || !w_q || !w_scale || !w_zero) return QPL_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(w_zero)) return QPL_ERR_ALIGN;
+  if (group != 32 && group != 64 && group != 128) return QPL_ERR_ARG;
+  qpl_status s = check_dims(N, K);
+  if (s != QPL_OK) return s;
+  if (K % group != 0) return QPL_ERR_SHAPE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(Timed(QPL_KERNEL_QUANT_W4G, st)(qpl::launch_quant_w4g(w, N, K, (int)group, w_q, w_scale, w_zero, st)));
+}
+
+QPL_EXPORT qpl_status qlinear_awq_w4a16(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                        const uint16_t* weight_scale, const uint8_t* weight_zero, int64_t group,
+                                        uint16_t* y, void* stream) {
+  if (!x || !weight || !weight_scale || !weight_zero || !y) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(weight_zero) || !aligned16(y))
+    return QPL_ERR_ALIGN;
+  if (group != 32 && group != 64 && group != 128) return QPL_ERR_ARG;
+  qpl_status s = check_gemm_dims(M, K, N);
+  if (s != QPL_OK) return s;
+  if (K % group != 0) return QPL_ERR_SHAPE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(Timed(QPL_KERNEL_GEMV_W4A16, st)(
+      qpl::launch_gemv_w4a16(x, M, K, N, weight, weight_scale, weight_zero, (int)group, y, st)));
+}
+
 QPL_EXPORT qpl_status dequant_weight(qpl_scheme scheme, const uint8_t* weight, const void* weight_scale,
                                      float weight_scale_2, int64_t N, int64_t K, uint16_t* w_bf16, void* stream) {
   if (scheme != QPL_FP8R && scheme != QPL_NVFP4) return QPL_ERR_ARG;

@@ -34,6 +34,12 @@ hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, fl
 hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
                                              const uint16_t* l1t, int64_t kl, float tdiv, uint16_t* xe, uint16_t* t,
                                              hipStream_t stream);
+// Weight-only 4-bit linear (group-wise codes, bf16 scales, byte zero points):
+// the quantizer (one lane per group) and the GEMV y = x W_hat^T.
+hipError_t launch_quant_w4g(const uint16_t* w, int64_t N, int64_t K, int group, uint8_t* wq, uint16_t* ws,
+                            uint8_t* wz, hipStream_t stream);
+hipError_t launch_gemv_w4a16(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* wq,
+                             const uint16_t* ws, const uint8_t* wz, int group, uint16_t* y, hipStream_t stream);
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
                                hipStream_t stream);

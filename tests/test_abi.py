@@ -90,6 +90,16 @@ def test_qlinear_validation(lib):
     assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, A, B, 200, D, A, ws, None) == SHAPE
     assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, MIS, B, 4, D, A, ws, None) == ALIGN
     assert lib.qlinear_nvfp4(*args, 1.0, 1.0, MIS, None, None, 0, D, A, ws, None) == ALIGN  # smoothing factors
+    # weight-only 4-bit: group size, K % group, pointers, alignment
+    assert lib.quant_weight_awq(A, 4, 64, 48, B, C, D, None) == ARG
+    assert lib.quant_weight_awq(A, 4, 96, 64, B, C, D, None) == SHAPE
+    assert lib.quant_weight_awq(A, 4, 64, 64, B, None, D, None) == NULL
+    assert lib.quant_weight_awq(A, 4, 64, 64, B, MIS, D, None) == ALIGN
+    assert lib.qlinear_awq_w4a16(A, 1, 64, 8, B, C, D, 16, A, None) == ARG
+    assert lib.qlinear_awq_w4a16(A, 1, 160, 8, B, C, D, 64, A, None) == SHAPE
+    assert lib.qlinear_awq_w4a16(A, 0, 64, 8, B, C, D, 64, A, None) == SHAPE
+    assert lib.qlinear_awq_w4a16(A, 1, 64, 8, B, C, None, 64, A, None) == NULL
+    assert lib.qlinear_awq_w4a16(A, 1, 64, 8, B, C, MIS, 64, A, None) == ALIGN
     assert lib.dequant_weight(5, A, B, 1.0, 4, 32, C, None) == ARG
     assert lib.dequant_weight(1, A, B, -1.0, 4, 32, C, None) == ARG
     assert lib.dequant_weight(0, A, None, 1.0, 4, 32, C, None) == NULL
