@@ -21,8 +21,8 @@ timed region (the library's event timing, limited to that kernel).  `parts` and
 `kernels` come from a second pass of the same steps with every launch timed.  The
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
 (rank 0, one GPU only).  `extras` times what lies beyond the step: the svdq linear
-with SVDQuant smoothing factors, and the weight-only 4-bit (awq_w4a16) GEMV at the
-FLUX modulation shapes.
+with SVDQuant smoothing factors, the INT4 variant of svdq_w4a4 at the DiT shapes,
+and the weight-only 4-bit (awq_w4a16) GEMV at the FLUX modulation shapes.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -236,6 +236,46 @@ def main():
                               "quant_nvfp4_lowrank_smooth_gbs": round(qlr_bytes / (ts / ns * 1e-3) / 1e9, 1)}}
     nl, tl = kern["quant_nvfp4_lowrank"]
     extras["quant_nvfp4_lowrank_gbs"] = round((qlr_bytes - 4.0 * e["K"]) / (tl / nl * 1e-3) / 1e9, 1)
+
+    # ---------------------------------------------------------------- beyond the step: INT4 W4A4
+    # The INT4 variant of svdq_w4a4 at the DiT shapes: weights quantized by the
+    # library's quantizer (one rule for weights and activations), timed per linear
+    # with HIP events and per kernel with the library's events.
+    for key, name, smooth in (("int4_dit", "nvfp4_dit", False), ("svdq_int4", "svdq_w4a4", False),
+                              ("svdq_int4_smooth", "svdq_w4a4", True)):
+        d = make(name)
+        xa = bf16(d["x"])
+        wa = bf16(d["w"])
+        wq4, ws4 = qpl.quant_act_int4(wa)
+        del wa
+        R = d.get("R", 0)
+        kw = dict(lora_down=bf16(d["l1"]), lora_up=bf16(d["l2"])) if R else {}
+        if smooth:
+            kw["smooth"] = torch.from_numpy(smooth_factors(name)).to(dev)
+        ya = torch.empty((d["M"], d["N"]), dtype=torch.bfloat16, device=dev)
+        wsb = torch.empty((qpl.qlinear_workspace_bytes(qpl.QPL_INT4, d["M"], d["K"], d["N"], R),), dtype=torch.uint8,
+                          device=dev)
+        for _ in range(args.warmup):
+            qpl.qlinear_int4(xa, wq4, ws4, y=ya, workspace=wsb, **kw)
+        torch.cuda.synchronize()
+        qpl.timing_collect()
+        qpl.timing_select(["gemm_int4"])
+        evs = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            qpl.qlinear_int4(xa, wq4, ws4, y=ya, workspace=wsb, **kw)
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        qpl.timing_select([])
+        ng_, tg_ = qpl.timing_collect()["gemm_int4"]
+        ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        fl = 2.0 * d["M"] * d["N"] * d["K"]
+        extras[key] = {"shape": [d["M"], d["K"], d["N"]] + ([R] if R else []), "ms": round(ms, 4),
+                       "tflops": round(fl / (ms * 1e-3) / 1e12, 1), "gemm_int4_us": round(1e3 * tg_ / ng_, 2),
+                       "gemm_int4_tflops": round(fl / (tg_ / ng_ * 1e-3) / 1e12, 1)}
+        del xa, wq4, ws4, ya, wsb
 
     # ---------------------------------------------------------------- beyond the step: weight-only 4-bit
     # FLUX modulation projections (awq_w4a16) at one and two conditioning rows,

@@ -48,7 +48,7 @@ typedef enum {
   QPL_ERR_LAUNCH = 7     /* the HIP runtime rejected a kernel launch */
 } qpl_status;
 
-typedef enum { QPL_FP8R = 0, QPL_NVFP4 = 1 } qpl_scheme;
+typedef enum { QPL_FP8R = 0, QPL_NVFP4 = 1, QPL_INT4 = 2 } qpl_scheme;
 
 /*
  * Row-wise FP8 quantization (guide "BFL (fp8r / nvfp4)", intro bullet on fp8r:
@@ -124,6 +124,35 @@ qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                          float weight_scale_2, float input_scale, const float* smooth,
                          const uint16_t* lora_down, const uint16_t* lora_up, int64_t R,
                          uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * INT4 variant of the SVDQuant W4A4 linear (Nunchaku post, "Introducing Nunchaku
+ * Lite": svdq_w4a4 comes in INT4 and NVFP4 variants; the post gives no INT4
+ * format, this library's):
+ *   codes          signed 4-bit two's complement, channel 2j in the low nibble of
+ *                  byte j: uint8 [rows, K/2]
+ *   scales         float [rows, K/64], one per group of 64 channels
+ *   rule           s = amax / 7 (fp32), q = clamp(rint(x / s), -8, 7) with a
+ *                  correctly rounded division, ties to even; an all-zero group
+ *                  has s = 0 and codes 0.  The same rule quantizes a weight.
+ * quant_act_int4: x bf16 [M,K] (K % 64 == 0) -> x_q, x_scale; with smooth
+ *   (float [K] or NULL, as in quant_act_nvfp4) the quantized activation is
+ *   bf16_rne(x / smooth).
+ * qlinear_int4:
+ *   y = bf16_rne( sum_g sx[m,g] sw[n,g] sum_{k in g} qx qw  +  (x L1) L2 )
+ *   with qx, sx from quant_act_int4(x, smooth), fp32 accumulation, and the
+ *   low-rank term (x replaced by the smoothed x when smooth is given) added
+ *   before the single rounding.  weight uint8 [N,K/2], weight_scale float
+ *   [N,K/64], lora_down / lora_up / R as in qlinear_nvfp4; ws of at least
+ *   qlinear_workspace_bytes(QPL_INT4, M, K, N, R).
+ * All pointers 16-byte aligned.
+ */
+qpl_status quant_act_int4(const uint16_t* x, int64_t M, int64_t K, const float* smooth,
+                          uint8_t* x_q, float* x_scale, void* stream);
+qpl_status qlinear_int4(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                        const uint8_t* weight, const float* weight_scale, const float* smooth,
+                        const uint16_t* lora_down, const uint16_t* lora_up, int64_t R,
+                        uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Weight-only 4-bit linear with bf16 activations (Nunchaku post, "Introducing
@@ -208,7 +237,11 @@ typedef enum {
   QPL_KERNEL_QUANT_NVFP4_LOWRANK = 10, /* nvfp4 quantize fused with x L1 (qlinear_nvfp4, R > 0) */
   QPL_KERNEL_QUANT_W4G = 11,        /* quant_weight_awq */
   QPL_KERNEL_GEMV_W4A16 = 12,       /* qlinear_awq_w4a16 */
-  QPL_KERNEL_COUNT = 13
+  QPL_KERNEL_QUANT_INT4 = 13,       /* quant_act_int4, and the INT4 quantize inside qlinear_int4 (R = 0) */
+  QPL_KERNEL_INT4_EXPAND = 14,      /* INT4 weight codes -> E4M3 bytes inside qlinear_int4 */
+  QPL_KERNEL_GEMM_INT4 = 15,
+  QPL_KERNEL_QUANT_INT4_LOWRANK = 16, /* INT4 quantize fused with x L1 (qlinear_int4, R > 0) */
+  QPL_KERNEL_COUNT = 17
 } qpl_kernel;
 
 void qpl_timing_enable(int on);

@@ -14,14 +14,16 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqpl.so")
 
 QPL_FP8R = 0
 QPL_NVFP4 = 1
+QPL_INT4 = 2
 
 EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp4", "dequant_weight",
-           "quant_weight_awq", "qlinear_awq_w4a16", "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
+           "quant_weight_awq", "qlinear_awq_w4a16", "quant_act_int4", "qlinear_int4", "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
            "qpl_timing_enable", "qpl_timing_select", "qpl_timing_collect")
 
 # qpl_kernel order of include/qpl.h
 KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_bf16", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
-           "lowrank_prep", "dequant", "amax", "weight_bf16", "quant_nvfp4_lowrank", "quant_w4g", "gemv_w4a16")
+           "lowrank_prep", "dequant", "amax", "weight_bf16", "quant_nvfp4_lowrank", "quant_w4g", "gemv_w4a16",
+           "quant_int4", "int4_expand", "gemm_int4", "quant_int4_lowrank")
 
 _lib = None
 
@@ -49,6 +51,8 @@ def load():
         "dequant_weight": [ctypes.c_int, P, P, F, I64, I64, P, P],
         "quant_weight_awq": [P, I64, I64, I64, P, P, P, P],
         "qlinear_awq_w4a16": [P, I64, I64, I64, P, P, P, I64, P, P],
+        "quant_act_int4": [P, I64, I64, P, P, P, P],
+        "qlinear_int4": [P, I64, I64, I64, P, P, P, P, P, I64, P, P, SZ, P],
         "qpl_amax_bf16": [P, I64, P, P],
     }
     for name, args in sig.items():
@@ -168,6 +172,42 @@ def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_dow
                                                  float(weight_scale_2), float(input_scale), _ptr(smooth),
                                                  _ptr(lora_down),
                                                  _ptr(lora_up), R, _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def quant_act_int4(x, smooth=None, x_q=None, x_scale=None, stream=None):
+    """bf16 [M,K] (K % 64 == 0) -> (packed INT4 codes uint8 [M,K/2], fp32 group scales [M,K/64])."""
+    M, K = x.shape
+    _expect(x, torch.bfloat16, (M, K), "x")
+    if smooth is not None:
+        _expect(smooth, torch.float32, (K,), "smooth")
+    x_q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device) if x_q is None else x_q
+    x_scale = torch.empty((M, K // 64), dtype=torch.float32, device=x.device) if x_scale is None else x_scale
+    _check("quant_act_int4", load().quant_act_int4(_ptr(x), M, K, _ptr(smooth), _ptr(x_q), _ptr(x_scale),
+                                                    _stream(stream)))
+    return x_q, x_scale
+
+
+def qlinear_int4(x, weight, weight_scale, lora_down=None, lora_up=None, y=None, workspace=None, stream=None,
+                 smooth=None):
+    """y[M,N] bf16 = INT4 W4A4 linear (+ (x L1) L2), the INT4 variant of svdq_w4a4."""
+    M, K = x.shape
+    N = weight.shape[0]
+    _expect(x, torch.bfloat16, (M, K), "x")
+    _expect(weight, torch.uint8, (N, K // 2), "weight")
+    _expect(weight_scale, torch.float32, (N, K // 64), "weight_scale")
+    if smooth is not None:
+        _expect(smooth, torch.float32, (K,), "smooth")
+    R = 0
+    if lora_down is not None:
+        R = lora_down.shape[1]
+        _expect(lora_down, torch.bfloat16, (K, R), "lora_down")
+        _expect(lora_up, torch.bfloat16, (R, N), "lora_up")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    ws, nbytes = _workspace(QPL_INT4, M, K, N, R, workspace, x.device)
+    _check("qlinear_int4", load().qlinear_int4(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale), _ptr(smooth),
+                                               _ptr(lora_down), _ptr(lora_up), R, _ptr(y), _ptr(ws), nbytes,
+                                               _stream(stream)))
     return y
 
 

@@ -47,7 +47,6 @@ constexpr int SROW = 64;            // bytes per slab row
 constexpr int SLAB = 256 * SROW;    // 16 KB per operand per stage
 constexpr int STAGE = 2 * SLAB;     // x slab then W slab
 constexpr int NST = 4;              // stages in the ring
-constexpr int DMA_PER_STAGE = 8;    // per wavefront: 4 x-slab and 4 W-slab instructions of 1 KB
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int soff(int r, int c) { return r * SROW + ((c ^ swz(r)) << 4); }
@@ -108,13 +107,15 @@ struct Bf16Mma {
 // activation slabs and 8 weight slabs in that XCD's L2.
 constexpr int GROUP_M = 4;
 
-__device__ __forceinline__ void tile_coords(int s, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
+// tm: rows of x per tile (256, or 128 for the INT4 GEMM); tiles are 256 columns wide.
+__device__ __forceinline__ void tile_coords(int s, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0,
+                                            int tm = 256) {
   const int per_group = GROUP_M * tiles_n;
   const int g = s / per_group;
   const int first_m = g * GROUP_M;
   const int gm = min(tiles_m - first_m, GROUP_M);
   const int r = s - g * per_group;
-  m0 = (int64_t)(first_m + r % gm) * 256;
+  m0 = (int64_t)(first_m + r % gm) * tm;
   n0 = (int64_t)(r / gm) * 256;
 }
 
@@ -158,28 +159,30 @@ constexpr int SCALE_BUF = 2048;      // per tile parity: s_x of the tile's 256 r
 // exchange halves (V_PERMLANE32_SWAP) so that each lane holds eight consecutive
 // columns of one row and stores them as one 16-byte segment.  NJ: 32-row blocks
 // per wavefront (4 for a 256-row tile, 2 for a 128-row half tile, whose rows are
-// m0 + 64 wm + 32 j + l % 32).  Returns the number of store instructions left in
-// flight: 8 NJ on the interior path, 0 on the edge path (which checks every
-// element and drains its stores).
-template <int NJ, class RowScale, class ColScale>
+// m0 + 64 wm + 32 j + l % 32); NI: 32-column blocks per wavefront (4: columns
+// n0 + 128 wn + ..., wn in 0..1; 2: n0 + 64 wn + ..., wn in 0..3).  Returns the
+// number of store instructions left in flight: 2 NJ NI on the interior path, 0 on
+// the edge path (which checks every element and drains its stores).
+template <int NJ, int NI = 4, class RowScale, class ColScale>
 __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
                                           int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
                                           const ColScale& cs) {
-  const bool fast = m0 + 64 * NJ <= M && n0 + 256 <= N && (N & 7) == 0;
+  // interior: the wavefront's rows and columns all inside the matrix
+  const bool fast = m0 + (wm + 1) * 32 * NJ <= M && n0 + (wn + 1) * 32 * NI <= N && (N & 7) == 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int mr = wm * 32 * NJ + j * 32 + (lane & 31);
     const float fr = rs(mr);
     const int64_t m = m0 + mr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
         uint32_t w[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int g = 2 * gp + h;
-          const f32x4 fc = cs(wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4);
+          const f32x4 fc = cs(wn * 32 * NI + i * 32 + g * 8 + (lane >> 5) * 4);
           const f32x16& a = acc[i][j];
           w[h][0] = pack_bf16((a[g * 4 + 0] * fr) * fc[0], (a[g * 4 + 1] * fr) * fc[1]);
           w[h][1] = pack_bf16((a[g * 4 + 2] * fr) * fc[2], (a[g * 4 + 3] * fr) * fc[3]);
@@ -187,7 +190,7 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
         const auto r0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
         const auto r1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
         const u32x4 v = u32x4{r0[0], r1[0], r0[1], r1[1]};
-        const int64_t n = n0 + wn * 128 + i * 32 + (2 * gp + (lane >> 5)) * 8;
+        const int64_t n = n0 + wn * 32 * NI + i * 32 + (2 * gp + (lane >> 5)) * 8;
         if (fast) {
           *reinterpret_cast<u32x4*>(y + m * N + n) = v;
         } else if (m < M) {
@@ -202,7 +205,7 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
         }
       }
   }
-  if (fast) return 8 * NJ;
+  if (fast) return 2 * NJ * NI;
   QPL_WAIT_VMCNT(0);
   return 0;
 }
@@ -453,6 +456,240 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   gemm_persistent<Bf16Mma, false, LOWRANK>(p, nullptr, nullptr, gscale, Y);
 }
 
+// ---------------------------------------------------------------------------
+// INT4 GEMM (the INT4 variant of svdq_w4a4).  The operands are the code values
+// -8..7 as E4M3 bytes [rows, K] with fp32 group scales stored group-major, s_x
+// [K/64, M] and s_w [K/64, N] (a slab's scales of consecutive rows are then
+// contiguous); a 64-byte slab row is exactly one group.  Per slab and 32 x 32 tile,
+// one V_MFMA_SCALE_F32_32X32X64_F8F6F4 from zero gives the group's dot products:
+// the products are integers of magnitude <= 64 and the sums stay below 2^12, and
+// the MFMA returns them exactly (checked against integer sums on 4M outputs with
+// random and extreme codes).  They are folded into fp32 accumulators as
+// acc += (P s_w[n]) s_x[m].
+// The optional low-rank pass (bf16 [T_hi | T_lo] and [L2^T | L2^T], as in the
+// nvfp4 GEMM) adds T L2 to the same accumulators on the bf16 MFMA.
+//
+// The fold runs on the VALU, so the accumulators live in VGPRs and the MFMA results
+// must too.  A workgroup has eight wavefronts (two per SIMD, so that one wave's
+// MFMAs overlap the other's fold) and owns TM rows of x by 256 rows of W; a
+// wavefront owns 32 NJ rows of x by 32 NI rows of W (2 x 4 waves).  A lane's s_x
+// is one value per x tile, while its s_w are 16 values per W tile (its 16 output
+// columns): the waves are made tall in x (NJ = TM / 64) and narrow in W (NI = 2)
+// so that the s_w reads from LDS stay few.  Without the low-rank pass TM = 256
+// (128 accumulators per wave: the slab traffic per MAC of the other GEMMs); the
+// low-rank pass needs more registers, so with it TM = 128.  Persistent, with the tile
+// order of the other GEMMs.  The ring has NST4 = 4 stages; slab g + 3 is issued
+// during slab g's step into the stage of slab g - 1, so the current slab's
+// fragments and scales stay in LDS while it is multiplied and folded.  A slab's
+// loads per wave: TM / 128 loads of 1 KB of x, two of W, and one dword load of 64
+// scales (waves 0-3: s_w; then s_x; any other wave loads nothing into a spare area).
+// ---------------------------------------------------------------------------
+template <bool LOWRANK>
+struct I4Cfg {
+  static constexpr int TM = LOWRANK ? 128 : 256;  // rows of x per tile
+  static constexpr int WM = 2, WN = 4;            // wavefronts along x rows, W rows
+  static constexpr int NJ = TM / 64;              // 32-row x tiles per wavefront
+  static constexpr int NI = 2;                    // 32-row W tiles per wavefront
+  static constexpr int XI = TM / 128;             // x loads per wave per slab
+  static constexpr int D = XI + 3;                // loads per wave per slab
+  static constexpr int XB = TM * SROW;            // x slab bytes
+  static constexpr int SC = XB + 256 * SROW;      // s_w (256 floats), then s_x (TM floats)
+  static constexpr int STAGE = SC + 1024 + 4 * TM;
+  static constexpr int NSTORE = 2 * NJ * NI;      // store_tile<NJ, NI> fast path
+};
+constexpr int NST4 = 4;
+
+template <bool LOWRANK>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_int4(
+    GemmArgs p, const float* __restrict__ sxp, const float* __restrict__ swp, uint16_t* __restrict__ Y) {
+  using C = I4Cfg<LOWRANK>;
+  constexpr int TM = C::TM, WN = C::WN, NJ = C::NJ, NI = C::NI, XI = C::XI, D = C::D, XB = C::XB, SC = C::SC;
+  constexpr int STAGE = C::STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST4 * STAGE + 256];  // + a spare area for dummy loads
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wv / WN, wn = wv % WN;
+  const int b = blockIdx.x;
+  const uint32_t lbase = lds_address(lds);
+  const uint32_t spare = lbase + NST4 * STAGE;
+
+  int nt = 0;
+  while (tile_seq(nt, b, p.nwg) < p.ntiles) ++nt;
+  const int nk1 = p.kbytes1 / SROW;  // groups of 64 channels (K % 64 == 0)
+  const int nk2 = LOWRANK ? (p.kbytes2 + SROW - 1) / SROW : 0;
+  const int nk = nk1 + nk2;
+
+  // lane geometry of the slab loads (16-byte chunk l % 4 of slab row + l / 4,
+  // swizzled): x instruction q fills rows 16 (XI wv + q) .., W instruction q rows
+  // 16 (2 wv + q) ..
+  int xrow[XI], xcb[XI], wrow[2], wcb[2];
+#pragma unroll
+  for (int q = 0; q < XI; ++q) {
+    xrow[q] = 16 * (XI * wv + q) + (lane >> 2);
+    xcb[q] = ((lane & 3) ^ swz(xrow[q])) * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    wrow[q] = 16 * (2 * wv + q) + (lane >> 2);
+    wcb[q] = ((lane & 3) ^ swz(wrow[q])) * 16;
+  }
+  // this wave's scale load: 64 of s_w (waves 0-3), 64 of s_x (waves 4 .. 4 + TM / 64 - 1)
+  const bool sc_w = wv < 4, sc_real = wv < 4 + TM / 64;
+  const int sc_first = 64 * (sc_w ? wv : wv - 4);
+  const uint32_t sc_dst = SC + (sc_w ? 0 : 1024) + 256 * (sc_w ? wv : wv - 4);
+
+  struct SlabSrc {
+    u32x4 dx, dw, dsc;
+    int pitch, kb, koff, stage;
+    bool scales;
+  };
+  int s_ti = 0, s_ks = 0, s_stage = 0;
+  int64_t s_m0 = 0, s_n0 = 0;
+  if (nt > 0) tile_coords(tile_seq(0, b, p.nwg), p.tiles_m, p.tiles_n, s_m0, s_n0, TM);
+  auto next_src = [&]() {
+    SlabSrc r;
+    const bool valid = s_ti < nt;
+    const bool pass2 = LOWRANK && s_ks >= nk1;
+    r.stage = s_stage;
+    r.scales = valid && !pass2 && sc_real;
+    r.pitch = pass2 ? p.pitch2 : p.pitch1;
+    r.kb = valid ? (pass2 ? p.kbytes2 : p.kbytes1) : 0;
+    r.koff = (pass2 ? s_ks - nk1 : s_ks) * SROW;
+    const int64_t lm = p.M - s_m0, ln = p.N - s_n0;
+    const int64_t rm = lm < TM ? lm : TM, rn = ln < 256 ? ln : 256;
+    r.dx = make_desc((pass2 ? p.a2 : p.a) + s_m0 * r.pitch, rm * r.pitch);
+    r.dw = make_desc((pass2 ? p.w2 : p.w) + s_n0 * r.pitch, rn * r.pitch);
+    r.dsc = sc_w ? make_desc(swp + (int64_t)s_ks * p.N + s_n0, rn * 4)
+                 : make_desc(sxp + (int64_t)s_ks * p.M + s_m0, rm * 4);
+    s_stage = s_stage == NST4 - 1 ? 0 : s_stage + 1;
+    if (++s_ks == nk) {
+      s_ks = 0;
+      ++s_ti;
+      if (s_ti < nt) tile_coords(tile_seq(s_ti, b, p.nwg), p.tiles_m, p.tiles_n, s_m0, s_n0, TM);
+    }
+    return r;
+  };
+  auto issue = [&](const SlabSrc& s, int d) {
+    const uint32_t st = lbase + s.stage * STAGE;
+    if (d < XI) {
+      const uint32_t vo = s.koff + xcb[d] < s.kb ? (uint32_t)(xrow[d] * s.pitch + xcb[d]) : kOutOfRange;
+      dma16(st + (XI * wv + d) * 1024, vo, s.dx, s.koff);
+    } else if (d < XI + 2) {
+      const int q = d - XI;
+      const uint32_t vo = s.koff + wcb[q] < s.kb ? (uint32_t)(wrow[q] * s.pitch + wcb[q]) : kOutOfRange;
+      dma16(st + XB + (2 * wv + q) * 1024, vo, s.dw, s.koff);
+    } else {
+      const uint32_t vo = s.scales ? (uint32_t)((sc_first + lane) * 4) : kOutOfRange;
+      dma4(s.scales ? st + sc_dst : spare, vo, s.dsc, 0);
+    }
+  };
+
+  // prologue: slabs 0 .. NST4 - 2
+#pragma unroll
+  for (int s0 = 0; s0 < NST4 - 1; ++s0) {
+    const SlabSrc src = next_src();
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(src, d);
+  }
+  // fragments: 32 bytes per lane, chunks 2 (lane / 32) and + 1 of the row, read as
+  // two 16-byte halves u (which are also the two bf16 MFMA steps of a low-rank
+  // slab) from the current slab's stage just before they are used; the other
+  // wavefront on the SIMD covers the LDS latency
+  auto frag = [&](const uint8_t* stage, bool wslab, int row, int u) {
+    return *reinterpret_cast<const i32x4*>(stage + (wslab ? XB : 0) + soff(row, 2 * (lane >> 5) + u));
+  };
+  int cur = 0;                     // stage of the slab being multiplied
+  int st1 = 0, st2 = 0, st3 = 0;  // stores left in flight after iterations g - 1, g - 2, g - 3
+  auto step = [&](Acc& acc, auto pass2) {
+    constexpr bool P2 = decltype(pass2)::value;
+    QPL_WAIT_LGKM0();
+    // slab g must have landed: issued after it (in step g - 3, or the prologue) are
+    // slabs g + 1 and g + 2 and the stores of the epilogues after iterations g - 3
+    // .. g - 1 (at most one epilogue: a tile is at least NST4 slabs)
+    const int extra = st1 + st2 + st3;
+    if (extra == 0) {
+      QPL_WAIT_VMCNT((NST4 - 2) * D);
+    } else if (extra == C::NSTORE) {
+      QPL_WAIT_VMCNT((NST4 - 2) * D + C::NSTORE);
+    } else {
+      QPL_WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_barrier();  // slab g is in LDS for every wave; slab g - 1's stage is free
+    const SlabSrc src = next_src();  // slab g + NST4 - 1, into slab g - 1's stage
+    const uint8_t* cs = lds + cur * STAGE;
+    cur = cur == NST4 - 1 ? 0 : cur + 1;
+    i32x4 fx[2][NJ];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) fx[u][j] = frag(cs, false, wm * 32 * NJ + j * 32 + (lane & 31), u);
+    float sx[NJ];
+    if constexpr (!P2) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        sx[j] = *reinterpret_cast<const float*>(cs + SC + 1024 + 4 * (wm * 32 * NJ + j * 32 + (lane & 31)));
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int wr = wn * 32 * NI + i * 32;  // first W row of the tile row
+      i32x4 fw[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) fw[u] = frag(cs, true, wr + (lane & 31), u);
+      // s_w of this lane's 16 output columns wr + 8 q + 4 (lane / 32) + 0..3
+      f32x4 sw[4];
+      if constexpr (!P2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sw[q] = *reinterpret_cast<const f32x4*>(cs + SC + 4 * (wr + 8 * q + 4 * (lane >> 5)));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if constexpr (P2) {
+          // bf16 low-rank slab in two 32x32x16 steps: step u takes chunk 2 (lane / 32) + u
+          // of both operands' rows, so each step sums the same (permuted) k positions of
+          // W and x, and the two steps cover the slab's four chunks once
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fw[u]),
+                                                                __builtin_bit_cast(bf16x8, fx[u][j]), acc[i][j], 0, 0, 0);
+        } else {
+          const i32x8 a = __builtin_shufflevector(fw[0], fw[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const i32x8 bx = __builtin_shufflevector(fx[0][j], fx[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+          const f32x16 pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bx, f32x16{}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[i][j][r] = __builtin_fmaf(pr[r] * sw[r >> 2][r & 3], sx[j], acc[i][j][r]);
+        }
+        // the slab's D loads spread over its NI NJ tiles
+        const int t = NJ * i + j;
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+          if (t == (d * NI * NJ) / D) issue(src, d);
+      }
+    }
+    st3 = st2;
+    st2 = st1;
+    st1 = 0;
+  };
+
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  for (int ti = 0; ti < nt; ++ti) {
+    Acc acc;
+    zero_acc(acc);
+    for (int kt = 0; kt < nk1; ++kt) step(acc, No{});
+    if constexpr (LOWRANK) {
+      for (int kt = 0; kt < nk2; ++kt) step(acc, Yes{});
+    }
+    int64_t m0, n0;
+    tile_coords(tile_seq(ti, b, p.nwg), p.tiles_m, p.tiles_n, m0, n0, TM);
+    st1 = store_tile<NJ, NI>(acc, wm, wn, lane, m0, n0, p.M, p.N, Y, [](int) { return 1.0f; },
+                             [](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
+    if (st1 == 0) st2 = st3 = 0;
+  }
+  QPL_WAIT_VMCNT(0);
+  QPL_WAIT_LGKM0();
+}
+
 // l1t[r][k] = L1[k][r] (zero for r >= R); l2t[n][c] = L2[c mod rpad][n] (zero past R).
 __global__ __launch_bounds__(256) void k_lowrank_transpose(const uint16_t* __restrict__ l1,
                                                            const uint16_t* __restrict__ l2, int64_t K, int64_t N,
@@ -530,6 +767,39 @@ hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscal
     hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, block, 0, stream, p, gscale, y);
   else
     hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, block, 0, stream, p, gscale, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_int4(const uint8_t* x8, const float* xs, const uint8_t* w8, const float* ws, int64_t M,
+                            int64_t K, int64_t N, LowRank lr, uint16_t* y, hipStream_t stream) {
+  GemmArgs p{};
+  p.a = x8;
+  p.w = w8;
+  p.M = M;
+  p.N = N;
+  p.pitch1 = (int)K;
+  p.kbytes1 = (int)K;
+  int nk = (int)(K / 64);
+  if (lr.kl > 0) {
+    p.a2 = reinterpret_cast<const uint8_t*>(lr.t);
+    p.w2 = reinterpret_cast<const uint8_t*>(lr.l2t);
+    p.pitch2 = (int)(2 * lr.kl);
+    p.kbytes2 = (int)(2 * lr.kl);
+    nk += (p.kbytes2 + SROW - 1) / SROW;
+  }
+  const int tm = lr.kl > 0 ? I4Cfg<true>::TM : I4Cfg<false>::TM;
+  p.tiles_m = (int)((M + tm - 1) / tm);
+  p.tiles_n = (int)((N + 255) / 256);
+  p.ntiles = p.tiles_m * p.tiles_n;
+  // persistent while every tile is at least NST4 slabs (one epilogue per wait window)
+  p.nwg = nk >= NST4 ? (p.ntiles < 256 ? p.ntiles : 256) : p.ntiles;
+  p.nfull = p.ntiles;
+  p.ntail = 0;
+  const dim3 grid((unsigned)p.nwg), block(512);
+  if (lr.kl > 0)
+    hipLaunchKernelGGL(k_gemm_int4<true>, grid, block, 0, stream, p, xs, ws, y);
+  else
+    hipLaunchKernelGGL(k_gemm_int4<false>, grid, block, 0, stream, p, xs, ws, y);
   return hipGetLastError();
 }
 

@@ -61,32 +61,39 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 int64_t rank_pad(int64_t R) { return (R + 31) / 32 * 32; }
 
 // Workspace layout.  fp8r: [xq: M*K bytes][xs: 4*M bytes].  nvfp4: [xe: 2*M*K]
-// [we: 2*N*K] (bf16 expansions of the quantized activations and weights) then,
-// when R > 0, [l1t: 2*rpad*K][t: 2*M*KL][l2t: 2*N*KL] with rpad = 32*ceil(R/32)
-// and KL = 2*rpad.  Each part is rounded up to 256 bytes.
+// [we: 2*N*K] (bf16 expansions of the quantized activations and weights).  INT4:
+// [xq: M*K][w8: N*K] (code values as E4M3 bytes) and, as parts 5 and 6, the
+// group-major scales [xs: 4*M*K/64][ws: 4*N*K/64].
+// nvfp4 and INT4 then, when R > 0, [l1t: 2*rpad*K][t: 2*M*KL][l2t: 2*N*KL] with
+// rpad = 32*ceil(R/32) and KL = 2*rpad.  Each part is rounded up to 256 bytes.
 struct Layout {
-  size_t off[5] = {0, 0, 0, 0, 0};
+  size_t off[7] = {0, 0, 0, 0, 0, 0, 0};
   size_t total = 0;
 };
 
 Layout layout(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R) {
   Layout L;
-  size_t parts[5] = {0, 0, 0, 0, 0};
+  size_t parts[7] = {0, 0, 0, 0, 0, 0, 0};
   if (scheme == QPL_FP8R) {
     parts[0] = size_t(M) * size_t(K);
     parts[1] = size_t(4) * size_t(M);
   } else {
-    parts[0] = size_t(2) * size_t(M) * size_t(K);
-    parts[1] = size_t(2) * size_t(N) * size_t(K);
+    const size_t eb = scheme == QPL_INT4 ? 1 : 2;  // bytes per expanded element
+    parts[0] = eb * size_t(M) * size_t(K);
+    parts[1] = eb * size_t(N) * size_t(K);
     if (R > 0) {
       const int64_t rp = rank_pad(R), kl = 2 * rp;
       parts[2] = size_t(2) * size_t(rp) * size_t(K);
       parts[3] = size_t(2) * size_t(M) * size_t(kl);
       parts[4] = size_t(2) * size_t(N) * size_t(kl);
     }
+    if (scheme == QPL_INT4) {
+      parts[5] = size_t(4) * size_t(M) * size_t(K / 64);
+      parts[6] = size_t(4) * size_t(N) * size_t(K / 64);
+    }
   }
   size_t o = 0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < 7; ++i) {
     L.off[i] = o;
     o += round256(parts[i]);
   }
@@ -199,8 +206,9 @@ QPL_EXPORT const char* qpl_status_str(qpl_status status) {
 QPL_EXPORT float qpl_nvfp4_global_scale(float amax) { return amax / 2688.0f; }
 
 QPL_EXPORT size_t qlinear_workspace_bytes(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R) {
-  if (scheme != QPL_FP8R && scheme != QPL_NVFP4) return 0;
+  if (scheme != QPL_FP8R && scheme != QPL_NVFP4 && scheme != QPL_INT4) return 0;
   if (check_gemm_dims(M, K, N) != QPL_OK || R < 0 || R > kMaxRank) return 0;
+  if (scheme == QPL_INT4 && K % 64 != 0) return 0;
   if (scheme == QPL_FP8R && R != 0) return 0;
   return layout(scheme, M, K, N, R).total;
 }
@@ -329,6 +337,67 @@ QPL_EXPORT qpl_status qlinear_awq_w4a16(const uint16_t* x, int64_t M, int64_t K,
   hipStream_t st = static_cast<hipStream_t>(stream);
   return launched(Timed(QPL_KERNEL_GEMV_W4A16, st)(
       qpl::launch_gemv_w4a16(x, M, K, N, weight, weight_scale, weight_zero, (int)group, y, st)));
+}
+
+QPL_EXPORT qpl_status quant_act_int4(const uint16_t* x, int64_t M, int64_t K, const float* smooth, uint8_t* x_q,
+                                     float* x_scale, void* stream) {
+  if (!x || !x_q || !x_scale) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x_q) || !aligned16(x_scale) || !aligned16(smooth)) return QPL_ERR_ALIGN;
+  qpl_status s = check_dims(M, K);
+  if (s != QPL_OK) return s;
+  if (K % 64 != 0) return QPL_ERR_SHAPE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(Timed(QPL_KERNEL_QUANT_INT4, st)(qpl::launch_quant_int4(x, M, K, smooth, false, x_q, x_scale, st)));
+}
+
+QPL_EXPORT qpl_status qlinear_int4(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                   const float* weight_scale, const float* smooth, const uint16_t* lora_down,
+                                   const uint16_t* lora_up, int64_t R, uint16_t* y, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!x || !weight || !weight_scale || !y || !ws) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws) ||
+      !aligned16(smooth))
+    return QPL_ERR_ALIGN;
+  qpl_status s = check_gemm_dims(M, K, N);
+  if (s != QPL_OK) return s;
+  if (K % 64 != 0) return QPL_ERR_SHAPE;
+  if (R < 0 || R > kMaxRank) return QPL_ERR_SHAPE;
+  if (R > 0 && (!lora_down || !lora_up)) return QPL_ERR_NULL;
+  if (R == 0 && (lora_down || lora_up)) return QPL_ERR_ARG;
+  if (R > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return QPL_ERR_ALIGN;
+  const Layout L = layout(QPL_INT4, M, K, N, R);
+  if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* xq = base + L.off[0];
+  uint8_t* w8 = base + L.off[1];
+  float* xs = reinterpret_cast<float*>(base + L.off[5]);
+  float* wst = reinterpret_cast<float*>(base + L.off[6]);
+  qpl::LowRank lr;
+  if (R > 0) {
+    const int64_t kl = 2 * rank_pad(R);
+    uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[2]);
+    uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[3]);
+    uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
+    if ((s = launched(Timed(QPL_KERNEL_LOWRANK_PREP, st)(
+             qpl::launch_lowrank_prep(lora_down, lora_up, K, N, R, kl, l1t, l2t, st)))) != QPL_OK)
+      return s;
+    if ((s = launched(Timed(QPL_KERNEL_QUANT_INT4_LOWRANK, st)(
+             qpl::launch_quant_int4_lowrank(x, M, K, smooth, l1t, kl, xq, xs, t, st)))) != QPL_OK)
+      return s;
+    lr.t = t;
+    lr.l2t = l2t;
+    lr.kl = kl;
+  } else if ((s = launched(Timed(QPL_KERNEL_QUANT_INT4, st)(
+                  qpl::launch_quant_int4(x, M, K, smooth, true, xq, xs, st)))) != QPL_OK) {
+    return s;
+  }
+  if ((s = launched(Timed(QPL_KERNEL_INT4_EXPAND, st)(
+           qpl::launch_expand_int4(weight, weight_scale, N, K, w8, wst, st)))) != QPL_OK)
+    return s;
+  return launched(Timed(QPL_KERNEL_GEMM_INT4, st)(qpl::launch_gemm_int4(xq, xs, w8, wst, M, K, N, lr, y, st)));
 }
 
 QPL_EXPORT qpl_status dequant_weight(qpl_scheme scheme, const uint8_t* weight, const void* weight_scale,

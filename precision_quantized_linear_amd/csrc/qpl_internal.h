@@ -34,6 +34,19 @@ hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, fl
 hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
                                              const uint16_t* l1t, int64_t kl, float tdiv, uint16_t* xe, uint16_t* t,
                                              hipStream_t stream);
+// INT4 (svdq_w4a4 INT4 variant): group-wise quantizer, writing packed codes and
+// scales [M, K/64], or (f8, for the GEMM) the E4M3 bytes of the code values and
+// scales group-major [K/64, M]; and the packed -> E4M3 byte expansion of a weight,
+// which also copies its scales [N, K/64] into group-major wst [K/64, N].
+hipError_t launch_quant_int4(const uint16_t* x, int64_t M, int64_t K, const float* lam, bool f8, uint8_t* xq,
+                             float* xs, hipStream_t stream);
+hipError_t launch_expand_int4(const uint8_t* wq, const float* ws, int64_t N, int64_t K, uint8_t* w8, float* wst,
+                              hipStream_t stream);
+// The INT4 quantizer (E4M3 code bytes, group-major scales) fused with T = x L1,
+// stored as in launch_quant_nvfp4_expand_lowrank with tdiv = 1.
+hipError_t launch_quant_int4_lowrank(const uint16_t* x, int64_t M, int64_t K, const float* lam, const uint16_t* l1t,
+                                     int64_t kl, uint8_t* xq, float* xs, uint16_t* t, hipStream_t stream);
+
 // Weight-only 4-bit linear (group-wise codes, bf16 scales, byte zero points):
 // the quantizer (one lane per group) and the GEMV y = x W_hat^T.
 hipError_t launch_quant_w4g(const uint16_t* w, int64_t N, int64_t K, int group, uint8_t* wq, uint16_t* ws,
@@ -64,6 +77,11 @@ hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscal
 
 // Factor layouts for the low-rank branch: l1t [kl / 2, K] = L1^T and l2t [N, kl] =
 // [L2^T | L2^T], both zero past R.
+// INT4 GEMM: x8 [M, K] and w8 [N, K] code values as E4M3 bytes, xs [K/64, M] and
+// ws [K/64, N] fp32 group scales (group-major), K % 64 == 0; optional low-rank
+// pass (tdiv 1).
+hipError_t launch_gemm_int4(const uint8_t* x8, const float* xs, const uint8_t* w8, const float* ws, int64_t M,
+                            int64_t K, int64_t N, LowRank lr, uint16_t* y, hipStream_t stream);
 hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,
                                uint16_t* l1t, uint16_t* l2t, hipStream_t stream);
 

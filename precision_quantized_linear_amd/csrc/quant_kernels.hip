@@ -301,7 +301,14 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __re
 // zeros past TK or K).  Step 1 divides its values by them, quantizes the smoothed
 // bf16 values and writes them back over the tile, and step 2 waits for every
 // wave's write-back, so that both branches read the same smoothed activation.
-template <int NCT, bool SMOOTH>
+//
+// INT4 (the INT4 variant of svdq_w4a4): step 1 quantizes 64-channel groups
+// instead (s = amax / 7, q = clamp(rint(x / s), -8, 7)): a group is eight chunks of
+// a row, held by an aligned block of eight lanes (the chunk swizzle only permutes
+// within such blocks), whose maximum takes three DPP steps.  It stores the codes
+// as the E4M3 bytes of their values (the INT4 GEMM's operand, 8 bytes per lane)
+// and the group's scale from the block's first lane.
+template <int NCT, bool SMOOTH, bool INT4>
 struct LrTile {
   static constexpr int TK = NCT <= 2 ? 256 : 128;  // k per tile
   static constexpr int CPR = TK / 8;                // 16-byte chunks per tile row
@@ -314,16 +321,19 @@ struct LrTile {
   static constexpr int XI = XB / 1024 / NW;         // x loads (and xe stores) per wave per tile, 1 KB each
   static constexpr int LI = LB / 1024 / NW;         // L1^T loads per wave per tile
   static constexpr int DW = XI + LI + (SMOOTH ? 1 : 0);  // loads per wave per tile
+  static constexpr int SPT = INT4 ? 2 * XI : XI;          // stores per wave per tile
 };
 
-template <int NCT, bool SMOOTH>
-__global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                               float c6g, float rc6g, Nvfp4ScaleTable tab,
-                                                               const uint16_t* __restrict__ l1t, int64_t kl,
-                                                               const float* __restrict__ lam, int rpw, float tdiv,
-                                                               uint16_t* __restrict__ xe,
-                                                               uint16_t* __restrict__ t_out) {
-  using C = LrTile<NCT, SMOOTH>;
+// xq: the bf16 expansion [M, K] (nvfp4) or the E4M3 code bytes [M, K] (INT4);
+// xs: the INT4 group scales [M, K/64] (unused for nvfp4).
+template <int NCT, bool SMOOTH, bool INT4>
+__global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                           float c6g, float rc6g, Nvfp4ScaleTable tab,
+                                                           const uint16_t* __restrict__ l1t, int64_t kl,
+                                                           const float* __restrict__ lam, int rpw, float tdiv,
+                                                           uint8_t* __restrict__ xq, float* __restrict__ xs,
+                                                           uint16_t* __restrict__ t_out) {
+  using C = LrTile<NCT, SMOOTH, INT4>;
   constexpr int TK = C::TK, CPR = C::CPR, S = C::S, XI = C::XI, LI = C::LI, NW = C::NW;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S * C::SB];
   __shared__ float tab_d[128], tab_rd[128];
@@ -336,8 +346,13 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
   const u32x4 dx = make_desc(x + m0 * K, rows * pitch);
   const u32x4 dl = make_desc(l1t, (int64_t)32 * NCT * pitch);
   const u32x4 df = make_desc(lam, SMOOTH ? K * 4 : 0);
-  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(xe + m0 * K, (short)0, (int)(rows * pitch),
-                                                                      (int)kRawBufferWord3);
+  const int64_t qpitch = INT4 ? K : 2 * K;  // bytes per row of xq
+  const int64_t ng = K / 64;
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(xq + m0 * qpitch, (short)0,
+                                                                      (int)(rows * qpitch), (int)kRawBufferWord3);
+  // INT4 scales group-major [K/64, M] (the GEMM's layout); M K / 16 < 2^31 bytes
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(xs, (short)0, INT4 ? (int)(M * ng * 4) : 0,
+                                                                       (int)kRawBufferWord3);
   const uint32_t lbase = lds_address(lds);
   const int ntiles = (int)((K + TK - 1) / TK);
 
@@ -380,9 +395,9 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
     const int after = kt < S - 1 ? kt : S - 1;
     switch (after) {
       case 0: QPL_WAIT_VMCNT((S - 2) * C::DW); break;
-      case 1: QPL_WAIT_VMCNT((S - 2) * C::DW + XI); break;
-      case 2: QPL_WAIT_VMCNT((S - 2) * C::DW + 2 * XI); break;
-      default: QPL_WAIT_VMCNT((S - 2) * C::DW + 3 * XI); break;
+      case 1: QPL_WAIT_VMCNT((S - 2) * C::DW + C::SPT); break;
+      case 2: QPL_WAIT_VMCNT((S - 2) * C::DW + 2 * C::SPT); break;
+      default: QPL_WAIT_VMCNT((S - 2) * C::DW + 3 * C::SPT); break;
     }
     QPL_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();  // every wave's part of tile kt is in LDS; tile kt - 1's buffer is free
@@ -395,9 +410,14 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
     for (int j = 0; j < XI; ++j) {
       const int r = slot_row(j, XI), c = slot_chunk(j, XI);
       if ((wv * XI + j) * 64 / CPR >= rows) {
-        // rows past the workgroup's: no work, but the store is still issued (and
+        // rows past the workgroup's: no work, but the stores are still issued (and
         // dropped) so that every wave retires the same number of operations
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, re, (int)kOutOfRange, 0, 0);
+        if constexpr (INT4) {
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, re, (int)kOutOfRange, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(0u, rsc, (int)kOutOfRange, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, re, (int)kOutOfRange, 0, 0);
+        }
         continue;
       }
       u32x4* slot = reinterpret_cast<u32x4*>(xt + ((wv * XI + j) * 64 + lane) * 16);
@@ -419,13 +439,43 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
       for (int i = 0; i < 4; ++i) m = absmax_acc(m, p[i]);
       // the other half of the block is in lane l ^ 1 (chunk c ^ 1 of the same row)
       m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
-      const Nvfp4Block sc = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
-      uint32_t o[4];
-      expand_word(nvfp4_word<false>(p, sc), sc.dsf, o);
-      const uint32_t so = voff(r, c, kt);
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, re,
-                                             so == kOutOfRange ? (int)kOutOfRange : (int)(so + (uint32_t)kt * TK * 2),
-                                             0, 0);
+      if constexpr (INT4) {
+        // the rest of the 64-channel group: lanes l ^ 2 (quad_perm 2,3,0,1), then the
+        // other quad of the 8-lane block (row_half_mirror)
+        m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+        m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+        const float s = absmax_value(m) / 7.0f;
+        uint32_t w0 = 0, w1 = 0;
+        if (s > 0.0f) {
+          const bool ok = div_rn_ok(s);
+          const float rs = 1.0f / s;
+          float q[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = bf16_lo(p[i]), b = bf16_hi(p[i]);
+            q[2 * i] = __builtin_amdgcn_fmed3f(__builtin_rintf(ok ? div_rn_finite(a, s, rs) : a / s), -8.0f, 7.0f);
+            q[2 * i + 1] = __builtin_amdgcn_fmed3f(__builtin_rintf(ok ? div_rn_finite(b, s, rs) : b / s), -8.0f, 7.0f);
+          }
+          w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+          w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)w0, true);
+          w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+          w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)w1, true);
+        }
+        const int64_t k0 = (int64_t)kt * TK + 8 * c;
+        const bool in_k = k0 < K;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, re, in_k ? (int)(r * K + k0) : (int)kOutOfRange, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(s), rsc,
+            in_k && (c & 7) == 0 && r < rows ? (int)(((k0 / 64) * M + m0 + r) * 4) : (int)kOutOfRange, 0, 0);
+      } else {
+        const Nvfp4Block sc = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
+        uint32_t o[4];
+        expand_word(nvfp4_word<false>(p, sc), sc.dsf, o);
+        const uint32_t so = voff(r, c, kt);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, re,
+                                               so == kOutOfRange ? (int)kOutOfRange : (int)(so + (uint32_t)kt * TK * 2),
+                                               0, 0);
+      }
     }
 
     if constexpr (SMOOTH) {
@@ -492,6 +542,124 @@ __global__ __launch_bounds__(512) void k_quant_nvfp4_expand_lr(const uint16_t* _
   }
 }
 
+// ---------------------------------------------------------------------------
+// INT4 (the INT4 variant of svdq_w4a4): one lane per group of 64 channels.
+// s = amax / 7 (correctly rounded); q = clamp(rint(x / s), -8, 7), the quotient
+// correctly rounded (Markstein step from RN(1/s) inside div_rn's range, IEEE
+// division outside); an all-zero group gives s = 0 and codes 0.  F8: each code is
+// written as the E4M3 byte of its integer value [rows, K] (the GEMM's operand:
+// -8..7 are exact in E4M3) and the scales group-major [K/64, rows] (so that the
+// GEMM reads one group's scales of consecutive rows contiguously); otherwise the
+// codes are packed two per byte, the even channel in the low nibble, and the
+// scales are row-major [rows, K/64].
+// ---------------------------------------------------------------------------
+template <bool SMOOTH, bool F8>
+__global__ __launch_bounds__(256) void k_quant_int4(const uint16_t* __restrict__ x, int64_t ngroups, int64_t ng,
+                                                    int64_t rows, const float* __restrict__ lam,
+                                                    uint8_t* __restrict__ xq, float* __restrict__ xs) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= ngroups) return;
+  uint32_t p[32];
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + gi * 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    p[4 * i] = v.x;
+    p[4 * i + 1] = v.y;
+    p[4 * i + 2] = v.z;
+    p[4 * i + 3] = v.w;
+  }
+  if constexpr (SMOOTH) {
+    const f32x4* l = reinterpret_cast<const f32x4*>(lam + (gi % ng) * 64);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const f32x4 v = l[i];
+      p[2 * i] = smooth_pair(p[2 * i], v[0], v[1]);
+      p[2 * i + 1] = smooth_pair(p[2 * i + 1], v[2], v[3]);
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = absmax_acc(m, p[i]);
+  const float s = absmax_value(m) / 7.0f;
+  uint32_t w[16];  // four codes per word, channel order: E4M3 bytes (F8) or int8
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = 0;
+  if (s > 0.0f) {
+    const bool ok = div_rn_ok(s);
+    const float r = 1.0f / s;
+    auto code = [&](float v) {
+      return __builtin_amdgcn_fmed3f(__builtin_rintf(ok ? div_rn_finite(v, s, r) : v / s), -8.0f, 7.0f);
+    };
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float q0 = code(bf16_lo(p[2 * i])), q1 = code(bf16_hi(p[2 * i]));
+      const float q2 = code(bf16_lo(p[2 * i + 1])), q3 = code(bf16_hi(p[2 * i + 1]));
+      if constexpr (F8) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+        w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+      } else {
+        w[i] = ((uint32_t)(int)q0 & 0xFFu) | (((uint32_t)(int)q1 & 0xFFu) << 8) |
+               (((uint32_t)(int)q2 & 0xFFu) << 16) | (((uint32_t)(int)q3 & 0xFFu) << 24);
+      }
+    }
+  }
+  if constexpr (F8) {
+    u32x4* dst = reinterpret_cast<u32x4*>(xq + gi * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+  } else {
+    // bytes (c0, c1, c2, c3) -> nibbles c0 | c1 << 4, c2 << 8 | c3 << 12
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = w[2 * i] & 0x0F0F0F0Fu, b = w[2 * i + 1] & 0x0F0F0F0Fu;
+      const uint32_t pa = (a & 0xFu) | ((a >> 4) & 0xF0u) | ((a >> 8) & 0xF00u) | ((a >> 12) & 0xF000u);
+      const uint32_t pb = (b & 0xFu) | ((b >> 4) & 0xF0u) | ((b >> 8) & 0xF00u) | ((b >> 12) & 0xF000u);
+      o[i] = pa | (pb << 16);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(xq + gi * 32);
+    dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+  }
+  if constexpr (F8) xs[(gi % ng) * rows + gi / ng] = s;
+  else xs[gi] = s;
+}
+
+// Packed INT4 codes [rows, K/2] -> E4M3 bytes of their values [rows, K]: one lane
+// per 16 packed bytes.  Nibble t is the value (t ^ 8) - 8; the converter writes
+// two values per operation (exact: small integers).  The lane holding the first
+// half of a group also copies the group's scale into the group-major layout
+// wst [K/64, rows] that the GEMM reads.
+__global__ __launch_bounds__(256) void k_expand_int4(const uint8_t* __restrict__ wq, int64_t nvec, int64_t K,
+                                                     int64_t rows, const float* __restrict__ ws,
+                                                     uint8_t* __restrict__ w8, float* __restrict__ wst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nvec) return;
+  {
+    const int64_t rb = K / 2, n = (16 * i) / rb, bo = (16 * i) % rb;  // row, byte within the row
+    if (bo % 32 == 0) {
+      const int64_t ng = K / 64, g = bo / 32;
+      wst[g * rows + n] = ws[n * ng + g];
+    }
+  }
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wq) + i);
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    auto val = [&](int byte, int shift) { return (float)((int)(((in[j] >> (8 * byte + shift)) & 0xFu) ^ 8u) - 8); };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(val(2 * h, 0), val(2 * h, 4), 0, false);
+      o[2 * j + h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(val(2 * h + 1, 0), val(2 * h + 1, 4), lo, true);
+    }
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(w8) + 2 * i;
+  dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+  dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 // Host side of the nvfp4 scale rule: d = dec(sf) * g and RN(1 / d) for every
 // block-scale code, in fp32 as on the device (the host build does not contract or
 // flush either).  Code 0x7F (NaN) is never produced.
@@ -538,42 +706,71 @@ hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, fl
   return hipGetLastError();
 }
 
-template <int NCT, bool SMOOTH>
-static void launch_expand_lr(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K, float c6g,
-                             float rc6g, const Nvfp4ScaleTable& tab, const uint16_t* l1t, int64_t kl,
-                             const float* lam, int rpw, float tdiv, uint16_t* xe, uint16_t* t) {
-  hipLaunchKernelGGL((k_quant_nvfp4_expand_lr<NCT, SMOOTH>), grid, dim3(512), 0, stream, x, M, K, c6g, rc6g, tab,
-                     l1t, kl, lam, rpw, tdiv, xe, t);
+template <int NCT, bool SMOOTH, bool INT4>
+static void launch_act_lr(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K, float c6g,
+                          float rc6g, const Nvfp4ScaleTable& tab, const uint16_t* l1t, int64_t kl, const float* lam,
+                          int rpw, float tdiv, uint8_t* xq, float* xs, uint16_t* t) {
+  hipLaunchKernelGGL((k_quant_act_lowrank<NCT, SMOOTH, INT4>), grid, dim3(512), 0, stream, x, M, K, c6g, rc6g, tab,
+                     l1t, kl, lam, rpw, tdiv, xq, xs, t);
 }
 
-template <int NCT>
-static void launch_expand_lr(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K, float c6g,
-                             float rc6g, const Nvfp4ScaleTable& tab, const uint16_t* l1t, int64_t kl,
-                             const float* lam, int rpw, float tdiv, uint16_t* xe, uint16_t* t) {
-  if (lam)
-    launch_expand_lr<NCT, true>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t);
-  else
-    launch_expand_lr<NCT, false>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t);
+template <bool INT4>
+static hipError_t launch_act_lowrank(const uint16_t* x, int64_t M, int64_t K, float c6g, float rc6g,
+                                     const Nvfp4ScaleTable& tab, const float* lam, const uint16_t* l1t, int64_t kl,
+                                     float tdiv, uint8_t* xq, float* xs, uint16_t* t, hipStream_t stream) {
+  // buffer offsets are 32-bit: the L1^T tile rows (at most 128) times the pitch
+  if (K > (int64_t{1} << 21)) return hipErrorInvalidValue;
+  // about one workgroup per CU (256 on MI355X), at most 32 rows each
+  const int64_t rpw64 = (M + 255) / 256;
+  const int rpw = (int)(rpw64 < 32 ? rpw64 : 32);
+  const dim3 grid((unsigned)((M + rpw - 1) / rpw));
+#define QPL_ACT_LR(NCT)                                                                                        \
+  (lam ? launch_act_lr<NCT, true, INT4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xq, xs, t) \
+       : launch_act_lr<NCT, false, INT4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xq, xs, t))
+  switch (kl / 64) {  // rpad / 32
+    case 1: QPL_ACT_LR(1); break;
+    case 2: QPL_ACT_LR(2); break;
+    case 3: QPL_ACT_LR(3); break;
+    case 4: QPL_ACT_LR(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QPL_ACT_LR
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
                                              const uint16_t* l1t, int64_t kl, float tdiv, uint16_t* xe, uint16_t* t,
                                              hipStream_t stream) {
-  // buffer offsets are 32-bit: the L1^T tile rows (at most 128) times the pitch
-  if (K > (int64_t{1} << 21)) return hipErrorInvalidValue;
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  const Nvfp4ScaleTable tab = nvfp4_scale_table(g);
-  // about one workgroup per CU (256 on MI355X), at most 32 rows each
-  const int64_t rpw64 = (M + 255) / 256;
-  const int rpw = (int)(rpw64 < 32 ? rpw64 : 32);
-  const dim3 grid((unsigned)((M + rpw - 1) / rpw));
-  switch (kl / 64) {  // rpad / 32
-    case 1: launch_expand_lr<1>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
-    case 2: launch_expand_lr<2>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
-    case 3: launch_expand_lr<3>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
-    case 4: launch_expand_lr<4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xe, t); break;
-    default: return hipErrorInvalidValue;
+  return launch_act_lowrank<false>(x, M, K, c6g, rc6g, nvfp4_scale_table(g), lam, l1t, kl, tdiv,
+                                   reinterpret_cast<uint8_t*>(xe), nullptr, t, stream);
+}
+
+hipError_t launch_quant_int4_lowrank(const uint16_t* x, int64_t M, int64_t K, const float* lam, const uint16_t* l1t,
+                                     int64_t kl, uint8_t* xq, float* xs, uint16_t* t, hipStream_t stream) {
+  if (M * (K / 64) * 4 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+  return launch_act_lowrank<true>(x, M, K, 0.0f, 0.0f, Nvfp4ScaleTable{}, lam, l1t, kl, 1.0f, xq, xs, t, stream);
+}
+
+hipError_t launch_quant_int4(const uint16_t* x, int64_t M, int64_t K, const float* lam, bool f8, uint8_t* xq,
+                             float* xs, hipStream_t stream) {
+  const int64_t ng = K / 64, n = M * ng;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (lam) {
+    if (f8) hipLaunchKernelGGL((k_quant_int4<true, true>), grid, block, 0, stream, x, n, ng, M, lam, xq, xs);
+    else hipLaunchKernelGGL((k_quant_int4<true, false>), grid, block, 0, stream, x, n, ng, M, lam, xq, xs);
+  } else {
+    if (f8) hipLaunchKernelGGL((k_quant_int4<false, true>), grid, block, 0, stream, x, n, ng, M, lam, xq, xs);
+    else hipLaunchKernelGGL((k_quant_int4<false, false>), grid, block, 0, stream, x, n, ng, M, lam, xq, xs);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_int4(const uint8_t* wq, const float* ws, int64_t N, int64_t K, uint8_t* w8, float* wst,
+                              hipStream_t stream) {
+  const int64_t nvec = N * K / 32;
+  hipLaunchKernelGGL(k_expand_int4, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0, stream, wq, nvec, K, N, ws,
+                     w8, wst);
   return hipGetLastError();
 }
 

@@ -55,6 +55,11 @@ def test_workspace_sizes(lib):
     assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 32, 4, 129) == 0  # rank too large
     assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, 4, 32, 4, 1) == 0     # fp8r has no low rank
     assert qpl.qlinear_workspace_bytes(7, 4, 32, 4) == 0
+    # INT4: codes of x and W as bytes, then (R > 0) the low-rank parts, then the x and W scales
+    r256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, M, K, N) == (r256(M * K) + r256(N * K) + r256(4 * M * K // 64) +
+                                                                 r256(4 * N * K // 64))
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, 4, 96, 4) == 0  # K % 64 != 0
 
 
 def test_global_scale(lib):
@@ -90,6 +95,15 @@ def test_qlinear_validation(lib):
     assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, A, B, 200, D, A, ws, None) == SHAPE
     assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, MIS, B, 4, D, A, ws, None) == ALIGN
     assert lib.qlinear_nvfp4(*args, 1.0, 1.0, MIS, None, None, 0, D, A, ws, None) == ALIGN  # smoothing factors
+    # INT4: K % 64, pointers, alignment, workspace, rank
+    assert lib.quant_act_int4(A, 4, 96, None, B, C, None) == SHAPE
+    assert lib.quant_act_int4(A, 4, 64, None, None, C, None) == NULL
+    assert lib.quant_act_int4(A, 4, 64, MIS, B, C, None) == ALIGN
+    assert lib.qlinear_int4(A, 4, 96, 8, B, C, None, None, None, 0, D, A, ws, None) == SHAPE
+    assert lib.qlinear_int4(A, 4, 64, 8, B, C, None, None, None, 0, D, A, 10, None) == WORKSPACE
+    assert lib.qlinear_int4(A, 4, 64, 8, B, C, None, A, None, 4, D, A, ws, None) == NULL
+    assert lib.qlinear_int4(A, 4, 64, 8, B, C, None, A, B, 200, D, A, ws, None) == SHAPE
+    assert lib.qlinear_int4(A, 4, 64, 8, B, MIS, None, None, None, 0, D, A, ws, None) == ALIGN
     # weight-only 4-bit: group size, K % group, pointers, alignment
     assert lib.quant_weight_awq(A, 4, 64, 48, B, C, D, None) == ARG
     assert lib.quant_weight_awq(A, 4, 96, 64, B, C, D, None) == SHAPE
