@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="activation rows per linear in the CPU sample")
+    ap.add_argument("--no-extras", action="store_true", help="skip the measurements beyond the step (extras)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 256 MiB device copy (the reference kernel for HBM counter scaling)")
     return ap.parse_args()
@@ -202,7 +203,33 @@ def main():
     qbytes = 3.0 * lin["fp8r"]["M"] * lin["fp8r"]["K"] + 4.0 * lin["fp8r"]["M"]
     quant_gbs = qbytes / (tq / nq * 1e-3) / 1e9
 
-    # ---------------------------------------------------------------- beyond the step: SVDQuant smoothing
+    extras = None if args.no_extras else measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors)
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(lin, args.cpu_rows)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e4m3/e2m1 operands, fp32 accumulate, bf16 out", "data": "synthetic",
+        "config": {"workload": "dit_linear_m4608: fp8r 4608x3072x12288 + nvfp4 4608x3072x12288 + "
+                               "svdq nvfp4 4608x3072x3072 r32",
+                   "global_batch": 4608, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "parts": parts,
+        "kernels": kernels,
+        "quant_fp8_row_gbs": round(quant_gbs, 1),
+        "extras": extras,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors):
+    """Timings of what lies beyond the step (the other rows of the method), each on its own."""
+    # ---------------------------------------------------------------- SVDQuant smoothing
     # The svdq linear again with per-channel smoothing factors (quantize fused with
     # x L1 now divides x by them first); same shapes, timed on its own.
     e = lin["svdq"]
@@ -303,27 +330,7 @@ def main():
         gbs = nbytes / (ta / na * 1e-3) / 1e9
         extras[f"{name}_m{M}"] = {"shape": [M, K, N, G], "us": round(1e3 * ta / na, 2), "gbs": round(gbs, 1),
                                   "frac_hbm": round(gbs / HBM_GBS, 4)}
-
-    # ---------------------------------------------------------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lin, args.cpu_rows)
-
-    out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "e4m3/e2m1 operands, fp32 accumulate, bf16 out", "data": "synthetic",
-        "config": {"workload": "dit_linear_m4608: fp8r 4608x3072x12288 + nvfp4 4608x3072x12288 + "
-                               "svdq nvfp4 4608x3072x3072 r32",
-                   "global_batch": 4608, "parallelism": "none (1 GPU)"},
-        "roofline": roofline,
-        "parts": parts,
-        "kernels": kernels,
-        "quant_fp8_row_gbs": round(quant_gbs, 1),
-        "extras": extras,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+    return extras
 
 
 def kernel_source_hash():
