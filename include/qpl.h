@@ -184,6 +184,86 @@ qpl_status qlinear_awq_w4a16(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                              const uint8_t* weight_zero, int64_t group, uint16_t* y, void* stream);
 
 /*
+ * Model-specific epilogues (Nunchaku post, "Introducing Nunchaku Lite", first
+ * paragraph: the original engine's fused QKV projections and fused GELU/MLP
+ * kernels).  The *_ex calls are qlinear_fp8r / qlinear_nvfp4 / qlinear_int4 with an
+ * epilogue descriptor `epi` (NULL: the plain call); everything else about them is
+ * as documented above.
+ *   act       QPL_ACT_GELU_TANH: y = bf16(gelu(v)) with v the layer's fp32 result
+ *             and gelu(v) = v / 2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), the tanh
+ *             form used by DiT feed-forward blocks, evaluated in fp32 as
+ *             v / (1 + exp(-2u)) through exp2 and a reciprocal (a few fp32 ulps)
+ *   q, k, v   fused QKV projection (all three set, or all NULL): the weight is
+ *             [W_q; W_k; W_v] (N = 3 heads head_dim rows) and row m of the result
+ *             goes to q, k and v instead of y:
+ *               part[(h tokens + token_offset + m) head_dim + e] = y[m, p d + h head_dim + e]
+ *             for part p = 0, 1, 2 (q, k, v), head h, d = heads head_dim; each of
+ *             q, k, v is bf16 [heads, tokens, head_dim] (the layout attention reads;
+ *             token_offset places the rows, e.g. image tokens after text tokens).
+ *             Requires head_dim a power of two in [8, 1024], 0 <= token_offset and
+ *             token_offset + M <= tokens, 16-byte aligned q, k, v, and act NONE;
+ *             y may then be NULL.  Rows of q, k, v outside the M written are left
+ *             untouched.
+ * Errors beyond the plain call's: QPL_ERR_ARG for an unknown act or act with QKV,
+ * QPL_ERR_NULL for one or two of q, k, v, or for y NULL without them,
+ * QPL_ERR_SHAPE for the QKV shape conditions above.
+ */
+typedef enum { QPL_ACT_NONE = 0, QPL_ACT_GELU_TANH = 1 } qpl_act;
+
+typedef struct {
+  qpl_act act;
+  uint16_t* q;
+  uint16_t* k;
+  uint16_t* v;
+  int64_t heads, head_dim, tokens, token_offset;
+} qpl_epilogue;
+
+qpl_status qlinear_fp8r_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                           const uint8_t* weight, const float* weight_scale, const qpl_epilogue* epi,
+                           uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+qpl_status qlinear_nvfp4_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                            const uint8_t* weight, const uint8_t* weight_scale,
+                            float weight_scale_2, float input_scale, const float* smooth,
+                            const uint16_t* lora_down, const uint16_t* lora_up, int64_t R,
+                            const qpl_epilogue* epi, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+qpl_status qlinear_int4_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                           const uint8_t* weight, const float* weight_scale, const float* smooth,
+                           const uint16_t* lora_down, const uint16_t* lora_up, int64_t R,
+                           const qpl_epilogue* epi, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fused GELU MLP of nvfp4 layers (same post and paragraph: fused GELU/MLP kernels):
+ *   h = bf16(gelu(fc1(x)))      fc1 as qlinear_nvfp4 with act GELU, [M,K] -> [M,H]
+ *   y = fc2(h)                  fc2 as qlinear_nvfp4, [M,H] -> [M,N]
+ * fc1's epilogue quantizes h the way fc2's own quantizer would (fc2's smoothing,
+ * then 16-column blocks under fc2's input_scale) and writes the expanded values
+ * e2m1(code) * dec(sf) (bf16) that fc2's GEMM multiplies, so h never reaches
+ * memory: the result equals the two layers run one after the other.  fc1 may carry
+ * smoothing and a low-rank branch; fc2 may carry smoothing but no low-rank branch
+ * (fc2->R must be 0: its x L1 needs whole rows of h).  Each layer's tensors are as
+ * in qlinear_nvfp4 (weight [rows, cols/2], weight_scale [rows, cols/16], ...).
+ * Workspace: qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, fc1->R) bytes (0 for
+ * invalid sizes); its first 2 M H bytes hold fc2's expanded operand after the
+ * call.  Errors: as qlinear_nvfp4 for either layer, and QPL_ERR_ARG for
+ * fc2->R != 0.
+ */
+typedef struct {
+  const uint8_t* weight;        /* uint8 [rows, cols/2], two E2M1 codes per byte */
+  const uint8_t* weight_scale;  /* E4M3 [rows, cols/16] */
+  float weight_scale_2;
+  float input_scale;
+  const float* smooth;          /* float [cols] or NULL */
+  const uint16_t* lora_down;    /* bf16 [cols, R] or NULL */
+  const uint16_t* lora_up;      /* bf16 [R, rows] or NULL */
+  int64_t R;
+} qpl_nvfp4_layer;
+
+size_t qlinear_mlp_nvfp4_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1);
+qpl_status qlinear_mlp_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t H, int64_t N,
+                             const qpl_nvfp4_layer* fc1, const qpl_nvfp4_layer* fc2,
+                             uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dequantize a weight to bf16 (guide, "Kernels" section, last paragraph: on other
  * devices the weight is dequantized to compute_dtype on every forward and the
  * layer runs as a regular linear; that linear is the caller's).
@@ -241,7 +321,9 @@ typedef enum {
   QPL_KERNEL_INT4_EXPAND = 14,      /* INT4 weight codes -> E4M3 bytes inside qlinear_int4 */
   QPL_KERNEL_GEMM_INT4 = 15,
   QPL_KERNEL_QUANT_INT4_LOWRANK = 16, /* INT4 quantize fused with x L1 (qlinear_int4, R > 0) */
-  QPL_KERNEL_COUNT = 17
+  QPL_KERNEL_GEMM_EPILOGUE = 17,    /* any GEMM with a GELU, QKV or next-layer epilogue (the *_ex calls, fc1 of
+                                       qlinear_mlp_nvfp4) */
+  QPL_KERNEL_COUNT = 18
 } qpl_kernel;
 
 void qpl_timing_enable(int on);

@@ -64,24 +64,29 @@ def _f32_up(a):
     return np.where(f.astype(np.float64) < a, np.nextafter(f, F32(np.inf)), f).astype(np.float64)
 
 
-def pre_activation_error(ref, abs_sum, K, extra_abs=None):
+def pre_activation_error(ref, abs_sum, K, extra_abs=None, gamma=None):
     """Bound on |y_fp32 - y_exact| for a layer output before its activation: the
-    fp32 accumulation floor ceil(K / 16) 2^-24 sum_k |a_k w_k| (plus the same on
-    the low-rank magnitudes) and two fp32 roundings of the scale products."""
-    g = math.ceil(K / 16) * 2.0 ** -24
+    accumulation floor gamma sum_k |a_k w_k| (gamma defaults to the fp32 floor
+    ceil(K / 16) 2^-24; the low-rank magnitudes take the fp32 floor) and two fp32
+    roundings of the scale products."""
+    g32 = math.ceil(K / 16) * 2.0 ** -24
+    g = g32 if gamma is None else gamma
     e = g * np.asarray(abs_sum, dtype=np.float64) + 2.0 ** -22 * np.abs(ref)
     if extra_abs is not None:
-        e = e + g * np.asarray(extra_abs, dtype=np.float64)
+        e = e + g32 * np.asarray(extra_abs, dtype=np.float64)
     return e
 
 
 def gelu_eval_error(v, h):
-    """Bound on the error of an fp32 evaluation of gelu at v through exp2 and a
-    reciprocal, each within a few fp32 ulps: the relative error grows with the
-    exponent's magnitude 2 |u|; plus an absolute floor below the bf16 range."""
+    """Bound on the error of an fp32 evaluation of gelu at v as v / (1 + 2^t) with
+    t = -2 u log2(e) computed in fp32, exp2 and a reciprocal each within a few fp32
+    ulps: a relative error of t (a few ulps) moves 2^t by |t| ln 2 times it, 2 |u|
+    times, so the relative error is bounded by 2^-23 (16 + 8 |u|); where 1 + 2^t
+    passes 2^126 the reciprocal may flush to zero, an absolute error below
+    |v| 2^-120; plus a floor below the bf16 range."""
     v = np.asarray(v, dtype=np.float64)
     u = SQRT_2_OVER_PI * (v + GELU_CUBIC * v ** 3)
-    return np.abs(h) * 2.0 ** -23 * (16.0 + 4.0 * np.abs(u)) + 2.0 ** -140
+    return np.abs(h) * 2.0 ** -23 * (16.0 + 8.0 * np.abs(u)) + np.abs(v) * 2.0 ** -120 + 2.0 ** -140
 
 
 def gelu_interval(ref, err):

@@ -17,13 +17,33 @@ QPL_NVFP4 = 1
 QPL_INT4 = 2
 
 EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp4", "dequant_weight",
-           "quant_weight_awq", "qlinear_awq_w4a16", "quant_act_int4", "qlinear_int4", "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
+           "quant_weight_awq", "qlinear_awq_w4a16", "quant_act_int4", "qlinear_int4", "qlinear_fp8r_ex",
+           "qlinear_nvfp4_ex", "qlinear_int4_ex", "qlinear_mlp_nvfp4", "qlinear_mlp_nvfp4_workspace_bytes",
+           "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
            "qpl_timing_enable", "qpl_timing_select", "qpl_timing_collect")
 
 # qpl_kernel order of include/qpl.h
 KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_bf16", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
            "lowrank_prep", "dequant", "amax", "weight_bf16", "quant_nvfp4_lowrank", "quant_w4g", "gemv_w4a16",
-           "quant_int4", "int4_expand", "gemm_int4", "quant_int4_lowrank")
+           "quant_int4", "int4_expand", "gemm_int4", "quant_int4_lowrank", "gemm_epilogue")
+
+QPL_ACT_NONE = 0
+QPL_ACT_GELU_TANH = 1
+_ACTS = {None: QPL_ACT_NONE, "none": QPL_ACT_NONE, "gelu_tanh": QPL_ACT_GELU_TANH}
+
+_P, _I64, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+
+
+class Epilogue(ctypes.Structure):
+    """qpl_epilogue of include/qpl.h."""
+    _fields_ = [("act", ctypes.c_int), ("q", _P), ("k", _P), ("v", _P), ("heads", _I64), ("head_dim", _I64),
+                ("tokens", _I64), ("token_offset", _I64)]
+
+
+class Nvfp4Layer(ctypes.Structure):
+    """qpl_nvfp4_layer of include/qpl.h."""
+    _fields_ = [("weight", _P), ("weight_scale", _P), ("weight_scale_2", _F), ("input_scale", _F),
+                ("smooth", _P), ("lora_down", _P), ("lora_up", _P), ("R", _I64)]
 
 _lib = None
 
@@ -54,6 +74,10 @@ def load():
         "quant_act_int4": [P, I64, I64, P, P, P, P],
         "qlinear_int4": [P, I64, I64, I64, P, P, P, P, P, I64, P, P, SZ, P],
         "qpl_amax_bf16": [P, I64, P, P],
+        "qlinear_fp8r_ex": [P, I64, I64, I64, P, P, P, P, P, SZ, P],
+        "qlinear_nvfp4_ex": [P, I64, I64, I64, P, P, F, F, P, P, P, I64, P, P, P, SZ, P],
+        "qlinear_int4_ex": [P, I64, I64, I64, P, P, P, P, P, I64, P, P, P, SZ, P],
+        "qlinear_mlp_nvfp4": [P, I64, I64, I64, I64, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -61,6 +85,8 @@ def load():
         fn.restype = ctypes.c_int
     lib.qlinear_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64, I64]
     lib.qlinear_workspace_bytes.restype = SZ
+    lib.qlinear_mlp_nvfp4_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+    lib.qlinear_mlp_nvfp4_workspace_bytes.restype = SZ
     lib.qpl_nvfp4_global_scale.argtypes = [F]
     lib.qpl_nvfp4_global_scale.restype = F
     lib.qpl_status_str.argtypes = [ctypes.c_int]
@@ -136,24 +162,57 @@ def _workspace(scheme, M, K, N, R, ws, device):
     return ws, ws.numel() * ws.element_size()
 
 
-def qlinear_fp8r(x, weight, weight_scale, y=None, workspace=None, stream=None):
-    """y[M,N] bf16 = fp8r linear of bf16 x [M,K] with E4M3 weight [N,K] and fp32 weight_scale [N]."""
+def _epilogue(act, qkv, M, N, y, device):
+    """(Epilogue or None, y, result): act names the activation ("gelu_tanh"); qkv is
+    (q, k, v, token_offset) with q, k, v bf16 [heads, tokens, head_dim]."""
+    if act not in _ACTS:
+        raise ValueError(f"act: expected one of {sorted(k for k in _ACTS if k)}, got {act!r}")
+    if act is None and qkv is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=device) if y is None else y
+        return None, y, y
+    e = Epilogue()
+    e.act = _ACTS[act]
+    if qkv is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=device) if y is None else y
+        return e, y, y
+    q, k, v, off = qkv
+    heads, tokens, head_dim = q.shape
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, torch.bfloat16, (heads, tokens, head_dim), name)
+    e.q, e.k, e.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    e.heads, e.head_dim, e.tokens, e.token_offset = heads, head_dim, tokens, int(off)
+    return e, None, (q, k, v)
+
+
+def _ref(e):
+    return None if e is None else ctypes.byref(e)
+
+
+def qlinear_fp8r(x, weight, weight_scale, y=None, workspace=None, stream=None, act=None, qkv=None):
+    """y[M,N] bf16 = fp8r linear of bf16 x [M,K] with E4M3 weight [N,K] and fp32 weight_scale [N].
+    act="gelu_tanh" applies GELU before the rounding; qkv=(q, k, v, token_offset) writes the
+    three column parts to q, k, v [heads, tokens, head_dim] instead (and returns them)."""
     M, K = x.shape
     N = weight.shape[0]
     _expect(x, torch.bfloat16, (M, K), "x")
     _expect(weight, torch.uint8, (N, K), "weight")
     _expect(weight_scale, torch.float32, (N,), "weight_scale")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    e, y, out = _epilogue(act, qkv, M, N, y, x.device)
     ws, nbytes = _workspace(QPL_FP8R, M, K, N, 0, workspace, x.device)
-    _check("qlinear_fp8r", load().qlinear_fp8r(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale), _ptr(y),
-                                               _ptr(ws), nbytes, _stream(stream)))
-    return y
+    if e is None:
+        _check("qlinear_fp8r", load().qlinear_fp8r(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale), _ptr(y),
+                                                   _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check("qlinear_fp8r_ex", load().qlinear_fp8r_ex(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale),
+                                                         _ref(e), _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    return out
 
 
 def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_down=None, lora_up=None, y=None,
-                  workspace=None, stream=None, smooth=None):
+                  workspace=None, stream=None, smooth=None, act=None, qkv=None):
     """y[M,N] bf16 = nvfp4 linear (+ (x L1) L2 when lora_down [K,R] / lora_up [R,N] are given);
-    with smooth (float32 [K]) both terms take the smoothed activation bf16(x / smooth)."""
+    with smooth (float32 [K]) both terms take the smoothed activation bf16(x / smooth).
+    act and qkv as in qlinear_fp8r."""
     M, K = x.shape
     N = weight.shape[0]
     _expect(x, torch.bfloat16, (M, K), "x")
@@ -166,13 +225,16 @@ def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_dow
         R = lora_down.shape[1]
         _expect(lora_down, torch.bfloat16, (K, R), "lora_down")
         _expect(lora_up, torch.bfloat16, (R, N), "lora_up")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    e, y, out = _epilogue(act, qkv, M, N, y, x.device)
     ws, nbytes = _workspace(QPL_NVFP4, M, K, N, R, workspace, x.device)
-    _check("qlinear_nvfp4", load().qlinear_nvfp4(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale),
-                                                 float(weight_scale_2), float(input_scale), _ptr(smooth),
-                                                 _ptr(lora_down),
-                                                 _ptr(lora_up), R, _ptr(y), _ptr(ws), nbytes, _stream(stream)))
-    return y
+    args = (_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale), float(weight_scale_2), float(input_scale),
+            _ptr(smooth), _ptr(lora_down), _ptr(lora_up), R)
+    if e is None:
+        _check("qlinear_nvfp4", load().qlinear_nvfp4(*args, _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check("qlinear_nvfp4_ex", load().qlinear_nvfp4_ex(*args, _ref(e), _ptr(y), _ptr(ws), nbytes,
+                                                           _stream(stream)))
+    return out
 
 
 def quant_act_int4(x, smooth=None, x_q=None, x_scale=None, stream=None):
@@ -189,8 +251,9 @@ def quant_act_int4(x, smooth=None, x_q=None, x_scale=None, stream=None):
 
 
 def qlinear_int4(x, weight, weight_scale, lora_down=None, lora_up=None, y=None, workspace=None, stream=None,
-                 smooth=None):
-    """y[M,N] bf16 = INT4 W4A4 linear (+ (x L1) L2), the INT4 variant of svdq_w4a4."""
+                 smooth=None, act=None, qkv=None):
+    """y[M,N] bf16 = INT4 W4A4 linear (+ (x L1) L2), the INT4 variant of svdq_w4a4; act and
+    qkv as in qlinear_fp8r."""
     M, K = x.shape
     N = weight.shape[0]
     _expect(x, torch.bfloat16, (M, K), "x")
@@ -203,11 +266,55 @@ def qlinear_int4(x, weight, weight_scale, lora_down=None, lora_up=None, y=None, 
         R = lora_down.shape[1]
         _expect(lora_down, torch.bfloat16, (K, R), "lora_down")
         _expect(lora_up, torch.bfloat16, (R, N), "lora_up")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    e, y, out = _epilogue(act, qkv, M, N, y, x.device)
     ws, nbytes = _workspace(QPL_INT4, M, K, N, R, workspace, x.device)
-    _check("qlinear_int4", load().qlinear_int4(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale), _ptr(smooth),
-                                               _ptr(lora_down), _ptr(lora_up), R, _ptr(y), _ptr(ws), nbytes,
-                                               _stream(stream)))
+    args = (_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale), _ptr(smooth), _ptr(lora_down), _ptr(lora_up), R)
+    if e is None:
+        _check("qlinear_int4", load().qlinear_int4(*args, _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check("qlinear_int4_ex", load().qlinear_int4_ex(*args, _ref(e), _ptr(y), _ptr(ws), nbytes,
+                                                         _stream(stream)))
+    return out
+
+
+def qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1=0):
+    return int(load().qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1))
+
+
+def _layer(d, rows, cols, name):
+    """Nvfp4Layer from a dict with weight [rows, cols/2], weight_scale [rows, cols/16],
+    weight_scale_2, input_scale and optional smooth [cols], lora_down [cols, R], lora_up [R, rows]."""
+    _expect(d["weight"], torch.uint8, (rows, cols // 2), name + ".weight")
+    _expect(d["weight_scale"], torch.uint8, (rows, cols // 16), name + ".weight_scale")
+    L = Nvfp4Layer()
+    L.weight, L.weight_scale = d["weight"].data_ptr(), d["weight_scale"].data_ptr()
+    L.weight_scale_2, L.input_scale = float(d["weight_scale_2"]), float(d["input_scale"])
+    if d.get("smooth") is not None:
+        _expect(d["smooth"], torch.float32, (cols,), name + ".smooth")
+        L.smooth = d["smooth"].data_ptr()
+    if d.get("lora_down") is not None:
+        R = d["lora_down"].shape[1]
+        _expect(d["lora_down"], torch.bfloat16, (cols, R), name + ".lora_down")
+        _expect(d["lora_up"], torch.bfloat16, (R, rows), name + ".lora_up")
+        L.lora_down, L.lora_up, L.R = d["lora_down"].data_ptr(), d["lora_up"].data_ptr(), R
+    return L
+
+
+def qlinear_mlp_nvfp4(x, fc1, fc2, y=None, workspace=None, stream=None):
+    """y [M,N] bf16 = fc2(bf16(gelu(fc1(x)))) for nvfp4 layers fc1 [H,K] and fc2 [N,H]
+    given as dicts (see _layer); fc1's epilogue quantizes the hidden activation for fc2,
+    whose expanded operand is left in the first 2 M H bytes of the workspace."""
+    M, K = x.shape
+    _expect(x, torch.bfloat16, (M, K), "x")
+    H = fc1["weight"].shape[0]
+    N = fc2["weight"].shape[0]
+    l1, l2 = _layer(fc1, H, K, "fc1"), _layer(fc2, N, H, "fc2")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    need = qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, l1.R)
+    ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device) if workspace is None else workspace
+    _check("qlinear_mlp_nvfp4", load().qlinear_mlp_nvfp4(_ptr(x), M, K, H, N, ctypes.byref(l1), ctypes.byref(l2),
+                                                         _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                                         _stream(stream)))
     return y
 
 

@@ -38,6 +38,7 @@
 
 #include "qpl_dma.h"
 #include "qpl_internal.h"
+#include "qpl_nvfp4.h"
 
 namespace qpl {
 
@@ -153,7 +154,94 @@ struct GemmArgs {
 constexpr int NSTORE = 32;           // 16-byte output stores per wave per tile (fast path)
 constexpr int SCALE_BUF = 2048;      // per tile parity: s_x of the tile's 256 rows, then s_w of its 256 columns
 
-// Epilogue of one tile: y = bf16((acc * rs(m)) * cs(n)).  acc[i][j] holds y^T: its
+// f(integral_constant<int, I>) for I = B .. E - 1, expanded at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Epilogue kinds (bit flags; the Nunchaku post, "Introducing Nunchaku Lite", names
+// fused QKV projections and fused GELU/MLP kernels as the model-specific paths of
+// its original engine):
+// * EPI_GELU: the tanh form of GELU on each fp32 result before the bf16 rounding;
+// * EPI_QKV: the output row's three parts (columns [0, d), [d, 2d), [2d, 3d)) go to
+//   three tensors [heads, tokens, head_dim] at a token offset, the layout attention
+//   reads, instead of the row-major y;
+// * EPI_NEXT_NVFP4: the bf16 result is quantized for the next layer as its nvfp4
+//   quantizer would (its smoothing, then 16-column blocks under its input_scale)
+//   and written as the expanded values e2m1(code) * dec(sf), the operand the nvfp4
+//   GEMM multiplies, so that the next layer reads it without a quantize pass.
+constexpr int EPI_GELU = 1, EPI_QKV = 2, EPI_NEXT_NVFP4 = 4;
+
+struct EpiArgs {
+  uint16_t* qkv[3];  // EPI_QKV: q, k, v
+  int64_t d;         // EPI_QKV: columns per part (heads * head_dim)
+  int64_t tokens;    // EPI_QKV: tokens per head
+  int64_t off;       // EPI_QKV: token of output row 0
+  int lg_hd;         // EPI_QKV: log2(head_dim)
+  const float* lam;  // EPI_NEXT_NVFP4: the next layer's smoothing factors [N], or null
+  float g;           // EPI_NEXT_NVFP4: the next layer's input_scale
+  float c6g, rc6g;   // EPI_NEXT_NVFP4: 6 g and RN(1 / (6 g))
+};
+
+// GELU, tanh form: v sigma(2u) with u = sqrt(2/pi) (v + 0.044715 v^3), since
+// (1 + tanh u) / 2 = 1 / (1 + exp(-2u)).  exp2 and the reciprocal run on the
+// transcendental unit; the exponent is t = -2 u log2(e) = v (C1 + C3 v^2).  Large
+// negative v gives t = +inf and a result of -0; large positive v gives v.
+constexpr float GELU_C1 = -0x1.26aec2p+1f;  // -2 sqrt(2/pi) log2(e), -2.3022082
+constexpr float GELU_C3 = -0x1.a5a7d0p-4f;  // GELU_C1 * 0.044715, -0.10294324
+__device__ __forceinline__ float gelu_tanh(float v) {
+  const float t = v * __builtin_fmaf(GELU_C3, v * v, GELU_C1);
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
+// EPI_NEXT_NVFP4 on eight consecutive bf16 results (four pairs) of one row: this
+// lane holds columns n .. n + 7 and lane l ^ 32 the other half of the 16-column
+// block; the block maximum is exchanged across the halves with one
+// V_PERMLANE32_SWAP (every lane of the wave takes part).  Returns the expanded
+// values in the same positions.
+__device__ __forceinline__ u32x4 next_nvfp4(const u32x4& v, int64_t n, int64_t N, const EpiArgs& e,
+                                            const float* tab_d, const float* tab_rd) {
+  uint32_t p[4] = {v.x, v.y, v.z, v.w};
+  if (e.lam && n < N) {
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(e.lam + n);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(e.lam + n + 4);
+    p[0] = smooth_pair(p[0], l0[0], l0[1]);
+    p[1] = smooth_pair(p[1], l0[2], l0[3]);
+    p[2] = smooth_pair(p[2], l1[0], l1[1]);
+    p[3] = smooth_pair(p[3], l1[2], l1[3]);
+  }
+  const float own = block_absmax(p, 4);
+  const uint32_t ob = __float_as_uint(own);
+  const auto sw = __builtin_amdgcn_permlane32_swap(ob, ob, false, false);
+  // one of the two results is this lane's value, the other its partner's
+  const float bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  const Nvfp4Block s = nvfp4_scale(bmax, e.c6g, e.rc6g, tab_d, tab_rd);
+  uint32_t o[4];
+  expand_word(nvfp4_word<false>(p, s), s.dsf, o);
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Destination of output element (m, n): y[m, n], or under EPI_QKV element
+// n mod head_dim of head (n mod d) / head_dim of part n / d at token off + m.
+template <int EPI>
+__device__ __forceinline__ uint16_t* out_ptr(uint16_t* __restrict__ y, int64_t m, int64_t n, int64_t N,
+                                             const EpiArgs& e) {
+  if constexpr ((EPI & EPI_QKV) != 0) {
+    const int part = (n >= e.d) + (n >= 2 * e.d);
+    const int64_t c = n - part * e.d;
+    const int64_t h = c >> e.lg_hd;
+    return e.qkv[part] + (((h * e.tokens + e.off + m) << e.lg_hd) + (c & ((int64_t{1} << e.lg_hd) - 1)));
+  } else {
+    return y + m * N + n;
+  }
+}
+
+// Epilogue of one tile: y = bf16(act((acc * rs(m)) * cs(n))), then the EPI output
+// transform.  acc[i][j] holds y^T: its
 // element r at lane l is row m = m0 + 128 wm + 32 j + l % 32, column
 // n = n0 + 128 wn + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4.  Lanes l and l + 32
 // exchange halves (V_PERMLANE32_SWAP) so that each lane holds eight consecutive
@@ -163,14 +251,17 @@ constexpr int SCALE_BUF = 2048;      // per tile parity: s_x of the tile's 256 r
 // n0 + 128 wn + ..., wn in 0..1; 2: n0 + 64 wn + ..., wn in 0..3).  Returns the
 // number of store instructions left in flight: 2 NJ NI on the interior path, 0 on
 // the edge path (which checks every element and drains its stores).
-template <int NJ, int NI = 4, class RowScale, class ColScale>
+template <int NJ, int NI = 4, int EPI = 0, class RowScale, class ColScale>
 __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
                                           int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
-                                          const ColScale& cs) {
+                                          const ColScale& cs, const EpiArgs& e = EpiArgs{},
+                                          const float* tab_d = nullptr, const float* tab_rd = nullptr) {
   // interior: the wavefront's rows and columns all inside the matrix
   const bool fast = m0 + (wm + 1) * 32 * NJ <= M && n0 + (wn + 1) * 32 * NI <= N && (N & 7) == 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
+  // unrolled at compile time: with a heavy epilogue the body exceeds what the
+  // unroll pragma accepts, and a rolled loop would index acc dynamically (scratch)
+  static_for<0, NJ>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
     const int mr = wm * 32 * NJ + j * 32 + (lane & 31);
     const float fr = rs(mr);
     const int64_t m = m0 + mr;
@@ -184,27 +275,36 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
           const int g = 2 * gp + h;
           const f32x4 fc = cs(wn * 32 * NI + i * 32 + g * 8 + (lane >> 5) * 4);
           const f32x16& a = acc[i][j];
-          w[h][0] = pack_bf16((a[g * 4 + 0] * fr) * fc[0], (a[g * 4 + 1] * fr) * fc[1]);
-          w[h][1] = pack_bf16((a[g * 4 + 2] * fr) * fc[2], (a[g * 4 + 3] * fr) * fc[3]);
+          float o[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            o[c] = (a[g * 4 + c] * fr) * fc[c];
+            if constexpr ((EPI & EPI_GELU) != 0) o[c] = gelu_tanh(o[c]);
+          }
+          w[h][0] = pack_bf16(o[0], o[1]);
+          w[h][1] = pack_bf16(o[2], o[3]);
         }
         const auto r0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
         const auto r1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-        const u32x4 v = u32x4{r0[0], r1[0], r0[1], r1[1]};
+        u32x4 v = u32x4{r0[0], r1[0], r0[1], r1[1]};
         const int64_t n = n0 + wn * 32 * NI + i * 32 + (2 * gp + (lane >> 5)) * 8;
+        if constexpr ((EPI & EPI_NEXT_NVFP4) != 0) v = next_nvfp4(v, n, N, e, tab_d, tab_rd);
+        // the segment's eight columns stay inside one head (head_dim >= 8, n % 8 == 0)
+        uint16_t* dst = out_ptr<EPI>(y, m, n, N, e);
         if (fast) {
-          *reinterpret_cast<u32x4*>(y + m * N + n) = v;
+          *reinterpret_cast<u32x4*>(dst) = v;
         } else if (m < M) {
-          const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+          const uint32_t el[4] = {v.x, v.y, v.z, v.w};
           if ((N & 7) == 0 && n + 8 <= N) {
-            *reinterpret_cast<u32x4*>(y + m * N + n) = v;
+            *reinterpret_cast<u32x4*>(dst) = v;
           } else {
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-              if (n + c < N) y[m * N + n + c] = (uint16_t)(e[c >> 1] >> (16 * (c & 1)));
+              if (n + c < N) dst[c] = (uint16_t)(el[c >> 1] >> (16 * (c & 1)));
           }
         }
       }
-  }
+  });
   if (fast) return 2 * NJ * NI;
   QPL_WAIT_VMCNT(0);
   return 0;
@@ -226,13 +326,18 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
 // Otherwise the output scale is gscale.  LOWRANK: pass 2 continues the same
 // accumulation with T / gscale and L2 (the quantizer stores T divided by gscale),
 // so y = bf16(gscale (x_q w_q^T + (T / gscale) L2)).
-template <class T, bool ROWCOL, bool LOWRANK>
+template <class T, bool ROWCOL, bool LOWRANK, int EPI>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* __restrict__ sa,
                                                 const float* __restrict__ sb, float gscale,
-                                                uint16_t* __restrict__ Y) {
+                                                uint16_t* __restrict__ Y, const EpiArgs& e) {
   constexpr int D = ROWCOL ? 10 : 8;  // loads per wave per slab
+  constexpr bool NEXT = (EPI & EPI_NEXT_NVFP4) != 0;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lsc[ROWCOL ? 3 * SCALE_BUF : 16];
+  // EPI_NEXT_NVFP4: the next layer's block-scale table (written here, read after
+  // the barriers of the first slabs)
+  __shared__ float tabs[NEXT ? 256 : 1];
+  if constexpr (NEXT) fill_scale_table(e.g, tabs, tabs + 128);
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wv >> 1, wn = wv & 1;
@@ -408,13 +513,13 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
     const Unit un = unit(ti);
     if constexpr (ROWCOL) {
       const float* ls = reinterpret_cast<const float*>(lsc + (ti & 1) * SCALE_BUF);
-      st1 = store_tile<NJ>(
+      st1 = store_tile<NJ, 4, EPI>(
           acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int r) { return ls[r]; },
-          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); });
+          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); }, e);
     } else {
-      st1 = store_tile<NJ>(
+      st1 = store_tile<NJ, 4, EPI>(
           acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return gscale; },
-          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
+          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e, tabs, tabs + 128);
     }
     if (st1 == 0) st2 = st3 = 0;
   };
@@ -445,15 +550,16 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
   QPL_WAIT_LGKM0();
 }
 
+template <int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_fp8r(
-    GemmArgs p, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ Y) {
-  gemm_persistent<Fp8Mma, true, false>(p, sa, sb, 1.0f, Y);
+    GemmArgs p, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ Y, EpiArgs e) {
+  gemm_persistent<Fp8Mma, true, false, EPI>(p, sa, sb, 1.0f, Y, e);
 }
 
-template <bool LOWRANK>
+template <bool LOWRANK, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
-    GemmArgs p, float gscale, uint16_t* __restrict__ Y) {
-  gemm_persistent<Bf16Mma, false, LOWRANK>(p, nullptr, nullptr, gscale, Y);
+    GemmArgs p, float gscale, uint16_t* __restrict__ Y, EpiArgs e) {
+  gemm_persistent<Bf16Mma, false, LOWRANK, EPI>(p, nullptr, nullptr, gscale, Y, e);
 }
 
 // ---------------------------------------------------------------------------
@@ -499,9 +605,9 @@ struct I4Cfg {
 };
 constexpr int NST4 = 4;
 
-template <bool LOWRANK>
+template <bool LOWRANK, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_int4(
-    GemmArgs p, const float* __restrict__ sxp, const float* __restrict__ swp, uint16_t* __restrict__ Y) {
+    GemmArgs p, const float* __restrict__ sxp, const float* __restrict__ swp, uint16_t* __restrict__ Y, EpiArgs e) {
   using C = I4Cfg<LOWRANK>;
   constexpr int TM = C::TM, WN = C::WN, NJ = C::NJ, NI = C::NI, XI = C::XI, D = C::D, XB = C::XB, SC = C::SC;
   constexpr int STAGE = C::STAGE;
@@ -682,8 +788,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     int64_t m0, n0;
     tile_coords(tile_seq(ti, b, p.nwg), p.tiles_m, p.tiles_n, m0, n0, TM);
-    st1 = store_tile<NJ, NI>(acc, wm, wn, lane, m0, n0, p.M, p.N, Y, [](int) { return 1.0f; },
-                             [](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; });
+    st1 = store_tile<NJ, NI, EPI>(acc, wm, wn, lane, m0, n0, p.M, p.N, Y, [](int) { return 1.0f; },
+                                  [](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e);
     if (st1 == 0) st2 = st3 = 0;
   }
   QPL_WAIT_VMCNT(0);
@@ -724,8 +830,30 @@ static void gemm_plan(GemmArgs& p, int nk) {
   p.ntail = split ? tail : 0;
 }
 
+// Kernel-side epilogue arguments and kind (EPI flags) of a launch.
+static int epi_kind(const Epilogue& ep, EpiArgs& e) {
+  e = EpiArgs{};
+  int k = ep.gelu ? EPI_GELU : 0;
+  if (ep.qkv[0]) {
+    k |= EPI_QKV;
+    for (int i = 0; i < 3; ++i) e.qkv[i] = ep.qkv[i];
+    e.d = ep.d;
+    e.tokens = ep.tokens;
+    e.off = ep.off;
+    e.lg_hd = ep.lg_hd;
+  }
+  if (ep.next_nvfp4) {
+    k |= EPI_NEXT_NVFP4;
+    e.lam = ep.lam;
+    e.g = ep.g;
+    e.c6g = 6.0f * ep.g;
+    e.rc6g = 1.0f / e.c6g;
+  }
+  return k;
+}
+
 hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws, int64_t M,
-                            int64_t K, int64_t N, uint16_t* y, hipStream_t stream) {
+                            int64_t K, int64_t N, const Epilogue& ep, uint16_t* y, hipStream_t stream) {
   GemmArgs p{};
   p.a = xq;
   p.w = w;
@@ -737,12 +865,33 @@ hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w
   p.tiles_n = (int)((N + 255) / 256);
   p.ntiles = p.tiles_m * p.tiles_n;
   gemm_plan(p, (p.kbytes1 + SROW - 1) / SROW);
-  hipLaunchKernelGGL(k_gemm_fp8r, dim3((unsigned)p.nwg), dim3(256), 0, stream, p, xs, ws, y);
+  EpiArgs e;
+  const dim3 grid((unsigned)p.nwg), block(256);
+  switch (epi_kind(ep, e)) {
+    case 0: hipLaunchKernelGGL(k_gemm_fp8r<0>, grid, block, 0, stream, p, xs, ws, y, e); break;
+    case EPI_GELU: hipLaunchKernelGGL(k_gemm_fp8r<EPI_GELU>, grid, block, 0, stream, p, xs, ws, y, e); break;
+    case EPI_QKV: hipLaunchKernelGGL(k_gemm_fp8r<EPI_QKV>, grid, block, 0, stream, p, xs, ws, y, e); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool LR>
+static hipError_t launch_nvfp4_epi(int kind, dim3 grid, hipStream_t stream, const GemmArgs& p, float gscale,
+                                   uint16_t* y, const EpiArgs& e) {
+  constexpr int GN = EPI_GELU | EPI_NEXT_NVFP4;
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((k_gemm_nvfp4<LR, 0>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
+    case EPI_GELU: hipLaunchKernelGGL((k_gemm_nvfp4<LR, EPI_GELU>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_nvfp4<LR, EPI_QKV>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
+    case GN: hipLaunchKernelGGL((k_gemm_nvfp4<LR, GN>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
-                             LowRank lr, uint16_t* y, hipStream_t stream) {
+                             LowRank lr, const Epilogue& ep, uint16_t* y, hipStream_t stream) {
   GemmArgs p{};
   p.a = reinterpret_cast<const uint8_t*>(xe);
   p.w = reinterpret_cast<const uint8_t*>(we);
@@ -762,16 +911,27 @@ hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscal
   p.tiles_n = (int)((N + 255) / 256);
   p.ntiles = p.tiles_m * p.tiles_n;
   gemm_plan(p, nk);
-  const dim3 grid((unsigned)p.nwg), block(256);
-  if (lr.kl > 0)
-    hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, block, 0, stream, p, gscale, y);
-  else
-    hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, block, 0, stream, p, gscale, y);
+  EpiArgs e;
+  const int kind = epi_kind(ep, e);
+  const dim3 grid((unsigned)p.nwg);
+  return lr.kl > 0 ? launch_nvfp4_epi<true>(kind, grid, stream, p, gscale, y, e)
+                   : launch_nvfp4_epi<false>(kind, grid, stream, p, gscale, y, e);
+}
+
+template <bool LR>
+static hipError_t launch_int4_epi(int kind, dim3 grid, hipStream_t stream, const GemmArgs& p, const float* xs,
+                                  const float* ws, uint16_t* y, const EpiArgs& e) {
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((k_gemm_int4<LR, 0>), grid, dim3(512), 0, stream, p, xs, ws, y, e); break;
+    case EPI_GELU: hipLaunchKernelGGL((k_gemm_int4<LR, EPI_GELU>), grid, dim3(512), 0, stream, p, xs, ws, y, e); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm_int4<LR, EPI_QKV>), grid, dim3(512), 0, stream, p, xs, ws, y, e); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_int4(const uint8_t* x8, const float* xs, const uint8_t* w8, const float* ws, int64_t M,
-                            int64_t K, int64_t N, LowRank lr, uint16_t* y, hipStream_t stream) {
+                            int64_t K, int64_t N, LowRank lr, const Epilogue& ep, uint16_t* y, hipStream_t stream) {
   GemmArgs p{};
   p.a = x8;
   p.w = w8;
@@ -795,12 +955,11 @@ hipError_t launch_gemm_int4(const uint8_t* x8, const float* xs, const uint8_t* w
   p.nwg = nk >= NST4 ? (p.ntiles < 256 ? p.ntiles : 256) : p.ntiles;
   p.nfull = p.ntiles;
   p.ntail = 0;
-  const dim3 grid((unsigned)p.nwg), block(512);
-  if (lr.kl > 0)
-    hipLaunchKernelGGL(k_gemm_int4<true>, grid, block, 0, stream, p, xs, ws, y);
-  else
-    hipLaunchKernelGGL(k_gemm_int4<false>, grid, block, 0, stream, p, xs, ws, y);
-  return hipGetLastError();
+  EpiArgs e;
+  const int kind = epi_kind(ep, e);
+  const dim3 grid((unsigned)p.nwg);
+  return lr.kl > 0 ? launch_int4_epi<true>(kind, grid, stream, p, xs, ws, y, e)
+                   : launch_int4_epi<false>(kind, grid, stream, p, xs, ws, y, e);
 }
 
 hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,

@@ -159,6 +159,139 @@ class Timed {
   hipEvent_t start_ = nullptr;
 };
 
+// Epilogue descriptor -> launcher form, with its checks: act known; q, k, v all
+// set or all null; with them N = 3 heads head_dim, head_dim a power of two in
+// [8, 1024], token_offset + M <= tokens and no activation; otherwise y set.
+qpl_status epilogue_of(const qpl_epilogue* epi, int64_t M, int64_t N, const uint16_t* y, qpl::Epilogue& ep) {
+  ep = qpl::Epilogue{};
+  if (!epi) return y ? QPL_OK : QPL_ERR_NULL;
+  if (epi->act != QPL_ACT_NONE && epi->act != QPL_ACT_GELU_TANH) return QPL_ERR_ARG;
+  ep.gelu = epi->act == QPL_ACT_GELU_TANH;
+  const int nset = (epi->q != nullptr) + (epi->k != nullptr) + (epi->v != nullptr);
+  if (nset == 0) return y ? QPL_OK : QPL_ERR_NULL;
+  if (nset != 3) return QPL_ERR_NULL;
+  if (!aligned16(epi->q) || !aligned16(epi->k) || !aligned16(epi->v)) return QPL_ERR_ALIGN;
+  if (ep.gelu) return QPL_ERR_ARG;
+  const int64_t hd = epi->head_dim;
+  if (hd < 8 || hd > 1024 || (hd & (hd - 1)) != 0) return QPL_ERR_SHAPE;
+  if (epi->heads < 1 || epi->heads > kMaxDim / hd || N != 3 * epi->heads * hd) return QPL_ERR_SHAPE;
+  if (epi->tokens < 1 || epi->token_offset < 0 || epi->token_offset > epi->tokens - M) return QPL_ERR_SHAPE;
+  if (epi->tokens > kMaxElems / (epi->heads * hd)) return QPL_ERR_SHAPE;
+  ep.qkv[0] = epi->q;
+  ep.qkv[1] = epi->k;
+  ep.qkv[2] = epi->v;
+  ep.d = epi->heads * hd;
+  ep.tokens = epi->tokens;
+  ep.off = epi->token_offset;
+  while ((int64_t{1} << ep.lg_hd) < hd) ++ep.lg_hd;
+  return QPL_OK;
+}
+
+qpl_kernel gemm_kind(const qpl::Epilogue& ep, qpl_kernel plain) {
+  return ep.gelu || ep.qkv[0] || ep.next_nvfp4 ? QPL_KERNEL_GEMM_EPILOGUE : plain;
+}
+
+qpl_status fp8r_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                       const float* weight_scale, const qpl_epilogue* epi, uint16_t* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!x || !weight || !weight_scale || !ws) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws))
+    return QPL_ERR_ALIGN;
+  qpl_status s = check_gemm_dims(M, K, N);
+  if (s != QPL_OK) return s;
+  qpl::Epilogue ep;
+  if ((s = epilogue_of(epi, M, N, y, ep)) != QPL_OK) return s;
+  const Layout L = layout(QPL_FP8R, M, K, N, 0);
+  if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* xq = base + L.off[0];
+  float* xs = reinterpret_cast<float*>(base + L.off[1]);
+  if ((s = launched(Timed(QPL_KERNEL_QUANT_FP8_ROW, st)(qpl::launch_quant_fp8_row(x, M, K, xq, xs, st)))) != QPL_OK)
+    return s;
+  return launched(Timed(gemm_kind(ep, QPL_KERNEL_GEMM_FP8R), st)(
+      qpl::launch_gemm_fp8r(xq, xs, weight, weight_scale, M, K, N, ep, y, st)));
+}
+
+// Checks of one nvfp4 layer's tensors for a linear [N, K] (weight, scales, global
+// scales, smoothing factors, low-rank factors against R).
+qpl_status check_nvfp4_layer(const uint8_t* weight, const uint8_t* weight_scale, float weight_scale_2,
+                             float input_scale, const float* smooth, const uint16_t* lora_down,
+                             const uint16_t* lora_up, int64_t R) {
+  if (!weight || !weight_scale) return QPL_ERR_NULL;
+  if (!aligned16(weight) || !aligned16(weight_scale) || !aligned16(smooth)) return QPL_ERR_ALIGN;
+  if (R < 0 || R > kMaxRank) return QPL_ERR_SHAPE;
+  if (R > 0 && (!lora_down || !lora_up)) return QPL_ERR_NULL;
+  if (R == 0 && (lora_down || lora_up)) return QPL_ERR_ARG;
+  if (R > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return QPL_ERR_ALIGN;
+  if (!positive_finite(weight_scale_2) || !positive_finite(input_scale) || !positive_finite(6.0f * input_scale))
+    return QPL_ERR_ARG;
+  if (!std::isfinite(input_scale * weight_scale_2)) return QPL_ERR_ARG;
+  return QPL_OK;
+}
+
+// The steps of an nvfp4 linear before its GEMM, in the workspace laid out by L at
+// base: the activation quantize (fused with T = x L1 when R > 0) into xe and the
+// weight expansion into we.
+qpl_status nvfp4_operands(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                          const uint8_t* weight_scale, float gscale, float input_scale, const float* smooth,
+                          const uint16_t* lora_down, const uint16_t* lora_up, int64_t R, const Layout& L,
+                          uint8_t* base, hipStream_t st, qpl::LowRank& lr) {
+  qpl_status s;
+  uint16_t* xe = reinterpret_cast<uint16_t*>(base + L.off[0]);
+  uint16_t* we = reinterpret_cast<uint16_t*>(base + L.off[1]);
+  lr = qpl::LowRank{};
+  if (R > 0) {
+    // SVDQuant branch: factor layouts, then the activation quantize fused with T = x L1
+    const int64_t kl = 2 * rank_pad(R);
+    uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[2]);
+    uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[3]);
+    uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
+    if ((s = launched(Timed(QPL_KERNEL_LOWRANK_PREP, st)(
+             qpl::launch_lowrank_prep(lora_down, lora_up, K, N, R, kl, l1t, l2t, st)))) != QPL_OK)
+      return s;
+    if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
+             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, smooth, l1t, kl, gscale, xe, t, st)))) != QPL_OK)
+      return s;
+    lr.t = t;
+    lr.l2t = l2t;
+    lr.kl = kl;
+  } else if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(
+                  qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, smooth, xe, st)))) != QPL_OK) {
+    return s;
+  }
+  // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue
+  return launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st)));
+}
+
+qpl_status nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                        const uint8_t* weight_scale, float weight_scale_2, float input_scale, const float* smooth,
+                        const uint16_t* lora_down, const uint16_t* lora_up, int64_t R, const qpl_epilogue* epi,
+                        uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !ws) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return QPL_ERR_ALIGN;
+  qpl_status s = check_nvfp4_layer(weight, weight_scale, weight_scale_2, input_scale, smooth, lora_down, lora_up, R);
+  if (s != QPL_OK) return s;
+  if ((s = check_gemm_dims(M, K, N)) != QPL_OK) return s;
+  qpl::Epilogue ep;
+  if ((s = epilogue_of(epi, M, N, y, ep)) != QPL_OK) return s;
+  const float gscale = input_scale * weight_scale_2;
+  const Layout L = layout(QPL_NVFP4, M, K, N, R);
+  if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
+  if ((s = check_device()) != QPL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  qpl::LowRank lr;
+  if ((s = nvfp4_operands(x, M, K, N, weight, weight_scale, gscale, input_scale, smooth, lora_down, lora_up, R, L,
+                          base, st, lr)) != QPL_OK)
+    return s;
+  const uint16_t* xe = reinterpret_cast<const uint16_t*>(base + L.off[0]);
+  const uint16_t* we = reinterpret_cast<const uint16_t*>(base + L.off[1]);
+  return launched(Timed(gemm_kind(ep, R > 0 ? QPL_KERNEL_GEMM_NVFP4_LOWRANK : QPL_KERNEL_GEMM_NVFP4), st)(
+      qpl::launch_gemm_nvfp4(xe, we, gscale, M, K, N, lr, ep, y, st)));
+}
+
 }  // namespace
 
 QPL_EXPORT void qpl_timing_enable(int on) { g_timing.store(on ? (1u << QPL_KERNEL_COUNT) - 1u : 0u); }
@@ -240,74 +373,99 @@ QPL_EXPORT qpl_status quant_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, f
 QPL_EXPORT qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
                                    const float* weight_scale, uint16_t* y, void* ws, size_t ws_bytes,
                                    void* stream) {
-  if (!x || !weight || !weight_scale || !y || !ws) return QPL_ERR_NULL;
-  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws))
-    return QPL_ERR_ALIGN;
-  qpl_status s = check_gemm_dims(M, K, N);
-  if (s != QPL_OK) return s;
-  const Layout L = layout(QPL_FP8R, M, K, N, 0);
-  if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
-  if ((s = check_device()) != QPL_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  uint8_t* xq = base + L.off[0];
-  float* xs = reinterpret_cast<float*>(base + L.off[1]);
-  if ((s = launched(Timed(QPL_KERNEL_QUANT_FP8_ROW, st)(qpl::launch_quant_fp8_row(x, M, K, xq, xs, st)))) != QPL_OK)
-    return s;
-  return launched(Timed(QPL_KERNEL_GEMM_FP8R, st)(qpl::launch_gemm_fp8r(xq, xs, weight, weight_scale, M, K, N, y, st)));
+  return fp8r_linear(x, M, K, N, weight, weight_scale, nullptr, y, ws, ws_bytes, stream);
+}
+
+QPL_EXPORT qpl_status qlinear_fp8r_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                      const float* weight_scale, const qpl_epilogue* epi, uint16_t* y, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return fp8r_linear(x, M, K, N, weight, weight_scale, epi, y, ws, ws_bytes, stream);
 }
 
 QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
                                     const uint8_t* weight_scale, float weight_scale_2, float input_scale,
                                     const float* smooth, const uint16_t* lora_down, const uint16_t* lora_up,
                                     int64_t R, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
-  if (!x || !weight || !weight_scale || !y || !ws) return QPL_ERR_NULL;
-  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws) ||
-      !aligned16(smooth))
-    return QPL_ERR_ALIGN;
-  qpl_status s = check_gemm_dims(M, K, N);
+  return nvfp4_linear(x, M, K, N, weight, weight_scale, weight_scale_2, input_scale, smooth, lora_down, lora_up, R,
+                      nullptr, y, ws, ws_bytes, stream);
+}
+
+QPL_EXPORT qpl_status qlinear_nvfp4_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                       const uint8_t* weight_scale, float weight_scale_2, float input_scale,
+                                       const float* smooth, const uint16_t* lora_down, const uint16_t* lora_up,
+                                       int64_t R, const qpl_epilogue* epi, uint16_t* y, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  return nvfp4_linear(x, M, K, N, weight, weight_scale, weight_scale_2, input_scale, smooth, lora_down, lora_up, R,
+                      epi, y, ws, ws_bytes, stream);
+}
+
+namespace {
+
+// Fused MLP: fc1 with GELU, whose epilogue writes fc2's quantized operand h_e
+// (workspace part 0), then fc2.  Workspace: [h_e: 2 M H][fc1's nvfp4 layout for
+// (M, K, H, R1)][fc2's expanded weight: 2 N H], each part rounded up to 256 bytes.
+struct MlpLayout {
+  size_t he = 0, fc1 = 0, we2 = 0, total = 0;
+  Layout l1;
+};
+
+MlpLayout mlp_layout(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1) {
+  MlpLayout L;
+  L.l1 = layout(QPL_NVFP4, M, K, H, R1);
+  L.fc1 = round256(size_t(2) * size_t(M) * size_t(H));
+  L.we2 = L.fc1 + L.l1.total;
+  L.total = L.we2 + round256(size_t(2) * size_t(N) * size_t(H));
+  return L;
+}
+
+}  // namespace
+
+QPL_EXPORT size_t qlinear_mlp_nvfp4_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1) {
+  if (check_gemm_dims(M, K, H) != QPL_OK || check_gemm_dims(M, H, N) != QPL_OK || R1 < 0 || R1 > kMaxRank) return 0;
+  return mlp_layout(M, K, H, N, R1).total;
+}
+
+QPL_EXPORT qpl_status qlinear_mlp_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t H, int64_t N,
+                                        const qpl_nvfp4_layer* fc1, const qpl_nvfp4_layer* fc2, uint16_t* y,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !fc1 || !fc2 || !y || !ws) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return QPL_ERR_ALIGN;
+  qpl_status s = check_nvfp4_layer(fc1->weight, fc1->weight_scale, fc1->weight_scale_2, fc1->input_scale,
+                                   fc1->smooth, fc1->lora_down, fc1->lora_up, fc1->R);
   if (s != QPL_OK) return s;
-  if (R < 0 || R > kMaxRank) return QPL_ERR_SHAPE;
-  if (R > 0 && (!lora_down || !lora_up)) return QPL_ERR_NULL;
-  if (R == 0 && (lora_down || lora_up)) return QPL_ERR_ARG;
-  if (R > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return QPL_ERR_ALIGN;
-  if (!positive_finite(weight_scale_2) || !positive_finite(input_scale) || !positive_finite(6.0f * input_scale))
-    return QPL_ERR_ARG;
-  const float gscale = input_scale * weight_scale_2;
-  if (!std::isfinite(gscale)) return QPL_ERR_ARG;
-  const Layout L = layout(QPL_NVFP4, M, K, N, R);
+  if ((s = check_nvfp4_layer(fc2->weight, fc2->weight_scale, fc2->weight_scale_2, fc2->input_scale, fc2->smooth,
+                             fc2->lora_down, fc2->lora_up, fc2->R)) != QPL_OK)
+    return s;
+  // fc2's low-rank branch would need whole hidden rows, which no fc1 tile holds
+  if (fc2->R != 0) return QPL_ERR_ARG;
+  if ((s = check_gemm_dims(M, K, H)) != QPL_OK || (s = check_gemm_dims(M, H, N)) != QPL_OK) return s;
+  const MlpLayout L = mlp_layout(M, K, H, N, fc1->R);
   if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
   if ((s = check_device()) != QPL_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  uint16_t* xe = reinterpret_cast<uint16_t*>(base + L.off[0]);
-  uint16_t* we = reinterpret_cast<uint16_t*>(base + L.off[1]);
+  uint16_t* he = reinterpret_cast<uint16_t*>(base);
+  uint8_t* b1 = base + L.fc1;
+  uint16_t* we2 = reinterpret_cast<uint16_t*>(base + L.we2);
+  const float g1 = fc1->input_scale * fc1->weight_scale_2;
   qpl::LowRank lr;
-  if (R > 0) {
-    // SVDQuant branch: factor layouts, then the activation quantize fused with T = x L1
-    const int64_t kl = 2 * rank_pad(R);
-    uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[2]);
-    uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[3]);
-    uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
-    if ((s = launched(Timed(QPL_KERNEL_LOWRANK_PREP, st)(
-             qpl::launch_lowrank_prep(lora_down, lora_up, K, N, R, kl, l1t, l2t, st)))) != QPL_OK)
-      return s;
-    if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
-             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, smooth, l1t, kl, gscale, xe, t, st)))) != QPL_OK)
-      return s;
-    lr.t = t;
-    lr.l2t = l2t;
-    lr.kl = kl;
-  } else if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(
-                  qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, smooth, xe, st)))) != QPL_OK) {
+  if ((s = nvfp4_operands(x, M, K, H, fc1->weight, fc1->weight_scale, g1, fc1->input_scale, fc1->smooth,
+                          fc1->lora_down, fc1->lora_up, fc1->R, L.l1, b1, st, lr)) != QPL_OK)
     return s;
-  }
-  // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue
-  if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st)))) !=
-      QPL_OK)
+  qpl::Epilogue ep;
+  ep.gelu = true;
+  ep.next_nvfp4 = true;
+  ep.lam = fc2->smooth;
+  ep.g = fc2->input_scale;
+  if ((s = launched(Timed(QPL_KERNEL_GEMM_EPILOGUE, st)(qpl::launch_gemm_nvfp4(
+           reinterpret_cast<const uint16_t*>(b1 + L.l1.off[0]), reinterpret_cast<const uint16_t*>(b1 + L.l1.off[1]),
+           g1, M, K, H, lr, ep, he, st)))) != QPL_OK)
     return s;
-  return launched(Timed(R > 0 ? QPL_KERNEL_GEMM_NVFP4_LOWRANK : QPL_KERNEL_GEMM_NVFP4, st)(
-      qpl::launch_gemm_nvfp4(xe, we, gscale, M, K, N, lr, y, st)));
+  if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(
+           qpl::launch_dequant_nvfp4(fc2->weight, fc2->weight_scale, 1.0f, N, H, we2, st)))) != QPL_OK)
+    return s;
+  return launched(Timed(QPL_KERNEL_GEMM_NVFP4, st)(qpl::launch_gemm_nvfp4(
+      he, we2, fc2->input_scale * fc2->weight_scale_2, M, H, N, qpl::LowRank{}, qpl::Epilogue{}, y, st)));
 }
 
 QPL_EXPORT qpl_status quant_weight_awq(const uint16_t* w, int64_t N, int64_t K, int64_t group, uint8_t* w_q,
@@ -351,11 +509,13 @@ QPL_EXPORT qpl_status quant_act_int4(const uint16_t* x, int64_t M, int64_t K, co
   return launched(Timed(QPL_KERNEL_QUANT_INT4, st)(qpl::launch_quant_int4(x, M, K, smooth, false, x_q, x_scale, st)));
 }
 
-QPL_EXPORT qpl_status qlinear_int4(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
-                                   const float* weight_scale, const float* smooth, const uint16_t* lora_down,
-                                   const uint16_t* lora_up, int64_t R, uint16_t* y, void* ws, size_t ws_bytes,
-                                   void* stream) {
-  if (!x || !weight || !weight_scale || !y || !ws) return QPL_ERR_NULL;
+namespace {
+
+qpl_status int4_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                              const float* weight_scale, const float* smooth, const uint16_t* lora_down,
+                              const uint16_t* lora_up, int64_t R, const qpl_epilogue* epi, uint16_t* y, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!x || !weight || !weight_scale || !ws) return QPL_ERR_NULL;
   if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws) ||
       !aligned16(smooth))
     return QPL_ERR_ALIGN;
@@ -366,6 +526,8 @@ QPL_EXPORT qpl_status qlinear_int4(const uint16_t* x, int64_t M, int64_t K, int6
   if (R > 0 && (!lora_down || !lora_up)) return QPL_ERR_NULL;
   if (R == 0 && (lora_down || lora_up)) return QPL_ERR_ARG;
   if (R > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return QPL_ERR_ALIGN;
+  qpl::Epilogue ep;
+  if ((s = epilogue_of(epi, M, N, y, ep)) != QPL_OK) return s;
   const Layout L = layout(QPL_INT4, M, K, N, R);
   if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
   if ((s = check_device()) != QPL_OK) return s;
@@ -397,7 +559,24 @@ QPL_EXPORT qpl_status qlinear_int4(const uint16_t* x, int64_t M, int64_t K, int6
   if ((s = launched(Timed(QPL_KERNEL_INT4_EXPAND, st)(
            qpl::launch_expand_int4(weight, weight_scale, N, K, w8, wst, st)))) != QPL_OK)
     return s;
-  return launched(Timed(QPL_KERNEL_GEMM_INT4, st)(qpl::launch_gemm_int4(xq, xs, w8, wst, M, K, N, lr, y, st)));
+  return launched(Timed(gemm_kind(ep, QPL_KERNEL_GEMM_INT4), st)(
+      qpl::launch_gemm_int4(xq, xs, w8, wst, M, K, N, lr, ep, y, st)));
+}
+
+}  // namespace
+
+QPL_EXPORT qpl_status qlinear_int4(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                   const float* weight_scale, const float* smooth, const uint16_t* lora_down,
+                                   const uint16_t* lora_up, int64_t R, uint16_t* y, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return int4_linear(x, M, K, N, weight, weight_scale, smooth, lora_down, lora_up, R, nullptr, y, ws, ws_bytes, stream);
+}
+
+QPL_EXPORT qpl_status qlinear_int4_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
+                                      const float* weight_scale, const float* smooth, const uint16_t* lora_down,
+                                      const uint16_t* lora_up, int64_t R, const qpl_epilogue* epi, uint16_t* y,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  return int4_linear(x, M, K, N, weight, weight_scale, smooth, lora_down, lora_up, R, epi, y, ws, ws_bytes, stream);
 }
 
 QPL_EXPORT qpl_status dequant_weight(qpl_scheme scheme, const uint8_t* weight, const void* weight_scale,

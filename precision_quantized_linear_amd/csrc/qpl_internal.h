@@ -59,8 +59,25 @@ hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K,
                                 uint16_t* out, hipStream_t stream);
 
+// What a GEMM's epilogue writes (default: y = bf16 result, row-major [M, N]).
+// gelu: the tanh form of GELU on the fp32 result before the bf16 rounding.
+// qkv: (all three set) the result's column parts [0, d), [d, 2d), [2d, 3d) go to
+// q, k, v, each [heads, tokens, 2^lg_hd] bf16, row m at token off + m; y unused.
+// next_nvfp4 (nvfp4 GEMM, with gelu): y receives the bf16 result quantized by the
+// nvfp4 rule under global scale g after smoothing by lam (nullable), as the expanded
+// values e2m1(code) * dec(sf); N % 16 == 0.
+struct Epilogue {
+  bool gelu = false;
+  uint16_t* qkv[3] = {nullptr, nullptr, nullptr};
+  int64_t d = 0, tokens = 0, off = 0;
+  int lg_hd = 0;
+  bool next_nvfp4 = false;
+  const float* lam = nullptr;
+  float g = 0.0f;
+};
+
 hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws,
-                            int64_t M, int64_t K, int64_t N, uint16_t* y, hipStream_t stream);
+                            int64_t M, int64_t K, int64_t N, const Epilogue& ep, uint16_t* y, hipStream_t stream);
 
 // Low-rank operands for the nvfp4 GEMM epilogue: t [M, KL] bf16 holds T = x L1 split
 // into hi and lo bf16 halves, l2t [N, KL] bf16 holds L2^T twice; KL = 2 * ceil(R/32) * 32.
@@ -73,7 +90,7 @@ struct LowRank {
 // xe [M,K] and we [N,K] are the bf16 expansions e2m1(code) * dec(sf) of the
 // quantized activations and weights; y = bf16(gscale * xe we^T [+ low-rank term]).
 hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
-                             LowRank lr, uint16_t* y, hipStream_t stream);
+                             LowRank lr, const Epilogue& ep, uint16_t* y, hipStream_t stream);
 
 // Factor layouts for the low-rank branch: l1t [kl / 2, K] = L1^T and l2t [N, kl] =
 // [L2^T | L2^T], both zero past R.
@@ -81,7 +98,7 @@ hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscal
 // ws [K/64, N] fp32 group scales (group-major), K % 64 == 0; optional low-rank
 // pass (tdiv 1).
 hipError_t launch_gemm_int4(const uint8_t* x8, const float* xs, const uint8_t* w8, const float* ws, int64_t M,
-                            int64_t K, int64_t N, LowRank lr, uint16_t* y, hipStream_t stream);
+                            int64_t K, int64_t N, LowRank lr, const Epilogue& ep, uint16_t* y, hipStream_t stream);
 hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,
                                uint16_t* l1t, uint16_t* l2t, hipStream_t stream);
 

@@ -49,6 +49,14 @@ WORKLOADS = {
     # FLUX adanorm_zero 3072 -> 6 x 3072 and adanorm_single 3072 -> 3 x 3072, group 64
     "awq_adanorm_zero": dict(c=6, scheme="w4a16", M=1, K=3072, N=18432, dist="normal", frac_out=0.0, mult=1.0, G=64),
     "awq_adanorm_single": dict(c=7, scheme="w4a16", M=1, K=3072, N=9216, dist="normal", frac_out=0.0, mult=1.0, G=64),
+    # FLUX double-block feed-forward (3072 -> 4 x 3072 -> 3072) as SVDQuant W4A4 layers:
+    # fc1 [N, K] with the rank-32 branch, fc2 [N2, N] without one (w2)
+    "svdq_mlp": dict(c=8, scheme="nvfp4", M=4608, K=3072, N=12288, N2=3072, dist="normal", frac_out=0.01,
+                     mult=10.0, n_cal=8, R=32),
+    # FLUX attention input projection: [W_q; W_k; W_v] for 24 heads of 128 over the
+    # 4096 image tokens, written after the 512 text tokens of the joint sequence
+    "qkv_dit": dict(c=9, scheme="nvfp4", M=4096, K=3072, N=9216, dist="normal", frac_out=0.01, mult=10.0, n_cal=8,
+                    heads=24, head_dim=128, tokens=4608, offset=512),
 }
 
 
@@ -80,13 +88,13 @@ def _normal(seed, shape, std):
     return bf16_round(_rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(std))
 
 
-def make(name, M=None, K=None, N=None):
+def make(name, M=None, K=None, N=None, N2=None):
     """Inputs of workload ``name`` as bf16 bit arrays (uint16).
 
     M, K, N override the sizes (same recipe and seeds) for the small parity cases.
     Returns a dict: spec, M, K, N, x [M,K], w [N,K] (the residual for the
     SVDQuant workload), and l1 [K,R], l2 [R,N] when the workload has a low-rank
-    branch.
+    branch; w2 [N2, N] for a workload with a second layer (N2 overrides its size).
     """
     spec = dict(WORKLOADS[name])
     M = spec["M"] if M is None else M
@@ -107,6 +115,10 @@ def make(name, M=None, K=None, N=None):
         out["l1"], out["l2"], out["R"] = l1, l2, R
     else:
         out["w"] = w
+    if "N2" in spec:
+        N2 = spec["N2"] if N2 is None else N2
+        out["N2"] = N2
+        out["w2"] = _normal(100 * c + 6, (N2, N), 0.02)
     return out
 
 

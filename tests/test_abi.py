@@ -138,3 +138,77 @@ def test_binding_rejects_wrong_tensors():
     x = torch.zeros((4, 32), dtype=torch.float32)
     with pytest.raises(ValueError):
         qpl.quant_act_fp8_row(x)
+
+
+def epi(act=0, qkv=False, heads=2, head_dim=16, tokens=8, off=0, only_q=False):
+    e = qpl.Epilogue()
+    e.act = act
+    if qkv or only_q:
+        e.q = 1 << 24
+        if not only_q:
+            e.k, e.v = 1 << 25, 1 << 26
+        e.heads, e.head_dim, e.tokens, e.token_offset = heads, head_dim, tokens, off
+    return ctypes.byref(e)
+
+
+def test_epilogue_validation(lib):
+    ws = 1 << 30
+    # plain descriptor: y still required; unknown activation
+    assert lib.qlinear_fp8r_ex(A, 4, 32, 8, B, C, epi(), None, A, ws, None) == NULL
+    assert lib.qlinear_fp8r_ex(A, 4, 32, 8, B, C, epi(act=7), D, A, ws, None) == ARG
+    nv = (A, 4, 32, 96, B, C, 1.0, 1.0, None, None, None, 0)
+    assert lib.qlinear_nvfp4_ex(*nv, epi(act=2), D, A, ws, None) == ARG
+    # QKV: all three or none, no activation with it, shape rules (N = 3 heads head_dim)
+    assert lib.qlinear_nvfp4_ex(*nv, epi(only_q=True), None, A, ws, None) == NULL
+    assert lib.qlinear_nvfp4_ex(*nv, epi(act=1, qkv=True), None, A, ws, None) == ARG
+    assert lib.qlinear_nvfp4_ex(*nv, epi(qkv=True, heads=3), None, A, ws, None) == SHAPE
+    assert lib.qlinear_nvfp4_ex(*nv, epi(qkv=True, heads=4, head_dim=8, tokens=8), None, A, ws, None) != SHAPE
+    assert lib.qlinear_nvfp4_ex(A, 4, 32, 36, B, C, 1.0, 1.0, None, None, None, 0,
+                                epi(qkv=True, heads=2, head_dim=6), None, A, ws, None) == SHAPE  # not a power of two
+    assert lib.qlinear_nvfp4_ex(*nv, epi(qkv=True, tokens=5, off=2), None, A, ws, None) == SHAPE  # 2 + 4 > 5
+    assert lib.qlinear_nvfp4_ex(*nv, epi(qkv=True, off=-1), None, A, ws, None) == SHAPE
+    e = qpl.Epilogue()
+    e.q, e.k, e.v = 1 << 24, (1 << 25) + 8, 1 << 26
+    e.heads, e.head_dim, e.tokens = 2, 16, 8
+    assert lib.qlinear_nvfp4_ex(*nv, ctypes.byref(e), None, A, ws, None) == ALIGN
+    i4 = (A, 4, 64, 96, B, C, None, None, None, 0)
+    assert lib.qlinear_int4_ex(*i4, epi(qkv=True, heads=3), None, A, ws, None) == SHAPE
+    assert lib.qlinear_int4_ex(*i4, epi(act=1), None, A, ws, None) == NULL
+
+
+def layer(R=0, bad_scale=False, lora=False):
+    L = qpl.Nvfp4Layer()
+    L.weight, L.weight_scale = 1 << 20, 1 << 21
+    L.weight_scale_2, L.input_scale = (0.0 if bad_scale else 1.0), 1.0
+    if lora:
+        L.lora_down, L.lora_up = 1 << 22, 1 << 23
+    L.R = R
+    return ctypes.byref(L)
+
+
+def test_mlp_validation_and_workspace(lib):
+    M, K, H, N = 4608, 3072, 12288, 3072
+    r256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    fc1 = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, H)
+    assert qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N) == r256(2 * M * H) + fc1 + r256(2 * N * H)
+    fc1r = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, H, 32)
+    assert qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, 32) == r256(2 * M * H) + fc1r + r256(2 * N * H)
+    assert qpl.qlinear_mlp_nvfp4_workspace_bytes(4, 32, 24, 8) == 0   # H % 16 != 0
+    assert qpl.qlinear_mlp_nvfp4_workspace_bytes(4, 32, 32, 8, 129) == 0
+    ws = 1 << 30
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), None, D, A, ws, None) == NULL
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(bad_scale=True), D, A, ws, None) == ARG
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(R=4, lora=True), D, A, ws, None) == ARG
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(R=4), layer(), D, A, ws, None) == NULL
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 24, 8, layer(), layer(), D, A, ws, None) == SHAPE
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(), D, A, 100, None) == WORKSPACE
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(), MIS, A, ws, None) == ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="forces the no-device status; a GPU is present")
+def test_epilogue_calls_reach_the_device_check(lib):
+    ws = 1 << 30
+    assert lib.qlinear_nvfp4_ex(A, 4, 32, 96, B, C, 1.0, 1.0, None, None, None, 0, epi(qkv=True), None, A, ws,
+                                None) == DEVICE
+    assert lib.qlinear_fp8r_ex(A, 4, 32, 8, B, C, epi(act=1), D, A, ws, None) == DEVICE
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(), D, A, ws, None) == DEVICE
