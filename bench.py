@@ -22,7 +22,9 @@ timed region (the library's event timing, limited to that kernel).  `parts` and
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
 (rank 0, one GPU only).  `extras` times what lies beyond the step: the svdq linear
 with SVDQuant smoothing factors, the INT4 variant of svdq_w4a4 at the DiT shapes,
-and the weight-only 4-bit (awq_w4a16) GEMV at the FLUX modulation shapes.
+the weight-only 4-bit (awq_w4a16) GEMV at the FLUX modulation shapes, and the
+model-specific epilogues: GELU on the nvfp4 linear, the GELU MLP against the same
+layers with a separate GELU pass, and the fused QKV scatter.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -41,7 +43,7 @@ METRIC = "qlinear TFLOP/s (act-quant+GEMM) and % of FP8/FP4 MFMA peak, M=4608"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_4608x3072x12288.md")
 # sources of the kernel the traffic counters were taken on; a changed source voids them
 TRAFFIC_SOURCES = ("precision_quantized_linear_amd/csrc/gemm_kernels.hip", "precision_quantized_linear_amd/csrc/qpl_dma.h",
-                   "precision_quantized_linear_amd/csrc/qpl_device.h")
+                   "precision_quantized_linear_amd/csrc/qpl_device.h", "precision_quantized_linear_amd/csrc/qpl_nvfp4.h")
 COPY_PROBE_BYTES = 256 << 20
 
 
@@ -330,7 +332,119 @@ def measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors)
         gbs = nbytes / (ta / na * 1e-3) / 1e9
         extras[f"{name}_m{M}"] = {"shape": [M, K, N, G], "us": round(1e3 * ta / na, 2), "gbs": round(gbs, 1),
                                   "frac_hbm": round(gbs / HBM_GBS, 4)}
+    extras.update(measure_epilogues(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors))
     return extras
+
+
+def measure_epilogues(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors):
+    """The model-specific epilogues: GELU on the nvfp4 linear, the GELU MLP against
+    the same layers with a separate GELU pass, and the fused QKV scatter."""
+    from synthetic import calibration_batches
+
+    def timed(fn, kinds=()):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        qpl.timing_collect()
+        qpl.timing_select(list(kinds))
+        evs = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        qpl.timing_select([])
+        got = qpl.timing_collect()
+        us = {k: round(1e3 * got[k][1] / got[k][0], 2) for k in kinds if got[k][0]}
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs), us
+
+    def gscale(t):
+        amax = torch.zeros((1,), dtype=torch.float32, device=dev)
+        qpl.amax_bf16(t.contiguous(), amax=amax)
+        return qpl.nvfp4_global_scale(float(amax.item()))
+
+    out = {}
+    # GELU on the nvfp4 linear 4608 x 3072 x 12288 (the step's dominant GEMM)
+    e = lin["nvfp4"]
+    ms, us = timed(lambda: qpl.qlinear_nvfp4(e["x"], e["wq"], e["wbs"], e["g_w"], e["g_in"], y=e["y"],
+                                             workspace=e["ws_buf"], act="gelu_tanh"), ["gemm_epilogue"])
+    ng, tg = kern["gemm_nvfp4"]
+    out["gelu_nvfp4"] = {"shape": [e["M"], e["K"], e["N"]], "ms": round(ms, 4), "gemm_us": us.get("gemm_epilogue"),
+                         "gemm_plain_us": round(1e3 * tg / ng, 2)}
+
+    # FLUX feed-forward 4608 x 3072 -> 12288 -> 3072 as SVDQuant layers (rank 32 and
+    # smoothing on both); fc2's input_scale calibrated on this batch's hidden activation
+    d = make("svdq_mlp")
+    M, K, H, N = d["M"], d["K"], d["N"], d["N2"]
+    x = bf16(d["x"])
+    w1, w2 = bf16(d["w"]), bf16(d["w2"])
+    g_w1, g_w2 = gscale(w1), gscale(w2)
+    w1q, w1b = qpl.quant_act_nvfp4(w1, g_w1)
+    w2q, w2b = qpl.quant_act_nvfp4(w2, g_w2)
+    del w1, w2
+    lam1 = torch.from_numpy(smooth_factors("svdq_mlp")).to(dev)
+    lam2 = torch.from_numpy(smooth_factors("svdq_mlp", K=H)).to(dev)
+    g1 = max(gscale(bf16(b)) for b in calibration_batches("svdq_mlp"))
+    lr1 = dict(lora_down=bf16(d["l1"]), lora_up=bf16(d["l2"]))
+    lr2 = dict(lora_down=bf16(d["l1_2"]), lora_up=bf16(d["l2_2"]))
+    h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ws1 = torch.empty((qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, H, 32),), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty((qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, H, N, 32),), dtype=torch.uint8, device=dev)
+    qpl.qlinear_nvfp4(x, w1q, w1b, g_w1, g1, y=h, act="gelu_tanh", smooth=lam1, workspace=ws1, **lr1)
+    g2 = gscale((h.float() / lam2).to(torch.bfloat16))
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fc1 = dict(weight=w1q, weight_scale=w1b, weight_scale_2=g_w1, input_scale=g1, smooth=lam1, **lr1)
+    fc2 = dict(weight=w2q, weight_scale=w2b, weight_scale_2=g_w2, input_scale=g2, smooth=lam2, **lr2)
+    wsm = torch.empty((qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, 32, 32),), dtype=torch.uint8, device=dev)
+
+    def unfused():
+        qpl.qlinear_nvfp4(x, w1q, w1b, g_w1, g1, y=h, smooth=lam1, workspace=ws1, **lr1)
+        torch.nn.functional.gelu(h, approximate="tanh")
+        qpl.qlinear_nvfp4(h, w2q, w2b, g_w2, g2, y=y2, smooth=lam2, workspace=ws2, **lr2)
+
+    ms_f, us_f = timed(lambda: qpl.qlinear_mlp_nvfp4(x, fc1, fc2, y=y2, workspace=wsm),
+                       ["gemm_epilogue", "gemm_nvfp4_lowrank", "quant_nvfp4_lowrank"])
+    ms_u, us_u = timed(unfused, ["gemm_nvfp4_lowrank"])
+    fl = 2.0 * M * K * H + 2.0 * M * H * N
+    out["mlp_nvfp4"] = {"shape": [M, K, H, N, 32], "ms": round(ms_f, 4), "tflops": round(fl / (ms_f * 1e-3) / 1e12, 1),
+                        "unfused_torch_gelu_ms": round(ms_u, 4),
+                        "fc1_gemm_gelu_us": us_f.get("gemm_epilogue"),
+                        "fc1_gemm_plain_us": us_u.get("gemm_nvfp4_lowrank"),
+                        "gemm_lowrank_us": us_f.get("gemm_nvfp4_lowrank"),
+                        "quant_lowrank_us": us_f.get("quant_nvfp4_lowrank")}
+    del x, w1q, w1b, w2q, w2b, h, ws1, ws2, y2, wsm
+
+    # FLUX attention input projection over the 4096 image tokens into q, k, v
+    # [24, 4608, 128] after the 512 text tokens
+    d = make("qkv_dit")
+    s = d["spec"]
+    x = bf16(d["x"])
+    w = bf16(d["w"])
+    g_w = gscale(w)
+    wq, wb = qpl.quant_act_nvfp4(w, g_w)
+    del w
+    g_in = max(gscale(bf16(b)) for b in calibration_batches("qkv_dit"))
+    q, k, v = (torch.empty((s["heads"], s["tokens"], s["head_dim"]), dtype=torch.bfloat16, device=dev)
+               for _ in range(3))
+    y = torch.empty((d["M"], d["N"]), dtype=torch.bfloat16, device=dev)
+    wsq = torch.empty((qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, d["M"], d["K"], d["N"], 0),), dtype=torch.uint8,
+                      device=dev)
+    dd = s["heads"] * s["head_dim"]
+
+    def plain_then_copy():
+        qpl.qlinear_nvfp4(x, wq, wb, g_w, g_in, y=y, workspace=wsq)
+        for i, t in enumerate((q, k, v)):
+            t[:, s["offset"]:].copy_(y[:, i * dd:(i + 1) * dd].view(d["M"], s["heads"], s["head_dim"]).transpose(0, 1))
+
+    ms_q, us_q = timed(lambda: qpl.qlinear_nvfp4(x, wq, wb, g_w, g_in, workspace=wsq, qkv=(q, k, v, s["offset"])),
+                       ["gemm_epilogue"])
+    ms_p, _ = timed(plain_then_copy)
+    out["qkv_nvfp4"] = {"shape": [d["M"], d["K"], d["N"]], "heads": s["heads"], "head_dim": s["head_dim"],
+                        "fused_ms": round(ms_q, 4), "plain_then_torch_copy_ms": round(ms_p, 4),
+                        "gemm_us": us_q.get("gemm_epilogue")}
+    return out
 
 
 def kernel_source_hash():

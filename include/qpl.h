@@ -232,20 +232,19 @@ qpl_status qlinear_int4_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                            const qpl_epilogue* epi, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Fused GELU MLP of nvfp4 layers (same post and paragraph: fused GELU/MLP kernels):
+ * GELU MLP of nvfp4 layers (same post and paragraph: fused GELU/MLP kernels):
  *   h = bf16(gelu(fc1(x)))      fc1 as qlinear_nvfp4 with act GELU, [M,K] -> [M,H]
  *   y = fc2(h)                  fc2 as qlinear_nvfp4, [M,H] -> [M,N]
- * fc1's epilogue quantizes h the way fc2's own quantizer would (fc2's smoothing,
- * then 16-column blocks under fc2's input_scale) and writes the expanded values
- * e2m1(code) * dec(sf) (bf16) that fc2's GEMM multiplies, so h never reaches
- * memory: the result equals the two layers run one after the other.  fc1 may carry
- * smoothing and a low-rank branch; fc2 may carry smoothing but no low-rank branch
- * (fc2->R must be 0: its x L1 needs whole rows of h).  Each layer's tensors are as
- * in qlinear_nvfp4 (weight [rows, cols/2], weight_scale [rows, cols/16], ...).
- * Workspace: qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, fc1->R) bytes (0 for
- * invalid sizes); its first 2 M H bytes hold fc2's expanded operand after the
- * call.  Errors: as qlinear_nvfp4 for either layer, and QPL_ERR_ARG for
- * fc2->R != 0.
+ * GELU runs in fc1's GEMM epilogue; fc2 quantizes h with its own smoothing, input
+ * scale and (fused with the quantize) low-rank down-projection, then runs its GEMM.
+ * The result equals the two layers called one after the other.  Either layer may
+ * carry smoothing and a low-rank branch; each layer's tensors are as in
+ * qlinear_nvfp4 (weight [rows, cols/2], weight_scale [rows, cols/16], ...).
+ * Workspace: qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, fc1->R, fc2->R) bytes (0
+ * for invalid sizes); its first 2 M H bytes hold fc2's expanded operand (the
+ * values e2m1(code) * dec(sf) of its quantized input, bf16) after the call, and
+ * the 2 M H bytes at offset qlinear_workspace_bytes(QPL_NVFP4, M, H, N, fc2->R)
+ * hold h.  Errors: as qlinear_nvfp4 for either layer.
  */
 typedef struct {
   const uint8_t* weight;        /* uint8 [rows, cols/2], two E2M1 codes per byte */
@@ -258,7 +257,7 @@ typedef struct {
   int64_t R;
 } qpl_nvfp4_layer;
 
-size_t qlinear_mlp_nvfp4_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1);
+size_t qlinear_mlp_nvfp4_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1, int64_t R2);
 qpl_status qlinear_mlp_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t H, int64_t N,
                              const qpl_nvfp4_layer* fc1, const qpl_nvfp4_layer* fc2,
                              uint16_t* y, void* ws, size_t ws_bytes, void* stream);

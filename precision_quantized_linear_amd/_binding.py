@@ -85,7 +85,7 @@ def load():
         fn.restype = ctypes.c_int
     lib.qlinear_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64, I64]
     lib.qlinear_workspace_bytes.restype = SZ
-    lib.qlinear_mlp_nvfp4_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+    lib.qlinear_mlp_nvfp4_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
     lib.qlinear_mlp_nvfp4_workspace_bytes.restype = SZ
     lib.qpl_nvfp4_global_scale.argtypes = [F]
     lib.qpl_nvfp4_global_scale.restype = F
@@ -277,8 +277,8 @@ def qlinear_int4(x, weight, weight_scale, lora_down=None, lora_up=None, y=None, 
     return out
 
 
-def qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1=0):
-    return int(load().qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1))
+def qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1=0, R2=0):
+    return int(load().qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1, R2))
 
 
 def _layer(d, rows, cols, name):
@@ -302,15 +302,15 @@ def _layer(d, rows, cols, name):
 
 def qlinear_mlp_nvfp4(x, fc1, fc2, y=None, workspace=None, stream=None):
     """y [M,N] bf16 = fc2(bf16(gelu(fc1(x)))) for nvfp4 layers fc1 [H,K] and fc2 [N,H]
-    given as dicts (see _layer); fc1's epilogue quantizes the hidden activation for fc2,
-    whose expanded operand is left in the first 2 M H bytes of the workspace."""
+    given as dicts (see _layer); GELU runs in fc1's epilogue.  After the call the first
+    2 M H bytes of the workspace hold fc2's expanded operand, and h follows fc2's part."""
     M, K = x.shape
     _expect(x, torch.bfloat16, (M, K), "x")
     H = fc1["weight"].shape[0]
     N = fc2["weight"].shape[0]
     l1, l2 = _layer(fc1, H, K, "fc1"), _layer(fc2, N, H, "fc2")
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
-    need = qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, l1.R)
+    need = qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, l1.R, l2.R)
     ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device) if workspace is None else workspace
     _check("qlinear_mlp_nvfp4", load().qlinear_mlp_nvfp4(_ptr(x), M, K, H, N, ctypes.byref(l1), ctypes.byref(l2),
                                                          _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),

@@ -38,7 +38,6 @@
 
 #include "qpl_dma.h"
 #include "qpl_internal.h"
-#include "qpl_nvfp4.h"
 
 namespace qpl {
 
@@ -169,12 +168,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // * EPI_GELU: the tanh form of GELU on each fp32 result before the bf16 rounding;
 // * EPI_QKV: the output row's three parts (columns [0, d), [d, 2d), [2d, 3d)) go to
 //   three tensors [heads, tokens, head_dim] at a token offset, the layout attention
-//   reads, instead of the row-major y;
-// * EPI_NEXT_NVFP4: the bf16 result is quantized for the next layer as its nvfp4
-//   quantizer would (its smoothing, then 16-column blocks under its input_scale)
-//   and written as the expanded values e2m1(code) * dec(sf), the operand the nvfp4
-//   GEMM multiplies, so that the next layer reads it without a quantize pass.
-constexpr int EPI_GELU = 1, EPI_QKV = 2, EPI_NEXT_NVFP4 = 4;
+//   reads, instead of the row-major y.
+constexpr int EPI_GELU = 1, EPI_QKV = 2;
 
 struct EpiArgs {
   uint16_t* qkv[3];  // EPI_QKV: q, k, v
@@ -182,11 +177,7 @@ struct EpiArgs {
   int64_t tokens;    // EPI_QKV: tokens per head
   int64_t off;       // EPI_QKV: token of output row 0
   int lg_hd;         // EPI_QKV: log2(head_dim)
-  const float* lam;  // EPI_NEXT_NVFP4: the next layer's smoothing factors [N], or null
-  float g;           // EPI_NEXT_NVFP4: the next layer's input_scale
-  float c6g, rc6g;   // EPI_NEXT_NVFP4: 6 g and RN(1 / (6 g))
 };
-
 // GELU, tanh form: v sigma(2u) with u = sqrt(2/pi) (v + 0.044715 v^3), since
 // (1 + tanh u) / 2 = 1 / (1 + exp(-2u)).  exp2 and the reciprocal run on the
 // transcendental unit; the exponent is t = -2 u log2(e) = v (C1 + C3 v^2).  Large
@@ -196,33 +187,6 @@ constexpr float GELU_C3 = -0x1.a5a7d0p-4f;  // GELU_C1 * 0.044715, -0.10294324
 __device__ __forceinline__ float gelu_tanh(float v) {
   const float t = v * __builtin_fmaf(GELU_C3, v * v, GELU_C1);
   return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
-}
-
-// EPI_NEXT_NVFP4 on eight consecutive bf16 results (four pairs) of one row: this
-// lane holds columns n .. n + 7 and lane l ^ 32 the other half of the 16-column
-// block; the block maximum is exchanged across the halves with one
-// V_PERMLANE32_SWAP (every lane of the wave takes part).  Returns the expanded
-// values in the same positions.
-__device__ __forceinline__ u32x4 next_nvfp4(const u32x4& v, int64_t n, int64_t N, const EpiArgs& e,
-                                            const float* tab_d, const float* tab_rd) {
-  uint32_t p[4] = {v.x, v.y, v.z, v.w};
-  if (e.lam && n < N) {
-    const f32x4 l0 = *reinterpret_cast<const f32x4*>(e.lam + n);
-    const f32x4 l1 = *reinterpret_cast<const f32x4*>(e.lam + n + 4);
-    p[0] = smooth_pair(p[0], l0[0], l0[1]);
-    p[1] = smooth_pair(p[1], l0[2], l0[3]);
-    p[2] = smooth_pair(p[2], l1[0], l1[1]);
-    p[3] = smooth_pair(p[3], l1[2], l1[3]);
-  }
-  const float own = block_absmax(p, 4);
-  const uint32_t ob = __float_as_uint(own);
-  const auto sw = __builtin_amdgcn_permlane32_swap(ob, ob, false, false);
-  // one of the two results is this lane's value, the other its partner's
-  const float bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  const Nvfp4Block s = nvfp4_scale(bmax, e.c6g, e.rc6g, tab_d, tab_rd);
-  uint32_t o[4];
-  expand_word(nvfp4_word<false>(p, s), s.dsf, o);
-  return u32x4{o[0], o[1], o[2], o[3]};
 }
 
 // Destination of output element (m, n): y[m, n], or under EPI_QKV element
@@ -254,8 +218,7 @@ __device__ __forceinline__ uint16_t* out_ptr(uint16_t* __restrict__ y, int64_t m
 template <int NJ, int NI = 4, int EPI = 0, class RowScale, class ColScale>
 __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
                                           int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
-                                          const ColScale& cs, const EpiArgs& e = EpiArgs{},
-                                          const float* tab_d = nullptr, const float* tab_rd = nullptr) {
+                                          const ColScale& cs, const EpiArgs& e = EpiArgs{}) {
   // interior: the wavefront's rows and columns all inside the matrix
   const bool fast = m0 + (wm + 1) * 32 * NJ <= M && n0 + (wn + 1) * 32 * NI <= N && (N & 7) == 0;
   // unrolled at compile time: with a heavy epilogue the body exceeds what the
@@ -286,9 +249,8 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
         }
         const auto r0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
         const auto r1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-        u32x4 v = u32x4{r0[0], r1[0], r0[1], r1[1]};
+        const u32x4 v = u32x4{r0[0], r1[0], r0[1], r1[1]};
         const int64_t n = n0 + wn * 32 * NI + i * 32 + (2 * gp + (lane >> 5)) * 8;
-        if constexpr ((EPI & EPI_NEXT_NVFP4) != 0) v = next_nvfp4(v, n, N, e, tab_d, tab_rd);
         // the segment's eight columns stay inside one head (head_dim >= 8, n % 8 == 0)
         uint16_t* dst = out_ptr<EPI>(y, m, n, N, e);
         if (fast) {
@@ -331,13 +293,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
                                                 const float* __restrict__ sb, float gscale,
                                                 uint16_t* __restrict__ Y, const EpiArgs& e) {
   constexpr int D = ROWCOL ? 10 : 8;  // loads per wave per slab
-  constexpr bool NEXT = (EPI & EPI_NEXT_NVFP4) != 0;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lsc[ROWCOL ? 3 * SCALE_BUF : 16];
-  // EPI_NEXT_NVFP4: the next layer's block-scale table (written here, read after
-  // the barriers of the first slabs)
-  __shared__ float tabs[NEXT ? 256 : 1];
-  if constexpr (NEXT) fill_scale_table(e.g, tabs, tabs + 128);
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wv >> 1, wn = wv & 1;
@@ -519,7 +476,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
     } else {
       st1 = store_tile<NJ, 4, EPI>(
           acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return gscale; },
-          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e, tabs, tabs + 128);
+          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e);
     }
     if (st1 == 0) st2 = st3 = 0;
   };
@@ -842,13 +799,6 @@ static int epi_kind(const Epilogue& ep, EpiArgs& e) {
     e.off = ep.off;
     e.lg_hd = ep.lg_hd;
   }
-  if (ep.next_nvfp4) {
-    k |= EPI_NEXT_NVFP4;
-    e.lam = ep.lam;
-    e.g = ep.g;
-    e.c6g = 6.0f * ep.g;
-    e.rc6g = 1.0f / e.c6g;
-  }
   return k;
 }
 
@@ -879,12 +829,10 @@ hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w
 template <bool LR>
 static hipError_t launch_nvfp4_epi(int kind, dim3 grid, hipStream_t stream, const GemmArgs& p, float gscale,
                                    uint16_t* y, const EpiArgs& e) {
-  constexpr int GN = EPI_GELU | EPI_NEXT_NVFP4;
   switch (kind) {
     case 0: hipLaunchKernelGGL((k_gemm_nvfp4<LR, 0>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
     case EPI_GELU: hipLaunchKernelGGL((k_gemm_nvfp4<LR, EPI_GELU>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
     case EPI_QKV: hipLaunchKernelGGL((k_gemm_nvfp4<LR, EPI_QKV>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
-    case GN: hipLaunchKernelGGL((k_gemm_nvfp4<LR, GN>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

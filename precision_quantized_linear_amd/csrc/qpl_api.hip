@@ -188,7 +188,7 @@ qpl_status epilogue_of(const qpl_epilogue* epi, int64_t M, int64_t N, const uint
 }
 
 qpl_kernel gemm_kind(const qpl::Epilogue& ep, qpl_kernel plain) {
-  return ep.gelu || ep.qkv[0] || ep.next_nvfp4 ? QPL_KERNEL_GEMM_EPILOGUE : plain;
+  return ep.gelu || ep.qkv[0] ? QPL_KERNEL_GEMM_EPILOGUE : plain;
 }
 
 qpl_status fp8r_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
@@ -401,28 +401,33 @@ QPL_EXPORT qpl_status qlinear_nvfp4_ex(const uint16_t* x, int64_t M, int64_t K, 
 
 namespace {
 
-// Fused MLP: fc1 with GELU, whose epilogue writes fc2's quantized operand h_e
-// (workspace part 0), then fc2.  Workspace: [h_e: 2 M H][fc1's nvfp4 layout for
-// (M, K, H, R1)][fc2's expanded weight: 2 N H], each part rounded up to 256 bytes.
+// GELU MLP: fc1 with the GELU epilogue writes h, then fc2 runs on h (its quantize,
+// fused with x L1 when it has a low-rank branch, then its GEMM).  Workspace:
+// [fc2's nvfp4 layout for (M, H, N, R2), whose first part is fc2's expanded
+// operand][h: 2 M H][fc1's nvfp4 layout for (M, K, H, R1)], each part rounded up
+// to 256 bytes.
 struct MlpLayout {
-  size_t he = 0, fc1 = 0, we2 = 0, total = 0;
-  Layout l1;
+  size_t h = 0, fc1 = 0, total = 0;
+  Layout l1, l2;
 };
 
-MlpLayout mlp_layout(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1) {
+MlpLayout mlp_layout(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1, int64_t R2) {
   MlpLayout L;
+  L.l2 = layout(QPL_NVFP4, M, H, N, R2);
   L.l1 = layout(QPL_NVFP4, M, K, H, R1);
-  L.fc1 = round256(size_t(2) * size_t(M) * size_t(H));
-  L.we2 = L.fc1 + L.l1.total;
-  L.total = L.we2 + round256(size_t(2) * size_t(N) * size_t(H));
+  L.h = L.l2.total;
+  L.fc1 = L.h + round256(size_t(2) * size_t(M) * size_t(H));
+  L.total = L.fc1 + L.l1.total;
   return L;
 }
 
 }  // namespace
 
-QPL_EXPORT size_t qlinear_mlp_nvfp4_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1) {
-  if (check_gemm_dims(M, K, H) != QPL_OK || check_gemm_dims(M, H, N) != QPL_OK || R1 < 0 || R1 > kMaxRank) return 0;
-  return mlp_layout(M, K, H, N, R1).total;
+QPL_EXPORT size_t qlinear_mlp_nvfp4_workspace_bytes(int64_t M, int64_t K, int64_t H, int64_t N, int64_t R1,
+                                                    int64_t R2) {
+  if (check_gemm_dims(M, K, H) != QPL_OK || check_gemm_dims(M, H, N) != QPL_OK) return 0;
+  if (R1 < 0 || R1 > kMaxRank || R2 < 0 || R2 > kMaxRank) return 0;
+  return mlp_layout(M, K, H, N, R1, R2).total;
 }
 
 QPL_EXPORT qpl_status qlinear_mlp_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t H, int64_t N,
@@ -436,36 +441,20 @@ QPL_EXPORT qpl_status qlinear_mlp_nvfp4(const uint16_t* x, int64_t M, int64_t K,
   if ((s = check_nvfp4_layer(fc2->weight, fc2->weight_scale, fc2->weight_scale_2, fc2->input_scale, fc2->smooth,
                              fc2->lora_down, fc2->lora_up, fc2->R)) != QPL_OK)
     return s;
-  // fc2's low-rank branch would need whole hidden rows, which no fc1 tile holds
-  if (fc2->R != 0) return QPL_ERR_ARG;
   if ((s = check_gemm_dims(M, K, H)) != QPL_OK || (s = check_gemm_dims(M, H, N)) != QPL_OK) return s;
-  const MlpLayout L = mlp_layout(M, K, H, N, fc1->R);
+  const MlpLayout L = mlp_layout(M, K, H, N, fc1->R, fc2->R);
   if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
   if ((s = check_device()) != QPL_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  uint16_t* he = reinterpret_cast<uint16_t*>(base);
-  uint8_t* b1 = base + L.fc1;
-  uint16_t* we2 = reinterpret_cast<uint16_t*>(base + L.we2);
-  const float g1 = fc1->input_scale * fc1->weight_scale_2;
-  qpl::LowRank lr;
-  if ((s = nvfp4_operands(x, M, K, H, fc1->weight, fc1->weight_scale, g1, fc1->input_scale, fc1->smooth,
-                          fc1->lora_down, fc1->lora_up, fc1->R, L.l1, b1, st, lr)) != QPL_OK)
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
+  qpl_epilogue gelu{};
+  gelu.act = QPL_ACT_GELU_TANH;
+  if ((s = nvfp4_linear(x, M, K, H, fc1->weight, fc1->weight_scale, fc1->weight_scale_2, fc1->input_scale,
+                        fc1->smooth, fc1->lora_down, fc1->lora_up, fc1->R, &gelu, h, base + L.fc1, L.l1.total,
+                        stream)) != QPL_OK)
     return s;
-  qpl::Epilogue ep;
-  ep.gelu = true;
-  ep.next_nvfp4 = true;
-  ep.lam = fc2->smooth;
-  ep.g = fc2->input_scale;
-  if ((s = launched(Timed(QPL_KERNEL_GEMM_EPILOGUE, st)(qpl::launch_gemm_nvfp4(
-           reinterpret_cast<const uint16_t*>(b1 + L.l1.off[0]), reinterpret_cast<const uint16_t*>(b1 + L.l1.off[1]),
-           g1, M, K, H, lr, ep, he, st)))) != QPL_OK)
-    return s;
-  if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(
-           qpl::launch_dequant_nvfp4(fc2->weight, fc2->weight_scale, 1.0f, N, H, we2, st)))) != QPL_OK)
-    return s;
-  return launched(Timed(QPL_KERNEL_GEMM_NVFP4, st)(qpl::launch_gemm_nvfp4(
-      he, we2, fc2->input_scale * fc2->weight_scale_2, M, H, N, qpl::LowRank{}, qpl::Epilogue{}, y, st)));
+  return nvfp4_linear(h, M, H, N, fc2->weight, fc2->weight_scale, fc2->weight_scale_2, fc2->input_scale,
+                      fc2->smooth, fc2->lora_down, fc2->lora_up, fc2->R, nullptr, y, base, L.l2.total, stream);
 }
 
 QPL_EXPORT qpl_status quant_weight_awq(const uint16_t* w, int64_t N, int64_t K, int64_t group, uint8_t* w_q,

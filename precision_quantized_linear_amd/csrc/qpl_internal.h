@@ -63,17 +63,11 @@ hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, 
 // gelu: the tanh form of GELU on the fp32 result before the bf16 rounding.
 // qkv: (all three set) the result's column parts [0, d), [d, 2d), [2d, 3d) go to
 // q, k, v, each [heads, tokens, 2^lg_hd] bf16, row m at token off + m; y unused.
-// next_nvfp4 (nvfp4 GEMM, with gelu): y receives the bf16 result quantized by the
-// nvfp4 rule under global scale g after smoothing by lam (nullable), as the expanded
-// values e2m1(code) * dec(sf); N % 16 == 0.
 struct Epilogue {
   bool gelu = false;
   uint16_t* qkv[3] = {nullptr, nullptr, nullptr};
   int64_t d = 0, tokens = 0, off = 0;
   int lg_hd = 0;
-  bool next_nvfp4 = false;
-  const float* lam = nullptr;
-  float g = 0.0f;
 };
 
 hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws,

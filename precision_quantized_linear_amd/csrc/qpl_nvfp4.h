@@ -1,6 +1,5 @@
-// The nvfp4 block rule on the device, shared by the quantizers and the GEMM
-// epilogue that quantizes a layer's output for the next layer (Diffusers guide
-// "BFL (fp8r / nvfp4)", intro bullet on nvfp4): per 16-element block
+// The nvfp4 block rule on the device (Diffusers guide "BFL (fp8r / nvfp4)", intro
+// bullet on nvfp4), used by the quantizers: per 16-element block
 // sf = E4M3(bmax / (6 g)), d = dec(sf) * g, codes E2M1(x / d) with correctly rounded
 // divisions, and the exact bf16 expansion e2m1(code) * dec(sf).
 #pragma once
@@ -81,19 +80,6 @@ __device__ __forceinline__ void expand_word(uint32_t w, float dsf, uint32_t* o) 
   o[1] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), dsf);
   o[2] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), dsf);
   o[3] = bf16_pair_of(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), dsf);
-}
-
-// The per-code table d = dec(sf) * g and RN(1 / d) for one global scale g, one
-// entry per thread for threads 0 .. 127 of the calling workgroup (the caller
-// synchronizes before reading it).  Matches the host's table bit for bit: the
-// decode is exact and both sides divide with IEEE rounding.
-__device__ __forceinline__ void fill_scale_table(float g, float* tab_d, float* tab_rd) {
-  const uint32_t c = threadIdx.x;
-  if (c < 128) {
-    const float d = c == 0x7Fu ? 0.0f : e4m3_decode(c) * g;
-    tab_d[c] = d;
-    tab_rd[c] = 1.0f / d;
-  }
 }
 
 }  // namespace qpl

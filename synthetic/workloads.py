@@ -50,7 +50,7 @@ WORKLOADS = {
     "awq_adanorm_zero": dict(c=6, scheme="w4a16", M=1, K=3072, N=18432, dist="normal", frac_out=0.0, mult=1.0, G=64),
     "awq_adanorm_single": dict(c=7, scheme="w4a16", M=1, K=3072, N=9216, dist="normal", frac_out=0.0, mult=1.0, G=64),
     # FLUX double-block feed-forward (3072 -> 4 x 3072 -> 3072) as SVDQuant W4A4 layers:
-    # fc1 [N, K] with the rank-32 branch, fc2 [N2, N] without one (w2)
+    # fc1 [N, K] and fc2 [N2, N] (w2, factors l1_2 [N, R], l2_2 [R, N2]), rank 32 each
     "svdq_mlp": dict(c=8, scheme="nvfp4", M=4608, K=3072, N=12288, N2=3072, dist="normal", frac_out=0.01,
                      mult=10.0, n_cal=8, R=32),
     # FLUX attention input projection: [W_q; W_k; W_v] for 24 heads of 128 over the
@@ -119,6 +119,8 @@ def make(name, M=None, K=None, N=None, N2=None):
         N2 = spec["N2"] if N2 is None else N2
         out["N2"] = N2
         out["w2"] = _normal(100 * c + 6, (N2, N), 0.02)
+        out["l1_2"] = _normal(100 * c + 7, (N, spec["R"]), 0.05)
+        out["l2_2"] = _normal(100 * c + 8, (spec["R"], N2), 0.05)
     return out
 
 

@@ -189,17 +189,18 @@ def layer(R=0, bad_scale=False, lora=False):
 def test_mlp_validation_and_workspace(lib):
     M, K, H, N = 4608, 3072, 12288, 3072
     r256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    fc1 = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, H)
-    assert qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N) == r256(2 * M * H) + fc1 + r256(2 * N * H)
-    fc1r = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, H, 32)
-    assert qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, 32) == r256(2 * M * H) + fc1r + r256(2 * N * H)
+    for R1, R2 in ((0, 0), (32, 0), (32, 32)):
+        fc1 = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, H, R1)
+        fc2 = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, H, N, R2)
+        assert qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1, R2) == fc2 + r256(2 * M * H) + fc1
     assert qpl.qlinear_mlp_nvfp4_workspace_bytes(4, 32, 24, 8) == 0   # H % 16 != 0
     assert qpl.qlinear_mlp_nvfp4_workspace_bytes(4, 32, 32, 8, 129) == 0
+    assert qpl.qlinear_mlp_nvfp4_workspace_bytes(4, 32, 32, 8, 0, 129) == 0
     ws = 1 << 30
     assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), None, D, A, ws, None) == NULL
     assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(bad_scale=True), D, A, ws, None) == ARG
-    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(R=4, lora=True), D, A, ws, None) == ARG
     assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(R=4), layer(), D, A, ws, None) == NULL
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(R=200, lora=True), D, A, ws, None) == SHAPE
     assert lib.qlinear_mlp_nvfp4(A, 4, 32, 24, 8, layer(), layer(), D, A, ws, None) == SHAPE
     assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(), D, A, 100, None) == WORKSPACE
     assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(), MIS, A, ws, None) == ALIGN
@@ -212,3 +213,5 @@ def test_epilogue_calls_reach_the_device_check(lib):
                                 None) == DEVICE
     assert lib.qlinear_fp8r_ex(A, 4, 32, 8, B, C, epi(act=1), D, A, ws, None) == DEVICE
     assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(), layer(), D, A, ws, None) == DEVICE
+    assert lib.qlinear_mlp_nvfp4(A, 4, 32, 32, 8, layer(R=4, lora=True), layer(R=4, lora=True), D, A, ws,
+                                 None) == DEVICE

@@ -9,12 +9,13 @@
   positions (gathered back, the GEMM acceptance test against the oracle), rows
   outside the written tokens stay untouched, and the values are bit-identical to
   the plain call's y.
-* fused GELU MLP (nvfp4): fc2's operand, left in the workspace, must be the nvfp4
-  quantization of some bf16 h inside the GELU interval (block by block; exact
-  where that quantization is unique); y must lie within the GEMM acceptance bound of
-  the oracle's fc2 on the oracle's own operand, widened by the largest effect the
-  non-unique codes can have; and y must be bit-identical to the two layers run as
-  separate calls.
+* GELU MLP (nvfp4): h (left in the workspace) inside the GELU interval as above;
+  fc2's operand, also left there, must be the nvfp4 quantization of some bf16 h in
+  that interval (block by block; exact where that quantization is unique); y must
+  lie within the GEMM acceptance bound of the oracle's fc2 on the oracle's own
+  operand, widened by the largest effect the non-unique codes (and, with fc2's
+  low-rank branch, the non-unique h) can have; and y must be bit-identical to the
+  two layers run as separate calls.
 """
 import math
 
@@ -243,14 +244,14 @@ def test_qkv_full_nvfp4():
     assert r["ok"], r
 
 
-# ---- fused GELU MLP -------------------------------------------------------------------
+# ---- GELU MLP -------------------------------------------------------------------------
 
-def mlp_case(M, K, H, N, lowrank, smooth1, smooth2, rows):
+def mlp_case(M, K, H, N, lr1, lr2, smooth1, smooth2, rows):
     d = make("svdq_mlp", M=M, K=K, N=H, N2=N)
     g1 = calibrate_input_scale(calibration_batches("svdq_mlp", M=M, K=K))
     lam1 = smooth_factors("svdq_mlp", K=K) if smooth1 else None
     lam2 = smooth_factors("svdq_mlp", K=H) if smooth2 else None
-    ref1, absum1, extra1, _ = nvfp4_pre(d, rows, g1, lam1, lowrank=lowrank)
+    ref1, absum1, extra1, _ = nvfp4_pre(d, rows, g1, lam1, lowrank=lr1)
     g_w1 = global_scale(amax_bf16(d["w"]))
     w1p, w1b = quant_nvfp4(d["w"], g_w1)
     h_nom = gelu_bf16_ref(ref1)
@@ -260,39 +261,53 @@ def mlp_case(M, K, H, N, lowrank, smooth1, smooth2, rows):
     w2p, w2b = quant_nvfp4(d["w2"], g_w2)
     fc1 = dict(weight=to_dev(w1p), weight_scale=to_dev(w1b), weight_scale_2=g_w1, input_scale=g1,
                smooth=None if lam1 is None else to_dev(lam1))
-    if lowrank:
+    if lr1:
         fc1.update(lora_down=to_dev_bf16(d["l1"]), lora_up=to_dev_bf16(d["l2"]))
     fc2 = dict(weight=to_dev(w2p), weight_scale=to_dev(w2b), weight_scale_2=g_w2, input_scale=g2,
                smooth=None if lam2 is None else to_dev(lam2))
+    if lr2:
+        fc2.update(lora_down=to_dev_bf16(d["l1_2"]), lora_up=to_dev_bf16(d["l2_2"]))
     x = to_dev_bf16(d["x"])
-    ws = torch.empty((qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, 32 if lowrank else 0),), dtype=torch.uint8,
-                     device="cuda")
+    R1, R2 = (32 if lr1 else 0), (32 if lr2 else 0)
+    ws = torch.empty((qpl.qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, R1, R2),), dtype=torch.uint8, device="cuda")
     y = qpl.qlinear_mlp_nvfp4(x, fc1, fc2, workspace=ws)
     # the same two layers as separate calls
     kw1 = {k: fc1[k] for k in ("lora_down", "lora_up") if k in fc1}
+    kw2 = {k: fc2[k] for k in ("lora_down", "lora_up") if k in fc2}
     h = qpl.qlinear_nvfp4(x, fc1["weight"], fc1["weight_scale"], g_w1, g1, smooth=fc1["smooth"], act="gelu_tanh",
                           **kw1)
-    y2 = qpl.qlinear_nvfp4(h, fc2["weight"], fc2["weight_scale"], g_w2, g2, smooth=fc2["smooth"])
+    y2 = qpl.qlinear_nvfp4(h, fc2["weight"], fc2["weight_scale"], g_w2, g2, smooth=fc2["smooth"], **kw2)
     torch.cuda.synchronize()
     r_rows = torch.from_numpy(rows).cuda()
     he = ws[:2 * M * H].view(torch.bfloat16).view(M, H)[r_rows]
+    h_off = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, H, N, R2)
+    hw = ws[h_off:h_off + 2 * M * H].view(torch.bfloat16).view(M, H)[r_rows]
     yb = bf16_bits(y)
     same = np.array_equal(yb, bf16_bits(y2))
 
+    # h: GELU of fc1 inside its interval
+    rh = check_gelu(bf16_bits(hw), ref1, absum1, K, extra1)
     # fc2's operand: an nvfp4 quantization of some h in the GELU interval
     lo, hi = gelu_interval(ref1, pre_activation_error(ref1, absum1, K, extra1))
-    lb, hb = bf16_interval(lo, hi)
-    if lam2 is not None:
-        lb, hb = smooth_interval(lb, hb, lam2)
+    hlb, hhb = bf16_interval(lo, hi)
+    lb, hb = (hlb, hhb) if lam2 is None else smooth_interval(hlb, hhb, lam2)
     rq = check_nvfp4_expanded(bf16_bits(he), lb, hb, g2)
 
     # y against the oracle's fc2 on its nominal operand, widened by the ambiguous codes
+    # (and, with fc2's low-rank branch, by the ambiguous smoothed h it reads)
     nominal, width = expanded_nominal_and_width(h_in, lb, hb, g2)
     gf = float(F32(g2))
     W2 = dequant_nvfp4(w2p, w2b, g_w2)
     ref2 = (nominal * gf) @ W2.T
     absum2 = np.abs(nominal * gf) @ np.abs(W2).T
     allow = (width * gf) @ np.abs(W2).T
+    if lr2:
+        ref2 = ref2 + lowrank_ref(h_in, d["l1_2"], d["l2_2"])
+        lr_abs = lowrank_abs(h_in, d["l1_2"], d["l2_2"])
+        dh = np.abs(f64(hb) - f64(lb))
+        l1a, l2a = np.abs(f64(d["l1_2"])), np.abs(f64(d["l2_2"]))
+        allow = allow + (dh @ l1a) @ l2a
+        absum2 = absum2 + lr_abs
     yv = f64(yb[rows])
     err = np.abs(yv - ref2)
     floor = gemm_gamma(H) * (absum2 + allow) + allow
@@ -303,30 +318,30 @@ def mlp_case(M, K, H, N, lowrank, smooth1, smooth2, rows):
     den = np.linalg.norm(ref2)
     frob = float(np.linalg.norm(yv - ref2) / den)
     frob_limit = 2e-3 + float(np.linalg.norm(allow) / den)
-    ok = rq["ok"] and same and fails == 0 and frob <= frob_limit
-    return dict(ok=ok, operand=rq, same_as_separate=same, fails=fails, worst=float(np.max(err / bound)), frob=frob,
-                frob_limit=frob_limit)
+    ok = rh["ok"] and rq["ok"] and same and fails == 0 and frob <= frob_limit
+    return dict(ok=ok, h=rh, operand=rq, same_as_separate=same, fails=fails, worst=float(np.max(err / bound)),
+                frob=frob, frob_limit=frob_limit)
 
 
 MLP_CASES = [
-    (300, 448, 512, 264, True, True, True),     # fc1 low rank, both smoothed, ragged M and N
-    (256, 512, 512, 256, False, False, False),  # plain BFL nvfp4 layers
-    (37, 320, 272, 72, True, False, True),      # H = 17 blocks of 16: a partial last tile of fc1
-    (1, 64, 16, 8, False, True, False),         # one hidden block
+    (300, 448, 512, 264, True, False, True, True),    # fc1 low rank, both smoothed, ragged M and N
+    (256, 512, 512, 256, False, False, False, False), # plain BFL nvfp4 layers
+    (37, 320, 272, 72, True, True, False, True),      # both low rank; H = 17 blocks of 16
+    (1, 64, 16, 8, False, True, True, False),         # one hidden block, fc2 low rank
 ]
 
 
-@pytest.mark.parametrize("M,K,H,N,lowrank,smooth1,smooth2", MLP_CASES)
-def test_mlp_nvfp4_small(M, K, H, N, lowrank, smooth1, smooth2):
-    say("mlp nvfp4", M, K, H, N, lowrank, smooth1, smooth2)
-    r = mlp_case(M, K, H, N, lowrank, smooth1, smooth2, np.arange(M))
+@pytest.mark.parametrize("M,K,H,N,lr1,lr2,smooth1,smooth2", MLP_CASES)
+def test_mlp_nvfp4_small(M, K, H, N, lr1, lr2, smooth1, smooth2):
+    say("mlp nvfp4", M, K, H, N, lr1, lr2, smooth1, smooth2)
+    r = mlp_case(M, K, H, N, lr1, lr2, smooth1, smooth2, np.arange(M))
     say(r)
     assert r["ok"], r
 
 
 def test_mlp_nvfp4_full():
-    # FLUX feed-forward 4608 x 3072 -> 12288 -> 3072, fc1 rank 32, both layers smoothed
+    # FLUX feed-forward 4608 x 3072 -> 12288 -> 3072, both layers rank 32 and smoothed
     say("mlp nvfp4 full", 4608, 3072, 12288, 3072)
-    r = mlp_case(4608, 3072, 12288, 3072, True, True, True, sample_rows(4608, n=32))
+    r = mlp_case(4608, 3072, 12288, 3072, True, True, True, True, sample_rows(4608, n=32))
     say(r)
     assert r["ok"], r
