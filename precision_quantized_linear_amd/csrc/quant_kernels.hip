@@ -760,20 +760,36 @@ __global__ __launch_bounds__(256) void k_dequant_fp8r(const uint8_t* __restrict_
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// nvfp4 weight to bf16, one 16-element block per lane: the hardware FP4 converter
+// gives the code values exactly.  G1 (weight_scale_2 = 1, the GEMM's expansion): the
+// products with dec(sf) are exact in bf16 (at most 6 significant bits), so they are
+// truncated into place.  Otherwise bf16_rne(fp32(e2m1 * dec(sf)) * g2).
+template <bool G1>
+__device__ __forceinline__ void dequant_block(uint32_t w0, uint32_t w1, float dsf, float g2, uint32_t* o) {
+  if constexpr (G1) {
+    expand_word(w0, dsf, o);
+    expand_word(w1, dsf, o + 4);
+  } else {
+    const uint32_t w[2] = {w0, w1};
+    auto out2 = [&](f32x2 v) { return pack_bf16((v[0] * dsf) * g2, (v[1] * dsf) * g2); };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      o[4 * h + 0] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 0));
+      o[4 * h + 1] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 1));
+      o[4 * h + 2] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 2));
+      o[4 * h + 3] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 3));
+    }
+  }
+}
+
+template <bool G1>
 __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict__ w, const uint8_t* __restrict__ wbs,
                                                        float g2, int64_t nblocks, uint16_t* __restrict__ out) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   const u32x2 c = reinterpret_cast<const u32x2*>(w)[b];
-  const float dsf = e4m3_decode(wbs[b]);
   uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t byte = ((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu;
-    const float lo = (e2m1_decode(byte & 0xFu) * dsf) * g2;
-    const float hi = (e2m1_decode(byte >> 4) * dsf) * g2;
-    o[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-  }
+  dequant_block<G1>(c.x, c.y, e4m3_decode(wbs[b]), g2, o);
   u32x4* dst = reinterpret_cast<u32x4*>(out + b * 16);
   dst[0] = u32x4{o[0], o[1], o[2], o[3]};
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
@@ -790,7 +806,11 @@ hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K, uint16_t* out,
                                 hipStream_t stream) {
   const int64_t nb = N * K / 16;
-  hipLaunchKernelGGL(k_dequant_nvfp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, w, wbs, g2, nb, out);
+  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  if (g2 == 1.0f)
+    hipLaunchKernelGGL(k_dequant_nvfp4<true>, grid, block, 0, stream, w, wbs, g2, nb, out);
+  else
+    hipLaunchKernelGGL(k_dequant_nvfp4<false>, grid, block, 0, stream, w, wbs, g2, nb, out);
   return hipGetLastError();
 }
 

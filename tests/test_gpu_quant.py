@@ -181,11 +181,13 @@ def test_dequant_weight_fp8r():
     assert np.array_equal(bf16_bits(out), dequant_weight_fp8r(wq, ws))
 
 
-def test_dequant_weight_nvfp4():
+@pytest.mark.parametrize("unit", [False, True])
+def test_dequant_weight_nvfp4(unit):
+    # an odd block count (129 x 65); weight_scale_2 = 1 takes the exact-product path
     w = make("nvfp4_dit", M=8, K=1040, N=129)["w"]
-    g = global_scale(amax_bf16(w))
+    g = np.float32(1.0) if unit else global_scale(amax_bf16(w))
     wp, wb = quant_nvfp4(w, g)
-    say("dequant_weight nvfp4", wp.shape)
+    say("dequant_weight nvfp4", wp.shape, "g = 1" if unit else "")
     out = qpl.dequant_weight(qpl.QPL_NVFP4, to_dev(wp), to_dev(wb), g, K=1040)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(out), dequant_weight_nvfp4(wp, wb, g))
