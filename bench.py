@@ -16,8 +16,8 @@ timing by the library's own quantizers, as a pre-quantized checkpoint would
 arrive.  Inputs are seeded synthetic data (see synthetic/workloads.py).
 
 The roofline object covers the dominant kernel (the nvfp4 GEMM at 4608 x 3072 x
-12288): its launches are timed with HIP events on the launch stream inside the
-timed region (the library's event timing, limited to that kernel).  `parts` and
+12288): its launches in every fifth step of the timed region are timed with HIP
+events on the launch stream (the library's event timing, limited to that kernel).  `parts` and
 `kernels` come from a second pass of the same steps with every launch timed.  The
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
 (rank 0, one GPU only).  `extras` times what lies beyond the step: the svdq linear
@@ -45,13 +45,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_4608x3072x1228
 TRAFFIC_SOURCES = ("precision_quantized_linear_amd/csrc/gemm_kernels.hip", "precision_quantized_linear_amd/csrc/qpl_dma.h",
                    "precision_quantized_linear_amd/csrc/qpl_device.h", "precision_quantized_linear_amd/csrc/qpl_nvfp4.h")
 COPY_PROBE_BYTES = 256 << 20
+EVENT_EVERY = 5  # timed steps per HIP-event sample of the dominant kernel
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # about 26 ms of the step: the clocks ramp over the first milliseconds of MFMA load
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="activation rows per linear in the CPU sample")
     ap.add_argument("--no-extras", action="store_true", help="skip the measurements beyond the step (extras)")
@@ -142,14 +144,15 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed region
-    # Only the dominant kernel carries HIP events here (an event pair costs a few
-    # microseconds of stream time); the per-kernel and per-linear breakdown comes
-    # from a second pass below with every launch bracketed.
+    # Only the dominant kernel carries HIP events here, and only in every
+    # EVENT_EVERY-th step: an event pair holds the stream for about 6 us on each side
+    # of the launch.  The per-kernel and per-linear breakdown comes from a second
+    # pass below with every launch bracketed.
     qpl.timing_collect()  # drop anything recorded so far
-    qpl.timing_select(["gemm_nvfp4"])
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        qpl.timing_select(["gemm_nvfp4"] if i % EVENT_EVERY == 0 else [])
         for k in order:
             run(k)
     torch.cuda.synchronize()
@@ -199,7 +202,7 @@ def main():
     traffic = measured_traffic()
     roofline = {"kernel": "gemm_nvfp4 (bf16 MFMA, 4608x3072x12288)", "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                "traffic": traffic, "avg_us": round(avg_s * 1e6, 2),
+                "traffic": traffic, "avg_us": round(avg_s * 1e6, 2), "event_samples": n_g,
                 "frac_of_fp4_peak": round(achieved / PEAK_TFLOPS["fp4"], 4)}
     nq, tq = kern["quant_fp8_row"]
     qbytes = 3.0 * lin["fp8r"]["M"] * lin["fp8r"]["K"] + 4.0 * lin["fp8r"]["M"]
