@@ -1,4 +1,6 @@
-"""CPU oracle for the BFL fp8r / nvfp4 quantized linear.
+"""CPU oracle for the quantized linear: BFL fp8r / nvfp4, the SVDQuant W4A4 layer
+(NVFP4 and INT4 variants), the weight-only 4-bit layer and the model-specific
+epilogues.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this package:
 only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -17,10 +19,16 @@ What it computes, and the page each part follows (all pages are the Diffusers
                 Inference to Diffusers", section "Background: SVDQuant and
                 Nunchaku"), the dequantize-to-compute_dtype fallback (guide,
                 "Kernels" section, last paragraph) and the GEMM acceptance test.
+* ``awq``       the weight-only 4-bit (awq_w4a16) format and layer (Nunchaku post,
+                "Introducing Nunchaku Lite", layer list).
+* ``int4``      the INT4 variant of svdq_w4a4 (same post and section).
+* ``epilogue``  GELU (tanh form), the GELU MLP and the fused QKV scatter (same post,
+                "Introducing Nunchaku Lite", first paragraph), with the interval
+                bounds that check outputs passing through GELU and requantization.
 
 Plain numpy throughout: float32 array arithmetic for the quantizers (every
 operation IEEE binary32 round-to-nearest-even, division correctly rounded, no
 fused multiply-add, no denormal flush) and float64 for the references.
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*.py``.
 """
-from . import formats, quant, reference  # noqa: F401
+from . import awq, epilogue, formats, int4, quant, reference  # noqa: F401
