@@ -20,7 +20,8 @@ The roofline object covers the dominant kernel (the nvfp4 GEMM at 4608 x 3072 x
 events on the launch stream (the library's event timing, limited to that kernel).  `parts` and
 `kernels` come from a second pass of the same steps with every launch timed.  The
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
-(rank 0, one GPU only).  `extras` times what lies beyond the step: the svdq linear
+(rank 0, one GPU only).  `cold` times the same step with its tensors rotated over three
+copies (working set above the 256 MB last-level cache).  `extras` times what lies beyond the step: the svdq linear
 with SVDQuant smoothing factors, the INT4 variant of svdq_w4a4 at the DiT shapes,
 the weight-only 4-bit (awq_w4a16) GEMV at the FLUX modulation shapes, and the
 model-specific epilogues: GELU on the nvfp4 linear, the GELU MLP against the same
@@ -208,6 +209,7 @@ def main():
     qbytes = 3.0 * lin["fp8r"]["M"] * lin["fp8r"]["K"] + 4.0 * lin["fp8r"]["M"]
     quant_gbs = qbytes / (tq / nq * 1e-3) / 1e9
 
+    cold = measure_cold(args, qpl, torch, lin, order, total_flops)
     extras = None if args.no_extras else measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors)
 
     # ---------------------------------------------------------------- CPU oracle baseline
@@ -226,10 +228,45 @@ def main():
         "parts": parts,
         "kernels": kernels,
         "quant_fp8_row_gbs": round(quant_gbs, 1),
+        "cold": cold,
         "extras": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_cold(args, qpl, torch, lin, order, total_flops, sets=3):
+    """The step with its inputs, weights, workspaces and outputs rotated over `sets`
+    copies, so that the working set exceeds the 256 MB MALL and each step finds its
+    operands in HBM rather than in the last-level cache."""
+    keys = ("x", "wq", "ws", "wbs", "l1", "l2", "y", "ws_buf")
+    copies = [{k: e for k, e in lin.items()}]
+    for _ in range(sets - 1):
+        copies.append({k: {f: (v.clone() if f in keys and torch.is_tensor(v) else v) for f, v in e.items()}
+                       for k, e in lin.items()})
+    nbytes = sum(v.numel() * v.element_size() for e in copies[0].values() for f, v in e.items()
+                 if f in keys and torch.is_tensor(v))
+
+    def run(e, key):
+        if key == "fp8r":
+            qpl.qlinear_fp8r(e["x"], e["wq"], e["ws"], y=e["y"], workspace=e["ws_buf"])
+        else:
+            kw = dict(lora_down=e["l1"], lora_up=e["l2"]) if e["R"] else {}
+            qpl.qlinear_nvfp4(e["x"], e["wq"], e["wbs"], e["g_w"], e["g_in"], y=e["y"], workspace=e["ws_buf"], **kw)
+
+    for i in range(args.warmup):
+        for k in order:
+            run(copies[i % sets][k], k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for k in order:
+            run(copies[i % sets][k], k)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del copies
+    return {"ms_per_step": round(ms, 4), "value": round(total_flops / (ms * 1e-3) / 1e12, 2), "sets": sets,
+            "working_set_mb": round(sets * nbytes / 1e6, 1)}
 
 
 def measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors):
