@@ -178,26 +178,55 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict_
 
 // Same quantization; each quantized value e2m1(code) * dec(sf) is written as bf16.
 // The product has at most 6 significant bits, so the bf16 value is exact.
+//
+// Layout: the tensor is a flat array of 16-byte vectors (eight bf16); vector j is
+// half j % 2 of block j / 2, so lanes l and l ^ 1 hold one block and every load and
+// store instruction of a wavefront covers 1 KB of consecutive bytes.  The block's
+// largest magnitude meets across the lane pair through DPP (quad_perm 1,0,3,2).  A
+// workgroup takes EXPAND_U runs of 256 consecutive vectors and issues all its loads
+// before it fills the scale table, so the table's latency overlaps theirs.  Stores
+// are plain: the GEMM reads this output next, and streaming (nontemporal) stores
+// made that GEMM measurably slower.
+constexpr int EXPAND_U = 4;
 
 template <bool SMOOTH>
-__global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __restrict__ x, int64_t nblocks,
+__global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __restrict__ x, int64_t nvec,
                                                             float c6g, float rc6g, Nvfp4ScaleTable tab,
-                                                            const float* __restrict__ lam, int64_t kb,
+                                                            const float* __restrict__ lam, int64_t kv,
                                                             uint16_t* __restrict__ xe) {
   __shared__ float tab_d[128], tab_rd[128];
+  const int64_t base = (int64_t)blockIdx.x * 256 * EXPAND_U + threadIdx.x;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x4 v[EXPAND_U];
+#pragma unroll
+  for (int u = 0; u < EXPAND_U; ++u) {
+    const int64_t j = base + 256 * u;
+    v[u] = j < nvec ? __builtin_nontemporal_load(xv + j) : u32x4{0u, 0u, 0u, 0u};
+  }
   load_scale_table(tab, tab_d, tab_rd);
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  uint32_t p[8];
-  load_block(x, b, p);
-  smooth_block<SMOOTH>(p, lam, b, kb);
-  const Nvfp4Block s = nvfp4_scale(block_absmax(p, 8), c6g, rc6g, tab_d, tab_rd);
-  uint32_t o[8];
-  expand_word(nvfp4_word<false>(p, s), s.dsf, o);
-  expand_word(nvfp4_word<false>(p + 4, s), s.dsf, o + 4);
-  u32x4* dst = reinterpret_cast<u32x4*>(xe + b * 16);
-  dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-  dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+#pragma unroll
+  for (int u = 0; u < EXPAND_U; ++u) {
+    // nvec is even, so both lanes of a pair are in range or neither is, and every
+    // lane takes part in the DPP exchange
+    const int64_t j = base + 256 * u;
+    uint32_t p[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    if constexpr (SMOOTH) {
+      if (j < nvec) {
+        const f32x4* l = reinterpret_cast<const f32x4*>(lam + (j % kv) * 8);
+        const f32x4 a = l[0], b = l[1];
+        p[0] = smooth_pair(p[0], a[0], a[1]);
+        p[1] = smooth_pair(p[1], a[2], a[3]);
+        p[2] = smooth_pair(p[2], b[0], b[1]);
+        p[3] = smooth_pair(p[3], b[2], b[3]);
+      }
+    }
+    uint32_t m = absmax_acc(absmax_acc(absmax_acc(absmax_acc(0u, p[0]), p[1]), p[2]), p[3]);
+    m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    const Nvfp4Block s = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
+    uint32_t o[4];
+    expand_word(nvfp4_word<false>(p, s), s.dsf, o);
+    if (j < nvec) reinterpret_cast<u32x4*>(xe)[j] = u32x4{o[0], o[1], o[2], o[3]};
+  }
 }
 
 // nvfp4 quantize-and-expand fused with the SVDQuant low-rank down-projection
@@ -626,13 +655,14 @@ hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, fl
                                      uint16_t* xe, hipStream_t stream) {
   const int64_t nb = M * (K / 16);
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  const int64_t nvec = 2 * nb;
+  const dim3 grid((unsigned)((nvec + 256 * EXPAND_U - 1) / (256 * EXPAND_U))), block(256);
   if (lam)
-    hipLaunchKernelGGL(k_quant_nvfp4_expand<true>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
-                       lam, K / 16, xe);
+    hipLaunchKernelGGL(k_quant_nvfp4_expand<true>, grid, block, 0, stream, x, nvec, c6g, rc6g,
+                       nvfp4_scale_table(g), lam, K / 8, xe);
   else
-    hipLaunchKernelGGL(k_quant_nvfp4_expand<false>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
-                       lam, K / 16, xe);
+    hipLaunchKernelGGL(k_quant_nvfp4_expand<false>, grid, block, 0, stream, x, nvec, c6g, rc6g,
+                       nvfp4_scale_table(g), lam, K / 8, xe);
   return hipGetLastError();
 }
 
@@ -760,39 +790,48 @@ __global__ __launch_bounds__(256) void k_dequant_fp8r(const uint8_t* __restrict_
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
-// nvfp4 weight to bf16, one 16-element block per lane: the hardware FP4 converter
-// gives the code values exactly.  G1 (weight_scale_2 = 1, the GEMM's expansion): the
-// products with dec(sf) are exact in bf16 (at most 6 significant bits), so they are
-// truncated into place.  Otherwise bf16_rne(fp32(e2m1 * dec(sf)) * g2).
+// nvfp4 weight to bf16.  Output vector j (eight bf16) is half j % 2 of block j / 2:
+// one dword of packed codes in, one 16-byte vector out per lane and step, so loads
+// and stores of a wavefront are consecutive; DEQUANT_U steps per lane, loads first.
+// The hardware FP4 converter gives the code values exactly.  G1 (weight_scale_2 = 1,
+// the GEMM's expansion): the products with dec(sf) are exact in bf16 (at most 6
+// significant bits), so they are truncated into place.  Otherwise
+// bf16_rne(fp32(e2m1 * dec(sf)) * g2).
+constexpr int DEQUANT_U = 4;
+
 template <bool G1>
-__device__ __forceinline__ void dequant_block(uint32_t w0, uint32_t w1, float dsf, float g2, uint32_t* o) {
+__device__ __forceinline__ void dequant_half(uint32_t w, float dsf, float g2, uint32_t* o) {
   if constexpr (G1) {
-    expand_word(w0, dsf, o);
-    expand_word(w1, dsf, o + 4);
+    expand_word(w, dsf, o);
   } else {
-    const uint32_t w[2] = {w0, w1};
     auto out2 = [&](f32x2 v) { return pack_bf16((v[0] * dsf) * g2, (v[1] * dsf) * g2); };
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      o[4 * h + 0] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 0));
-      o[4 * h + 1] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 1));
-      o[4 * h + 2] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 2));
-      o[4 * h + 3] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 3));
-    }
+    o[0] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0));
+    o[1] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1));
+    o[2] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2));
+    o[3] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3));
   }
 }
 
 template <bool G1>
 __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict__ w, const uint8_t* __restrict__ wbs,
-                                                       float g2, int64_t nblocks, uint16_t* __restrict__ out) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  const u32x2 c = reinterpret_cast<const u32x2*>(w)[b];
-  uint32_t o[8];
-  dequant_block<G1>(c.x, c.y, e4m3_decode(wbs[b]), g2, o);
-  u32x4* dst = reinterpret_cast<u32x4*>(out + b * 16);
-  dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-  dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+                                                       float g2, int64_t nvec, uint16_t* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * 256 * DEQUANT_U + threadIdx.x;
+  uint32_t c[DEQUANT_U], sc[DEQUANT_U];
+#pragma unroll
+  for (int u = 0; u < DEQUANT_U; ++u) {
+    const int64_t j = base + 256 * u;
+    c[u] = j < nvec ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(w) + j) : 0u;
+    sc[u] = j < nvec ? wbs[j >> 1] : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < DEQUANT_U; ++u) {
+    const int64_t j = base + 256 * u;
+    if (j < nvec) {
+      uint32_t o[4];
+      dequant_half<G1>(c[u], e4m3_decode(sc[u]), g2, o);
+      reinterpret_cast<u32x4*>(out)[j] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
 }
 
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
@@ -805,12 +844,12 @@ hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int
 
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K, uint16_t* out,
                                 hipStream_t stream) {
-  const int64_t nb = N * K / 16;
-  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  const int64_t nvec = N * K / 8;
+  const dim3 grid((unsigned)((nvec + 256 * DEQUANT_U - 1) / (256 * DEQUANT_U))), block(256);
   if (g2 == 1.0f)
-    hipLaunchKernelGGL(k_dequant_nvfp4<true>, grid, block, 0, stream, w, wbs, g2, nb, out);
+    hipLaunchKernelGGL(k_dequant_nvfp4<true>, grid, block, 0, stream, w, wbs, g2, nvec, out);
   else
-    hipLaunchKernelGGL(k_dequant_nvfp4<false>, grid, block, 0, stream, w, wbs, g2, nb, out);
+    hipLaunchKernelGGL(k_dequant_nvfp4<false>, grid, block, 0, stream, w, wbs, g2, nvec, out);
   return hipGetLastError();
 }
 
