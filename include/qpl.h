@@ -117,7 +117,12 @@ qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N,
  *   lora_up         bf16 [R,N] (L2) or NULL when R == 0
  *   R               rank, 0..128
  *   y               bf16 [M,N]          out
- *   ws, ws_bytes    scratch of at least qlinear_workspace_bytes(QPL_NVFP4, M, K, N, R)
+ *   ws, ws_bytes    scratch of at least qlinear_workspace_bytes(QPL_NVFP4, M, K, N, R);
+ *                   after the call its first 2 M K bytes hold the expanded activation
+ *                   (bf16 [M,K], the values e2m1(code) * dec(sf) of quant_act_nvfp4's
+ *                   output, exact; a zero may lose its sign) and the 2 N K bytes from
+ *                   offset 256 * ceil(2 M K / 256) the expanded weight (bf16 [N,K],
+ *                   e2m1(code) * dec(sf), exact)
  */
 qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                          const uint8_t* weight, const uint8_t* weight_scale,

@@ -6,10 +6,10 @@ import torch
 
 import precision_quantized_linear_amd as qpl
 from helpers import adversarial_rows, bf16_bits, host, to_dev, to_dev_bf16
-from oracle.formats import bf16_bits_to_f32
+from oracle.formats import bf16_bits_to_f32, f32_to_bf16_bits
 from oracle.quant import (amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4,
                           smooth_bf16)
-from oracle.reference import dequant_weight_fp8r, dequant_weight_nvfp4
+from oracle.reference import dequant_nvfp4, dequant_weight_fp8r, dequant_weight_nvfp4
 from synthetic import bf16_round, calibration_batches, make, smooth_factors
 
 pytestmark = pytest.mark.gpu
@@ -209,3 +209,76 @@ def test_quant_deterministic():
     a = [host(t) for t in qpl.quant_act_nvfp4(x, 0.01)]
     b = [host(t) for t in qpl.quant_act_nvfp4(x, 0.01)]
     assert all(np.array_equal(p, q) for p, q in zip(a, b))
+
+
+# ---- the GEMM's operands: bf16 expansions of the quantized activation and weight ----
+
+def expanded_bits(packed, block_scale):
+    """bf16 bits of e2m1(code) * dec(sf): exact (at most 6 significant bits)."""
+    return f32_to_bf16_bits(dequant_nvfp4(packed, block_scale, 1.0).astype(np.float32))
+
+
+def unsigned_zero(b):
+    b = b.copy()
+    b[b == 0x8000] = 0
+    return b
+
+
+def run_expansions(x_bits, g_in, wq, wb, lam=None):
+    M, K = x_bits.shape
+    N = wq.shape[0]
+    ws = torch.empty((qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N, 0),), dtype=torch.uint8, device="cuda")
+    qpl.qlinear_nvfp4(to_dev_bf16(x_bits), to_dev(wq), to_dev(wb), 1.0, g_in, workspace=ws,
+                      smooth=None if lam is None else to_dev(lam))
+    torch.cuda.synchronize()
+    w_off = (2 * M * K + 255) // 256 * 256
+    xe = bf16_bits(ws[:2 * M * K].view(torch.bfloat16))
+    we = bf16_bits(ws[w_off:w_off + 2 * N * K].view(torch.bfloat16))
+    return xe.reshape(M, K), we.reshape(N, K)
+
+
+def assert_expanded_equal(x_bits, g_in, wq, wb, lam=None):
+    xe, we = run_expansions(x_bits, g_in, wq, wb, lam)
+    xin = x_bits if lam is None else smooth_bf16(x_bits, lam)
+    cq, cs = quant_nvfp4(xin, g_in)
+    ref_x = unsigned_zero(expanded_bits(cq, cs))
+    bad = np.argwhere(unsigned_zero(xe) != ref_x)
+    assert bad.size == 0, f"{len(bad)} expanded activations differ, first at {bad[:3].tolist()}"
+    bad = np.argwhere(we != expanded_bits(wq, wb))
+    assert bad.size == 0, f"{len(bad)} expanded weights differ, first at {bad[:3].tolist()}"
+
+
+def random_weight(N, K, seed):
+    """Every code byte and every finite block-scale code (0..126), uniformly."""
+    rng = np.random.default_rng(seed)
+    return (rng.integers(0, 256, (N, K // 2)).astype(np.uint8),
+            rng.integers(0, 127, (N, K // 16)).astype(np.uint8))
+
+
+@pytest.mark.parametrize("name,M,K,N,smoothed", [
+    ("nvfp4_dit", None, None, 40, False),     # 4608 x 3072 activation, full size
+    ("svdq_w4a4", 300, 400, 48, False),       # ragged: 7500 vectors, a partial last workgroup
+    ("svdq_w4a4", 37, 272, 33, True),         # smoothed, odd rows
+    ("nvfp4_dit", 1, 16, 1, False),           # one block
+])
+def test_qlinear_nvfp4_expanded_operands(name, M, K, N, smoothed):
+    d = make(name, M=M, K=K)
+    K = d["K"]
+    lam = smooth_factors("svdq_w4a4", K=K) if smoothed else None
+    batches = calibration_batches(name, M=64 if M is None else M, K=K)
+    if lam is not None:
+        batches = (smooth_bf16(b, lam) for b in batches)
+    g = calibrate_input_scale(batches)
+    wq, wb = random_weight(N, K, seed=K + N)
+    say("qlinear_nvfp4 expanded operands", name, d["x"].shape, N, "smoothed" if smoothed else "", g)
+    assert_expanded_equal(d["x"], g, wq, wb, lam)
+
+
+@pytest.mark.parametrize("g", [1e-30, 1e-4, 0.25, 1e6, 5e37])
+def test_qlinear_nvfp4_expanded_adversarial(g):
+    # block scales saturated at 448 (small g) or underflowed to 0 (huge g), signed
+    # zeros, subnormal inputs
+    x = adversarial_rows(256, seed=7)
+    wq, wb = random_weight(24, 256, seed=8)
+    say("qlinear_nvfp4 expanded operands, adversarial", x.shape, g)
+    assert_expanded_equal(x, np.float32(g), wq, wb)
