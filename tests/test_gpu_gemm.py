@@ -147,15 +147,17 @@ def test_qlinear_nvfp4_full(name):
 
 @pytest.mark.parametrize("scheme,M,N", [("fp8r", 4608, 12288), ("nvfp4", 4608, 12288), ("fp8r", 4500, 12200),
                                          ("nvfp4", 4400, 12288), ("svdq", 4500, 12288), ("fp8r", 4608, 16384),
-                                         ("nvfp4", 4500, 16384), ("fp8r", 4608, 16640)])
+                                         ("nvfp4", 4500, 16384), ("fp8r", 4608, 16640), ("fp8r", 4500, 12250),
+                                         ("nvfp4", 4600, 12250), ("nvfp4", 4608, 3072)])
 def test_last_round_tiles(scheme, M, N):
     # 18 x 48 = 864 tiles of 256 x 256 over 256 persistent workgroups: the 96
     # tiles left for a fourth round (tile rows 16 and 17) are computed as 192 half
     # tiles of 128 x 256.  Checked: those rows and the band above them, every
     # column, at a short K.  M = 4500 leaves 20 rows in the second half of the
-    # last tile row, M = 4400 none; N = 12200 is ragged.  18 x 64 = 1152 tiles
+    # last tile row, M = 4400 none, M = 4600 rows in both halves; N = 12200 and
+    # 12250 are ragged (12250: N % 8 = 2, element stores).  18 x 64 = 1152 tiles
     # leave 128 (every workgroup takes a half tile); 18 x 65 = 1170 leave 146,
-    # which are computed whole.
+    # which are computed whole; 18 x 12 = 216 fill one round.
     K = 256
     rows = np.arange(3840, M)
     if scheme == "fp8r":
