@@ -314,10 +314,11 @@ typedef enum {
   QPL_KERNEL_GEMM_FP8R = 3,
   QPL_KERNEL_GEMM_NVFP4 = 4,
   QPL_KERNEL_GEMM_NVFP4_LOWRANK = 5, /* nvfp4 GEMM with the low-rank epilogue */
-  QPL_KERNEL_LOWRANK_PREP = 6,      /* low-rank factor transposes */
+  QPL_KERNEL_LOWRANK_PREP = 6,      /* low-rank factor transposes (qlinear_int4) */
   QPL_KERNEL_DEQUANT = 7,
   QPL_KERNEL_AMAX = 8,
-  QPL_KERNEL_WEIGHT_BF16 = 9,       /* nvfp4 weight expansion inside qlinear_nvfp4 */
+  QPL_KERNEL_WEIGHT_BF16 = 9,       /* nvfp4 weight expansion inside qlinear_nvfp4; with R > 0 the same
+                                       launch writes the low-rank factor layouts */
   QPL_KERNEL_QUANT_NVFP4_LOWRANK = 10, /* nvfp4 quantize fused with x L1 (qlinear_nvfp4, R > 0) */
   QPL_KERNEL_QUANT_W4G = 11,        /* quant_weight_awq */
   QPL_KERNEL_GEMV_W4A16 = 12,       /* qlinear_awq_w4a16 */
@@ -325,7 +326,7 @@ typedef enum {
   QPL_KERNEL_INT4_EXPAND = 14,      /* INT4 weight codes -> E4M3 bytes inside qlinear_int4 */
   QPL_KERNEL_GEMM_INT4 = 15,
   QPL_KERNEL_QUANT_INT4_LOWRANK = 16, /* INT4 quantize fused with x L1 (qlinear_int4, R > 0) */
-  QPL_KERNEL_GEMM_EPILOGUE = 17,    /* any GEMM with a GELU, QKV or next-layer epilogue (the *_ex calls, fc1 of
+  QPL_KERNEL_GEMM_EPILOGUE = 17,    /* any GEMM with a GELU or QKV epilogue (the *_ex calls, fc1 of
                                        qlinear_mlp_nvfp4) */
   QPL_KERNEL_COUNT = 18
 } qpl_kernel;

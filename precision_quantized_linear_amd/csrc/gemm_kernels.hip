@@ -742,22 +742,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   QPL_WAIT_LGKM0();
 }
 
-// l1t[r][k] = L1[k][r] (zero for r >= R); l2t[n][c] = L2[c mod rpad][n] (zero past R).
-__global__ __launch_bounds__(256) void k_lowrank_transpose(const uint16_t* __restrict__ l1,
-                                                           const uint16_t* __restrict__ l2, int64_t K, int64_t N,
-                                                           int64_t R, int64_t rpad, int64_t kl,
-                                                           uint16_t* __restrict__ l1t, uint16_t* __restrict__ l2t) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n1 = rpad * K, n2 = N * kl;
-  if (i < n1) {
-    const int64_t r = i / K, k = i % K;
-    l1t[i] = r < R ? l1[k * R + r] : (uint16_t)0;
-  } else if (i < n1 + n2) {
-    const int64_t j = i - n1, n = j / kl, c = (j % kl) % rpad;
-    l2t[j] = c < R ? l2[c * N + n] : (uint16_t)0;
-  }
-}
-
 }  // namespace
 
 // Persistent workgroups: one per CU while every slab stream is at least NST
@@ -897,15 +881,6 @@ hipError_t launch_gemm_int4(const uint8_t* x8, const float* xs, const uint8_t* w
   const dim3 grid((unsigned)p.nwg);
   return lr.kl > 0 ? launch_int4_epi<true>(kind, grid, stream, p, xs, ws, y, e)
                    : launch_int4_epi<false>(kind, grid, stream, p, xs, ws, y, e);
-}
-
-hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,
-                               uint16_t* l1t, uint16_t* l2t, hipStream_t stream) {
-  const int64_t rpad = kl / 2;
-  const int64_t ntr = rpad * K + N * kl;
-  hipLaunchKernelGGL(k_lowrank_transpose, dim3((unsigned)((ntr + 255) / 256)), dim3(256), 0, stream, l1, l2, K, N, R,
-                     rpad, kl, l1t, l2t);
-  return hipGetLastError();
 }
 
 }  // namespace qpl

@@ -243,24 +243,25 @@ qpl_status nvfp4_operands(const uint16_t* x, int64_t M, int64_t K, int64_t N, co
   uint16_t* we = reinterpret_cast<uint16_t*>(base + L.off[1]);
   lr = qpl::LowRank{};
   if (R > 0) {
-    // SVDQuant branch: factor layouts, then the activation quantize fused with T = x L1
+    // SVDQuant branch: the weight expansion, which also writes the factor layouts,
+    // then the activation quantize fused with T = x L1 (it reads L1^T)
     const int64_t kl = 2 * rank_pad(R);
     uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[2]);
     uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[3]);
     uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
-    if ((s = launched(Timed(QPL_KERNEL_LOWRANK_PREP, st)(
-             qpl::launch_lowrank_prep(lora_down, lora_up, K, N, R, kl, l1t, l2t, st)))) != QPL_OK)
-      return s;
-    if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
-             qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, smooth, l1t, kl, gscale, xe, t, st)))) != QPL_OK)
+    const qpl::LowRankPrep prep{lora_down, lora_up, K, N, R, kl / 2, kl, l1t, l2t};
+    if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(
+             qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st, &prep)))) != QPL_OK)
       return s;
     lr.t = t;
     lr.l2t = l2t;
     lr.kl = kl;
-  } else if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(
-                  qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, smooth, xe, st)))) != QPL_OK) {
-    return s;
+    return launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
+        qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, smooth, l1t, kl, gscale, xe, t, st)));
   }
+  if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(
+           qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, smooth, xe, st)))) != QPL_OK)
+    return s;
   // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue
   return launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st)));
 }

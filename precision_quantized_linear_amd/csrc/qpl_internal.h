@@ -56,8 +56,18 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, int64_t M, int64_t K, int64_t N,
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
                                hipStream_t stream);
+// Factor layouts of the low-rank branch (see launch_lowrank_prep): L1 [K, R] and
+// L2 [R, N] bf16 in; l1t [rpad, K] and l2t [N, kl] out, rpad = kl / 2.
+struct LowRankPrep {
+  const uint16_t* l1 = nullptr;
+  const uint16_t* l2 = nullptr;
+  int64_t K = 0, N = 0, R = 0, rpad = 0, kl = 0;
+  uint16_t* l1t = nullptr;
+  uint16_t* l2t = nullptr;
+};
+// lr: also write those layouts, in the same launch.
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K,
-                                uint16_t* out, hipStream_t stream);
+                                uint16_t* out, hipStream_t stream, const LowRankPrep* lr = nullptr);
 
 // What a GEMM's epilogue writes (default: y = bf16 result, row-major [M, N]).
 // gelu: the tanh form of GELU on the fp32 result before the bf16 rounding.

@@ -812,10 +812,38 @@ __device__ __forceinline__ void dequant_half(uint32_t w, float dsf, float g2, ui
   }
 }
 
-template <bool G1>
+// Factor layouts of the SVDQuant low-rank branch, one element per thread:
+// l1t[r][k] = L1[k][r] (zero for r >= R) and l2t[n][c] = L2[c mod rpad][n] (zero
+// past R): L1 transposed for the fused quantizer, [L2^T | L2^T] for the GEMM's
+// second pass.
+__device__ __forceinline__ void lowrank_layout(const LowRankPrep& q, int64_t i) {
+  const int64_t n1 = q.rpad * q.K, n2 = q.N * q.kl;
+  if (i < n1) {
+    const int64_t r = i / q.K, k = i % q.K;
+    q.l1t[i] = r < q.R ? q.l1[k * q.R + r] : (uint16_t)0;
+  } else if (i < n1 + n2) {
+    const int64_t j = i - n1, n = j / q.kl, c = (j % q.kl) % q.rpad;
+    q.l2t[j] = c < q.R ? q.l2[c * q.N + n] : (uint16_t)0;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_lowrank_transpose(LowRankPrep q) {
+  lowrank_layout(q, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// LR: the first lr_blocks workgroups write the factor layouts instead (one launch
+// fewer per low-rank layer; their scattered reads overlap the expansion's stream).
+template <bool G1, bool LR>
 __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict__ w, const uint8_t* __restrict__ wbs,
-                                                       float g2, int64_t nvec, uint16_t* __restrict__ out) {
-  const int64_t base = (int64_t)blockIdx.x * 256 * DEQUANT_U + threadIdx.x;
+                                                       float g2, int64_t nvec, uint16_t* __restrict__ out,
+                                                       LowRankPrep q, unsigned lr_blocks) {
+  if constexpr (LR) {
+    if (blockIdx.x < lr_blocks) {
+      lowrank_layout(q, (int64_t)blockIdx.x * 256 + threadIdx.x);
+      return;
+    }
+  }
+  const int64_t base = (int64_t)(blockIdx.x - (LR ? lr_blocks : 0u)) * 256 * DEQUANT_U + threadIdx.x;
   uint32_t c[DEQUANT_U], sc[DEQUANT_U];
 #pragma unroll
   for (int u = 0; u < DEQUANT_U; ++u) {
@@ -834,6 +862,17 @@ __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict
   }
 }
 
+static unsigned lowrank_blocks(const LowRankPrep& q) {
+  return (unsigned)((q.rpad * q.K + q.N * q.kl + 255) / 256);
+}
+
+hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,
+                               uint16_t* l1t, uint16_t* l2t, hipStream_t stream) {
+  const LowRankPrep q{l1, l2, K, N, R, kl / 2, kl, l1t, l2t};
+  hipLaunchKernelGGL(k_lowrank_transpose, dim3(lowrank_blocks(q)), dim3(256), 0, stream, q);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int64_t K, uint16_t* out,
                                hipStream_t stream) {
   const int64_t nch = N * K / 16;
@@ -843,13 +882,23 @@ hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int
 }
 
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K, uint16_t* out,
-                                hipStream_t stream) {
+                                hipStream_t stream, const LowRankPrep* lr) {
   const int64_t nvec = N * K / 8;
-  const dim3 grid((unsigned)((nvec + 256 * DEQUANT_U - 1) / (256 * DEQUANT_U))), block(256);
-  if (g2 == 1.0f)
-    hipLaunchKernelGGL(k_dequant_nvfp4<true>, grid, block, 0, stream, w, wbs, g2, nvec, out);
-  else
-    hipLaunchKernelGGL(k_dequant_nvfp4<false>, grid, block, 0, stream, w, wbs, g2, nvec, out);
+  const unsigned deq = (unsigned)((nvec + 256 * DEQUANT_U - 1) / (256 * DEQUANT_U));
+  const LowRankPrep q = lr ? *lr : LowRankPrep{};
+  const unsigned nlr = lr ? lowrank_blocks(q) : 0u;
+  const dim3 grid(deq + nlr), block(256);
+  if (g2 == 1.0f) {
+    if (lr)
+      hipLaunchKernelGGL((k_dequant_nvfp4<true, true>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
+    else
+      hipLaunchKernelGGL((k_dequant_nvfp4<true, false>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
+  } else {
+    if (lr)
+      hipLaunchKernelGGL((k_dequant_nvfp4<false, true>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
+    else
+      hipLaunchKernelGGL((k_dequant_nvfp4<false, false>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
+  }
   return hipGetLastError();
 }
 
