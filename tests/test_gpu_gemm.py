@@ -205,9 +205,10 @@ def test_qlinear_nvfp4_smoothed(name, M, K, N, R):
 
 
 @pytest.mark.parametrize("R,M,K", [(1, 130, 256), (20, 130, 256), (64, 130, 256), (100, 130, 256), (128, 45, 208),
-                                   (33, 17, 48)])
+                                   (33, 17, 48), (64, 5120, 256), (32, 6000, 256), (100, 5200, 192)])
 def test_qlinear_nvfp4_lowrank_ranks(R, M, K):
-    # every padded rank width (32, 64, 96, 128 columns of T), ragged M and K % 32 == 16
+    # every padded rank width (32, 64, 96, 128 columns of T), ragged M and K % 32 == 16;
+    # the fused quantizer with 20, 24 and 21 rows per workgroup (M = 5120, 6000, 5200)
     d = make("svdq_w4a4", M=M, K=K, N=200)
     rng = np.random.default_rng(R)
     from synthetic import bf16_round

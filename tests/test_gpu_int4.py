@@ -95,6 +95,8 @@ def sample_rows(M, n=64, seed=0):
     ("svdq_w4a4", 130, 256, 200, 64, False),    # two 32-column groups of T
     ("svdq_w4a4", 45, 192, 200, 100, True),     # four groups (TK = 128), smoothing
     ("nvfp4_dit", 300, 400 + 48, 520, 0, True), # smoothing without the low-rank branch
+    ("svdq_w4a4", 6000, 256, 200, 32, False),   # 24 rows per fused-quantizer workgroup
+    ("svdq_w4a4", 5120, 320, 72, None, True),   # 20 rows per workgroup, smoothing
 ])
 def test_qlinear_int4_small(name, M, K, N, R, smooth):
     d = make(name, M=M, K=K, N=N)
