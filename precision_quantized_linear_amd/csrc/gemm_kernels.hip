@@ -26,14 +26,17 @@
 //   stage holds the 256-row slab of both operands (32 KB) and four stages ring
 //   through 128 KB of the 160 KB LDS;
 // * slabs move global -> LDS with buffer_load_dwordx4 ... lds (no register
-//   staging), issued four stages ahead and spread between the MFMAs; rows past
-//   the matrix and bytes past K read as zero through the buffer range check;
+//   staging): slab g + 4 is issued while slab g is multiplied, three steps before
+//   its fragments are first read, spread between the MFMAs; rows past the matrix
+//   and bytes past K read as zero through the buffer range check;
 // * the 16-byte chunks of each 64-byte row are XOR-swizzled with
 //   (r ^ r >> 3) & 3, which makes the MFMA operand reads bank-conflict free;
 // * operand fragments of the next slab are read into the registers of the
 //   current slab's fragments as each one is used for the last time;
-// * operands are swapped (the MFMA computes y^T), so each lane ends with four
-//   consecutive output columns of a row and stores them as one 8-byte segment.
+// * operands are swapped (the MFMA computes y^T), so each lane ends with runs of
+//   four consecutive output columns of a row; lanes l and l + 32 swap halves
+//   (V_PERMLANE32_SWAP) and each stores eight consecutive columns as one 16-byte
+//   segment.
 #include <type_traits>
 
 #include "qpl_dma.h"
