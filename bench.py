@@ -182,11 +182,13 @@ def main():
 
     parts = {}
     for k in order:
-        ms = sum(a.elapsed_time(b) for a, b in ev[k]) / len(ev[k])
+        per_step = sorted(a.elapsed_time(b) for a, b in ev[k])
+        ms = sum(per_step) / len(per_step)
         e = lin[k]
         tf = e["flops"] / (ms * 1e-3) / 1e12
         peak = "fp8" if k == "fp8r" else "fp4"
         parts[k] = {"shape": [e["M"], e["K"], e["N"]] + ([e["R"]] if e["R"] else []), "ms": round(ms, 4),
+                    "ms_median": round(per_step[len(per_step) // 2], 4), "ms_min": round(per_step[0], 4),
                     "tflops": round(tf, 1), f"pct_{peak}_peak": round(100 * tf / PEAK_TFLOPS[peak], 2)}
         if k != "fp8r":
             parts[k]["pct_bf16_peak"] = round(100 * tf / PEAK_TFLOPS["bf16"], 2)
