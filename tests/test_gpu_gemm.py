@@ -269,3 +269,38 @@ def test_fp8_mfma_accumulation_bound():
     excess = np.maximum(np.abs(yb - ref) - 4 * ulp_bf16(ref), 0) / absum
     say("fp8 MFMA excess error / sum|aw|: max", excess.max())
     assert excess.max() <= FP8_MFMA_GAMMA
+
+
+@pytest.mark.parametrize("scheme", ["fp8r", "nvfp4"])
+def test_output_past_2_31_elements(scheme):
+    # M x N = 131072 x 32768 = 2^32 outputs (8 GB of bf16): the element offsets of rows past
+    # 65536 exceed 2^31, so the quantizer's and the epilogue's addressing must be 64-bit.
+    # K = 64 gives one or two slabs per tile, so each of the 65536 tiles has a workgroup.
+    M, K, N = 131072, 64, 32768
+    d = make("fp8r_dit_n3072" if scheme == "fp8r" else "nvfp4_dit", M=M, K=K, N=N)
+    x, w = d["x"], d["w"]
+    rows = np.unique(np.concatenate([[0, 65535, 65536, 65537, 98304, M - 2, M - 1],
+                                     np.random.default_rng(3).choice(M, 25, replace=False)]))
+    say("output past 2^31 elements", scheme, M, K, N)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    if scheme == "fp8r":
+        xq, xs = quant_fp8_row(x[rows])
+        wq, ws = quant_fp8_row(w)
+        a, b = dequant_fp8r(xq, xs), dequant_fp8r(wq, ws)
+        qpl.qlinear_fp8r(to_dev_bf16(x), to_dev(wq), to_dev(ws), y=y)
+        gamma = fp8_gamma(K)
+    else:
+        g_in = calibrate_input_scale(calibration_batches("nvfp4_dit", M=64, K=K))
+        g_w = global_scale(amax_bf16(w))
+        xp, xb = quant_nvfp4(x[rows], g_in)
+        wp, wb = quant_nvfp4(w, g_w)
+        a, b = dequant_nvfp4(xp, xb, g_in), dequant_nvfp4(wp, wb, g_w)
+        qpl.qlinear_nvfp4(to_dev_bf16(x), to_dev(wp), to_dev(wb), g_w, g_in, y=y)
+        gamma = None
+    got = bf16_bits(y[torch.from_numpy(rows).cuda()])
+    torch.cuda.synchronize()
+    del y
+    ref, absum = a @ b.T, np.abs(a) @ np.abs(b).T
+    r = check_gemm(got, ref, absum, K, gamma=gamma)
+    say(r)
+    assert r["ok"], r
