@@ -16,9 +16,10 @@ timing by the library's own quantizers, as a pre-quantized checkpoint would
 arrive.  Inputs are seeded synthetic data (see synthetic/workloads.py).
 
 The roofline object covers the dominant kernel (the nvfp4 GEMM at 4608 x 3072 x
-12288): its launches in every fifth step of the timed region are timed with HIP
-events on the launch stream (the library's event timing, limited to that kernel).  `parts` and
-`kernels` come from a second pass of the same steps with every launch timed.  The
+12288): after the timed region, a second pass of the same steps times every launch
+with HIP events on the launch stream (the library's event timing); the roofline
+takes that kernel's average over all of them, and `parts` and `kernels` come from
+the same pass.  The
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
 (rank 0, one GPU only).  `cold` times the same step with its tensors rotated over three
 copies (working set above the 256 MB last-level cache).  `extras` times what lies beyond the step: the svdq linear
@@ -46,7 +47,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_4608x3072x1228
 TRAFFIC_SOURCES = ("precision_quantized_linear_amd/csrc/gemm_kernels.hip", "precision_quantized_linear_amd/csrc/qpl_dma.h",
                    "precision_quantized_linear_amd/csrc/qpl_device.h", "precision_quantized_linear_amd/csrc/qpl_nvfp4.h")
 COPY_PROBE_BYTES = 256 << 20
-EVENT_EVERY = 5  # timed steps per HIP-event sample of the dominant kernel
 
 
 def parse():
@@ -145,21 +145,17 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed region
-    # Only the dominant kernel carries HIP events here, and only in every
-    # EVENT_EVERY-th step: an event pair holds the stream for about 6 us on each side
-    # of the launch.  The per-kernel and per-linear breakdown comes from a second
+    # No events here (an event pair holds the stream for a few microseconds on each
+    # side of a launch); the per-kernel and per-linear breakdown comes from a second
     # pass below with every launch bracketed.
     qpl.timing_collect()  # drop anything recorded so far
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        qpl.timing_select(["gemm_nvfp4"] if i % EVENT_EVERY == 0 else [])
+    for _ in range(args.steps):
         for k in order:
             run(k)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    qpl.timing_select([])
-    dominant = qpl.timing_collect()["gemm_nvfp4"]
     log(f"timed {args.steps} steps in {t_total * 1e3:.1f} ms")
 
     ms_step = t_total * 1e3 / args.steps
@@ -198,18 +194,28 @@ def main():
     kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for k, (n, t) in kern.items() if n}
 
     # ---------------------------------------------------------------- roofline (dominant kernel)
-    n_g, t_g = dominant
+    # every launch of the breakdown pass (clocks ramped by the warm-up and the timed region)
+    n_g, t_g = kern["gemm_nvfp4"]
     avg_s = t_g / n_g * 1e-3
     e = lin["nvfp4"]
     achieved = e["flops"] / avg_s / 1e12
     traffic = measured_traffic()
-    roofline = {"kernel": "gemm_nvfp4 (bf16 MFMA, 4608x3072x12288)", "bound": "mfma", "achieved": round(achieved, 1),
-                "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                "traffic": traffic, "avg_us": round(avg_s * 1e6, 2), "event_samples": n_g,
+    roofline = {"kernel": "gemm_nvfp4 (packed E2M1 + E4M3 operands expanded to f16, f16 MFMA, 4608x3072x12288)",
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
+                "avg_us": round(avg_s * 1e6, 2), "event_samples": n_g,
                 "frac_of_fp4_peak": round(achieved / PEAK_TFLOPS["fp4"], 4)}
-    nq, tq = kern["quant_fp8_row"]
-    qbytes = 3.0 * lin["fp8r"]["M"] * lin["fp8r"]["K"] + 4.0 * lin["fp8r"]["M"]
-    quant_gbs = qbytes / (tq / nq * 1e-3) / 1e9
+    # the quantizers against HBM on their algorithmic bytes: fp8r 2 B in + 1 B out per
+    # element (+ 4 B per row); nvfp4 2 B in + 0.5 B codes + 1/16 B scales per element
+    # (+ T out for the fused low-rank quantizer)
+    def gbs(kind, nbytes):
+        n, t = kern[kind]
+        return round(nbytes / (t / n * 1e-3) / 1e9, 1) if n else None
+    mk = lin["fp8r"]["M"] * lin["fp8r"]["K"]
+    quant_gbs = {"quant_fp8_row": gbs("quant_fp8_row", 3.0 * mk + 4.0 * lin["fp8r"]["M"]),
+                 "quant_nvfp4_linear": gbs("quant_nvfp4_linear", 2.5625 * lin["nvfp4"]["M"] * lin["nvfp4"]["K"]),
+                 "quant_nvfp4_lowrank": gbs("quant_nvfp4_lowrank", 2.5625 * lin["svdq"]["M"] * lin["svdq"]["K"] +
+                                            4.0 * lin["svdq"]["M"] * 32 * ((lin["svdq"]["R"] + 31) // 32))}
 
     cold = measure_cold(args, qpl, torch, lin, order, total_flops)
     extras = None if args.no_extras else measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors)
@@ -229,7 +235,7 @@ def main():
         "roofline": roofline,
         "parts": parts,
         "kernels": kernels,
-        "quant_fp8_row_gbs": round(quant_gbs, 1),
+        "quant_gbs": quant_gbs,
         "cold": cold,
         "extras": extras,
         "cpu_baseline": cpu,
@@ -300,7 +306,8 @@ def measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors)
     ns, ts = qpl.timing_collect()["quant_nvfp4_lowrank"]
     ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
     kl = 2 * 32 * ((e["R"] + 31) // 32)
-    qlr_bytes = 4.0 * e["M"] * e["K"] + 2.0 * e["M"] * kl + 4.0 * e["K"]  # x in, expanded x out, T out, factors
+    # x in, packed codes and scales out, T out (hi | lo bf16), smoothing factors
+    qlr_bytes = 2.5625 * e["M"] * e["K"] + 2.0 * e["M"] * kl + 4.0 * e["K"]
     extras = {"svdq_smooth": {"shape": [e["M"], e["K"], e["N"], e["R"]], "ms": round(ms, 4),
                               "tflops": round(e["flops"] / (ms * 1e-3) / 1e12, 1),
                               "quant_nvfp4_lowrank_smooth_us": round(1e3 * ts / ns, 2),
@@ -470,22 +477,13 @@ def measure_epilogues(args, qpl, torch, dev, bf16, lin, kern, make, smooth_facto
     g_in = max(gscale(bf16(b)) for b in calibration_batches("qkv_dit"))
     q, k, v = (torch.empty((s["heads"], s["tokens"], s["head_dim"]), dtype=torch.bfloat16, device=dev)
                for _ in range(3))
-    y = torch.empty((d["M"], d["N"]), dtype=torch.bfloat16, device=dev)
     wsq = torch.empty((qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, d["M"], d["K"], d["N"], 0),), dtype=torch.uint8,
                       device=dev)
-    dd = s["heads"] * s["head_dim"]
-
-    def plain_then_copy():
-        qpl.qlinear_nvfp4(x, wq, wb, g_w, g_in, y=y, workspace=wsq)
-        for i, t in enumerate((q, k, v)):
-            t[:, s["offset"]:].copy_(y[:, i * dd:(i + 1) * dd].view(d["M"], s["heads"], s["head_dim"]).transpose(0, 1))
 
     ms_q, us_q = timed(lambda: qpl.qlinear_nvfp4(x, wq, wb, g_w, g_in, workspace=wsq, qkv=(q, k, v, s["offset"])),
                        ["gemm_epilogue"])
-    ms_p, _ = timed(plain_then_copy)
     out["qkv_nvfp4"] = {"shape": [d["M"], d["K"], d["N"]], "heads": s["heads"], "head_dim": s["head_dim"],
-                        "fused_ms": round(ms_q, 4), "plain_then_torch_copy_ms": round(ms_p, 4),
-                        "gemm_us": us_q.get("gemm_epilogue")}
+                        "fused_ms": round(ms_q, 4), "gemm_us": us_q.get("gemm_epilogue")}
     return out
 
 
@@ -561,11 +559,25 @@ def cpu_baseline(lin, rows, min_seconds=10.0, max_passes=4):
             del y
         passes += 1
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
     r = min(rows, min(e["M"] for e in lin.values()))
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} pass(es) over {r} activation rows of each of the 3 linears (full weights), "
-                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+                      f"{dt:.1f} s", "seconds": round(dt, 2), "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "blas": ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in blas}))}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -24,6 +24,11 @@
  *   returns a non-zero status and touches no memory.  Checks: non-NULL pointers,
  *   16-byte aligned pointers, M, N >= 1, K >= 16 and K % 16 == 0, scalars finite
  *   and > 0, workspace large enough, and a current HIP device that is gfx950.
+ * - Size limits of the linears (QPL_ERR_SHAPE beyond them): the GEMMs address a
+ *   256-row tile of an operand with 32-bit offsets below 2^30, so K < 2^22 for
+ *   fp8r and INT4 (K-byte rows) and K < 2^23 for nvfp4 (K/2-byte rows); with a
+ *   low-rank branch (R > 0) K <= 2^21 and the activation's scales (8 M ceil(K/128)
+ *   bytes for nvfp4, 4 M K/64 for INT4) below 2^31 bytes.
  * - Inputs must be finite: NaN or infinity in x or W is outside the contract.
  * - Faults inside a kernel surface at the caller's next synchronization.
  */
@@ -111,18 +116,26 @@ qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N,
  *   weight          uint8 [N,K/2]        packed E2M1
  *   weight_scale    uint8 E4M3 [N,K/16]
  *   weight_scale_2  global weight scale, finite and > 0
- *   input_scale     calibrated activation scale, finite and > 0, 6 * input_scale finite
+ *   input_scale     calibrated activation scale, finite and > 0, 6 * input_scale finite;
+ *                   the product input_scale * weight_scale_2 must be a normal fp32
+ *                   number (else QPL_ERR_ARG); it scales the fp32 4-bit product
  *   smooth          float [K] smoothing factors or NULL (as in quant_act_nvfp4)
  *   lora_down       bf16 [K,R] (L1) or NULL when R == 0
  *   lora_up         bf16 [R,N] (L2) or NULL when R == 0
  *   R               rank, 0..128
  *   y               bf16 [M,N]          out
  *   ws, ws_bytes    scratch of at least qlinear_workspace_bytes(QPL_NVFP4, M, K, N, R);
- *                   after the call its first 2 M K bytes hold the expanded activation
- *                   (bf16 [M,K], the values e2m1(code) * dec(sf) of quant_act_nvfp4's
- *                   output, exact; a zero may lose its sign) and the 2 N K bytes from
- *                   offset 256 * ceil(2 M K / 256) the expanded weight (bf16 [N,K],
- *                   e2m1(code) * dec(sf), exact)
+ *                   after the call it holds the quantized activation the GEMM read:
+ *                   its first M K/2 bytes are the packed codes (identical to
+ *                   quant_act_nvfp4's x_q), and the 8 M S bytes from offset
+ *                   256 ceil(M K/2 / 256) its block scales in the GEMM's slab-major
+ *                   layout [S, M, 8], S = ceil(K/128): byte (s M + m) 8 + i is block
+ *                   8 s + i of row m (quant_act_nvfp4's x_block_scale[m, 8 s + i]),
+ *                   zero for 8 s + i >= K/16.
+ * The GEMM multiplies the packed operands as they are: E2M1 codes and E4M3 block
+ * scales are expanded in registers to exact f16 values and summed in fp32 on the
+ * MFMA units.  With R > 0 the 4-bit product is scaled by input_scale *
+ * weight_scale_2 before the low-rank term is added.
  */
 qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                          const uint8_t* weight, const uint8_t* weight_scale,
@@ -246,10 +259,10 @@ qpl_status qlinear_int4_ex(const uint16_t* x, int64_t M, int64_t K, int64_t N,
  * carry smoothing and a low-rank branch; each layer's tensors are as in
  * qlinear_nvfp4 (weight [rows, cols/2], weight_scale [rows, cols/16], ...).
  * Workspace: qlinear_mlp_nvfp4_workspace_bytes(M, K, H, N, fc1->R, fc2->R) bytes (0
- * for invalid sizes); its first 2 M H bytes hold fc2's expanded operand (the
- * values e2m1(code) * dec(sf) of its quantized input, bf16) after the call, and
- * the 2 M H bytes at offset qlinear_workspace_bytes(QPL_NVFP4, M, H, N, fc2->R)
- * hold h.  Errors: as qlinear_nvfp4 for either layer.
+ * for invalid sizes); it starts with fc2's qlinear_nvfp4 workspace, so after the
+ * call it holds fc2's quantized input as described there (codes, then slab-major
+ * block scales), and the 2 M H bytes at offset qlinear_workspace_bytes(QPL_NVFP4,
+ * M, H, N, fc2->R) hold h.  Errors: as qlinear_nvfp4 for either layer.
  */
 typedef struct {
   const uint8_t* weight;        /* uint8 [rows, cols/2], two E2M1 codes per byte */
@@ -310,15 +323,15 @@ float qpl_nvfp4_global_scale(float amax);
 typedef enum {
   QPL_KERNEL_QUANT_FP8_ROW = 0,     /* fp8r activation / weight quantize */
   QPL_KERNEL_QUANT_NVFP4 = 1,       /* nvfp4 quantize to packed codes */
-  QPL_KERNEL_QUANT_NVFP4_BF16 = 2,  /* nvfp4 quantize inside qlinear_nvfp4 (bf16 output) */
+  QPL_KERNEL_QUANT_NVFP4_LINEAR = 2, /* nvfp4 quantize inside qlinear_nvfp4 (R = 0; slab-major scales) */
   QPL_KERNEL_GEMM_FP8R = 3,
   QPL_KERNEL_GEMM_NVFP4 = 4,
   QPL_KERNEL_GEMM_NVFP4_LOWRANK = 5, /* nvfp4 GEMM with the low-rank epilogue */
   QPL_KERNEL_LOWRANK_PREP = 6,      /* low-rank factor transposes (qlinear_int4) */
   QPL_KERNEL_DEQUANT = 7,
   QPL_KERNEL_AMAX = 8,
-  QPL_KERNEL_WEIGHT_BF16 = 9,       /* nvfp4 weight expansion inside qlinear_nvfp4; with R > 0 the same
-                                       launch writes the low-rank factor layouts */
+  QPL_KERNEL_NVFP4_PREP = 9,        /* qlinear_nvfp4's preparation: the weight's block scales into the
+                                       GEMM's layout and, with R > 0, the low-rank factor layouts */
   QPL_KERNEL_QUANT_NVFP4_LOWRANK = 10, /* nvfp4 quantize fused with x L1 (qlinear_nvfp4, R > 0) */
   QPL_KERNEL_QUANT_W4G = 11,        /* quant_weight_awq */
   QPL_KERNEL_GEMV_W4A16 = 12,       /* qlinear_awq_w4a16 */

@@ -23,8 +23,8 @@ EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp
            "qpl_timing_enable", "qpl_timing_select", "qpl_timing_collect")
 
 # qpl_kernel order of include/qpl.h
-KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_bf16", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
-           "lowrank_prep", "dequant", "amax", "weight_bf16", "quant_nvfp4_lowrank", "quant_w4g", "gemv_w4a16",
+KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_linear", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
+           "lowrank_prep", "dequant", "amax", "nvfp4_prep", "quant_nvfp4_lowrank", "quant_w4g", "gemv_w4a16",
            "quant_int4", "int4_expand", "gemm_int4", "quant_int4_lowrank", "gemm_epilogue")
 
 QPL_ACT_NONE = 0

@@ -505,11 +505,378 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   gemm_persistent<Fp8Mma, true, false, EPI>(p, sa, sb, 1.0f, Y, e);
 }
 
+// ---------------------------------------------------------------------------
+// nvfp4 GEMM on the packed operands (guide "BFL (fp8r / nvfp4)", "Kernels" table,
+// nvfp4 row: the quantized tensors keep their storage format; Nunchaku post,
+// "Background: SVDQuant and Nunchaku": the 4-bit GEMM carries the low-rank
+// up-projection).  Both operands stay E2M1 codes (two per byte) with one E4M3
+// scale per 16 elements all the way into LDS; each lane expands its own MFMA
+// fragments in registers to f16 values e2m1(code) * dec(sf): the FP4 converter
+// gives the code values and one packed f16 multiply applies the block scale.
+// The product has at most 6 significant bits and lies in [2^-10, 2688], so the
+// f16 value is exact, and so is each f16 x f16 product the MFMA forms
+// (V_MFMA_F32_32X32X16_F16, fp32 accumulation).  input_scale * weight_scale_2
+// scales the fp32 result.
+//
+// Tiling and schedule follow gemm_persistent (256 x 256 tiles, 4 wavefronts of
+// 128 x 128, persistent workgroups, XCD-grouped tile order, half tiles in the
+// last round, y^T epilogue), with these slabs:
+// * a slab is 128 K elements: 64 code bytes per row (16 KB per operand) and 8
+//   block-scale bytes per row (2 KB per operand, slab-major in global memory:
+//   [K/128][rows][8], zero past K/16, so one 1 KB load moves 128 rows' scales);
+//   a stage is 36 KB and four stages ring through 144 KB of LDS;
+// * lane half h of a fragment row takes blocks 4h .. 4h + 3 of the slab: code
+//   bytes 32h .. 32h + 31 (two 16-byte LDS reads) and one scale dword.  MFMA step
+//   s (0..7) multiplies nibbles 8 (s % 2) .. + 7 of block 4h + s / 2; both
+//   operands use this order, so the pairs of a product are the same k;
+// * software pipeline across slabs: the second half of a slab's codes is read
+//   from LDS when the slab starts, and once its steps 0-3 have used the first half,
+//   the first half and the scales of the next slab are read into those registers.
+//   The barrier at the top of slab g therefore waits for slab g + 1 and frees the
+//   stage of slab g - 1, into which slab g + 3 is issued (9 loads per wave: 8 of
+//   codes and 1 of scales, spread over the slab's 128 MFMAs);
+// * blocks past K have scale 0 (they multiply to 0 whatever codes straddle the row
+//   end), rows past M or N read zeros through the buffer range check.
+// LOWRANK: after the packed slabs of a tile the accumulators are multiplied by
+// gscale, then bf16 slabs of [T_hi | T_lo] and [L2^T | L2^T] (64 bytes per row)
+// continue the same accumulation on the bf16 MFMA, so y = bf16(gscale x_q w_q^T
+// + T L2) with T unscaled.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int PK_CODES = 256 * SROW;                // code bytes per operand per stage
+constexpr int PK_SC = 256 * 8;                      // block-scale bytes per operand per stage
+constexpr int PK_STAGE = 2 * PK_CODES + 2 * PK_SC;  // [x codes][w codes][x scales][w scales]
+constexpr int PK_NST = 4;
+constexpr int PK_D = 9;                             // loads per wave per slab
+
+struct PackedArgs {
+  const uint8_t* xq;   // activation codes [M, K/2]
+  const uint8_t* wq;   // weight codes [N, K/2]
+  const uint8_t* xs;   // activation block scales [S, M, 8], S = ceil(K/128)
+  const uint8_t* wsc;  // weight block scales [S, N, 8]
+  const uint8_t* a2;   // low-rank pass: [T_hi | T_lo] bf16 [M, kl]
+  const uint8_t* w2;   // [L2^T | L2^T] bf16 [N, kl]
+  int64_t M, N;
+  int cpitch;          // code bytes per row (K/2)
+  int nk1;             // packed slabs per tile (S)
+  int pitch2, kbytes2; // low-rank rows: 2 kl bytes
+  int tiles_m, tiles_n, ntiles, nwg, nfull, ntail;
+};
+
+// (s, s) as an f16 pair for the E4M3 scale in byte j of sc (exact).
+__device__ __forceinline__ f16x2 e4m3_pair(uint32_t sc, uint32_t j) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(sc, sc, j * 0x01010101u), 1.0f, false);
+}
+
+// Eight E2M1 codes (a dword, element 2i in the low nibble of byte i) times the
+// pair s: f16 values code * s in element order.
+__device__ __forceinline__ f16x8 fp4_expand(uint32_t cw, f16x2 s) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * s;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * s;
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * s;
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * s;
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 template <bool LOWRANK, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
-    GemmArgs p, float gscale, uint16_t* __restrict__ Y, EpiArgs e) {
-  gemm_persistent<Bf16Mma, false, LOWRANK, EPI>(p, nullptr, nullptr, gscale, Y, e);
+    PackedArgs p, float gscale, uint16_t* __restrict__ Y, EpiArgs e) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PK_NST * PK_STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wv >> 1, wn = wv & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int b = blockIdx.x;
+  const uint32_t lbase = lds_address(lds);
+
+  // units of work: whole tiles, then (has_half) one 128-row half of a leftover tile.
+  // With the low-rank pass a workgroup takes one tile (the host launches one per
+  // tile): the pass's extra state leaves no registers for the persistent loop.
+  int nt = 0;
+  if constexpr (LOWRANK) {
+    nt = 1;
+  } else {
+    while (tile_seq(nt, b, p.nwg) < p.nfull) ++nt;
+  }
+  const int hu = LOWRANK ? 0 : tile_seq(nt, b, p.nwg) - p.nfull;
+  const bool has_half = !LOWRANK && hu < 2 * p.ntail;
+  const int nu = nt + (has_half ? 1 : 0);
+  const int nk1 = p.nk1;
+  const int nk2 = LOWRANK ? (p.kbytes2 + SROW - 1) / SROW : 0;
+  const int nk = nk1 + nk2;
+  struct Unit {
+    int64_t m0, n0;
+    int rows;
+  };
+  auto unit = [&](int ti) {
+    Unit r;
+    if (ti < nt) {
+      tile_coords(tile_seq(ti, b, p.nwg), p.tiles_m, p.tiles_n, r.m0, r.n0);
+      r.rows = 256;
+    } else {
+      tile_coords(p.nfull + (hu >> 1), p.tiles_m, p.tiles_n, r.m0, r.n0);
+      r.m0 += 128 * (hu & 1);
+      r.rows = 128;
+    }
+    return r;
+  };
+
+  // row loads: instruction q of this wave fills slab rows 16 (4 wv + q) .. + 15;
+  // lane l writes physical chunk l % 4 of row + l / 4 (logical chunk (l % 4) ^ swz),
+  // at byte offset vo1 (packed rows) or vo2 (low-rank rows) of the tile
+  int cb[4];
+  uint32_t vo1[4], vo2[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lrow = 16 * (4 * wv + q) + (lane >> 2);
+    cb[q] = ((lane & 3) ^ swz(lrow)) * 16;
+    vo1[q] = (uint32_t)(lrow * p.cpitch + cb[q]);
+    vo2[q] = LOWRANK ? (uint32_t)(lrow * p.pitch2 + cb[q]) : 0u;
+  }
+  // scale loads: wave wv moves rows 128 (wv % 2) .. + 127 of operand wv / 2 (x, W)
+  const bool sc_x = wv < 2;
+  const int sc_r0 = 128 * (wv & 1);
+
+  struct SlabSrc {
+    u32x4 dx, dw, ds;
+    int kb, koff, stage;
+    bool pass2;
+  };
+  int s_ti = 0, s_ks = 0, s_stage = 0;
+  Unit s_u{0, 0, 256};
+  if (nu > 0) s_u = unit(0);
+  auto next_src = [&]() {
+    SlabSrc r;
+    const bool valid = s_ti < nu;
+    const bool pass2 = LOWRANK && s_ks >= nk1;
+    r.stage = s_stage;
+    r.pass2 = pass2;
+    const int pitch = pass2 ? p.pitch2 : p.cpitch;
+    r.kb = valid ? (pass2 ? p.kbytes2 : p.cpitch) : 0;
+    r.koff = (pass2 ? s_ks - nk1 : s_ks) * SROW;
+    const int64_t left = p.M - s_u.m0;
+    const int64_t rm = left < 0 ? 0 : (left < s_u.rows ? left : s_u.rows);
+    const int64_t rn = M_rows(p.N - s_u.n0);
+    r.dx = make_desc((pass2 ? p.a2 : p.xq) + s_u.m0 * pitch, rm * pitch);
+    r.dw = make_desc((pass2 ? p.w2 : p.wq) + s_u.n0 * pitch, rn * pitch);
+    const int64_t lim = (sc_x ? rm : rn) - sc_r0;
+    const int64_t nrow = (valid && !pass2) ? (lim < 0 ? 0 : (lim < 128 ? lim : 128)) : 0;
+    const int64_t srows = sc_x ? p.M : p.N;
+    const int64_t row0 = (sc_x ? s_u.m0 : s_u.n0) + sc_r0;
+    r.ds = make_desc((sc_x ? p.xs : p.wsc) + ((int64_t)(pass2 ? 0 : s_ks) * srows + row0) * 8, nrow * 8);
+    s_stage = s_stage == PK_NST - 1 ? 0 : s_stage + 1;
+    if (++s_ks == nk) {
+      s_ks = 0;
+      ++s_ti;
+      if (s_ti < nu) s_u = unit(s_ti);
+    }
+    return r;
+  };
+  auto issue = [&](const SlabSrc& s, int d) {
+    const uint32_t st = lbase + s.stage * PK_STAGE;
+    if (d < 8) {
+      const int q = d & 3;
+      const bool wslab = d >= 4;
+      const uint32_t vo = s.koff + cb[q] < s.kb ? (LOWRANK && s.pass2 ? vo2[q] : vo1[q]) : kOutOfRange;
+      dma16(st + (wslab ? PK_CODES : 0) + (4 * wv + q) * 1024, vo, wslab ? s.dw : s.dx, s.koff);
+    } else {
+      // 1 KB of scales (128 rows x 8 bytes); rows past the unit read zero
+      dma16(st + 2 * PK_CODES + (sc_x ? 0 : PK_SC) + sc_r0 * 8, (uint32_t)lane * 16u, s.ds, 0);
+    }
+  };
+
+  // prologue: slabs 0 .. 2, then slab 0's first code half and scales
+#pragma unroll
+  for (int s0 = 0; s0 < PK_NST - 1; ++s0) {
+    const SlabSrc src = next_src();
+#pragma unroll
+    for (int d = 0; d < PK_D; ++d) issue(src, d);
+  }
+  QPL_WAIT_VMCNT(2 * PK_D);
+  __builtin_amdgcn_s_barrier();
+
+  // fragment rows of tile-row t of a unit with nj x tile-rows: t < 4 W, t >= 4 x
+  auto frow = [&](int t, int nj) { return t < 4 ? wn * 128 + t * 32 + r32 : wm * 32 * nj + (t - 4) * 32 + r32; };
+  // code dword s (step s) of every tile-row of the slab in stage st: bytes 32 h + 4 s
+  // of the row, i.e. chunk 2 h + s / 4 at offset 4 (s % 4)
+  auto read_codes = [&](const uint8_t* st, int nj, int s, uint32_t (&dst)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      dst[t] = *reinterpret_cast<const uint32_t*>(st + (t < 4 ? PK_CODES : 0) + soff(frow(t, nj), 2 * h + (s >> 2)) +
+                                                  4 * (s & 3));
+  };
+  // block-scale dword (blocks 4 h .. 4 h + 3) of every tile-row of the slab in stage st
+  auto read_scales = [&](const uint8_t* st, int nj, uint32_t (&dst)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      dst[t] = *reinterpret_cast<const uint32_t*>(st + 2 * PK_CODES + (t < 4 ? PK_SC : 0) + frow(t, nj) * 8 + 4 * h);
+  };
+  // The expansion runs one MFMA step ahead and the code reads two: while step s of
+  // a slab is multiplied (fragments F), step s + 1 is expanded (from codes C) and the
+  // codes of step s + 2 are read.  Across slabs, the last two steps of a slab do this
+  // for the first steps of the next one when it is a packed slab.
+  f16x8 F[8];             // fragments of the step being multiplied (t < 4: W, t >= 4: x)
+  uint32_t C[8], sc[8];   // codes of the next step, scales of the current slab
+  auto expand_step = [&](const uint32_t (&c)[8], const uint32_t (&scd)[8], int blk, f16x8 (&dst)[8], int ntr) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (t < ntr) dst[t] = fp4_expand(c[t], e4m3_pair(scd[t], blk));
+  };
+  // first step of the slab in stage st (a unit with nj x tile-rows), unpipelined
+  auto prime = [&](const uint8_t* st, int nj) {
+    uint32_t c0[8];
+    read_codes(st, nj, 0, c0);
+    read_scales(st, nj, sc);
+    read_codes(st, nj, 1, C);
+    expand_step(c0, sc, 0, F, 8);
+  };
+  prime(lds, nt > 0 ? 4 : 2);
+
+  int cur = 0;                // stage of the slab being multiplied
+  int st1 = 0, st2 = 0;       // stores left in flight after iterations g - 1, g - 2
+  // Top of a slab: slab g + 1 has landed (issued after it: slab g + 2's loads and
+  // the stores of the epilogues after iterations g - 2 and g - 1), every wave is
+  // done with slab g - 1, whose stage receives slab g + 3.
+  auto top = [&]() {
+    QPL_WAIT_LGKM0();
+    const int extra = st1 + st2;
+    if (extra == 0) {
+      QPL_WAIT_VMCNT(PK_D);
+    } else if (extra == NSTORE) {
+      QPL_WAIT_VMCNT(PK_D + NSTORE);
+    } else {
+      QPL_WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_barrier();
+    st2 = st1;
+    st1 = 0;
+    return next_src();
+  };
+
+  // A packed slab.  njn: x tile-rows of the unit the next slab belongs to, or 0
+  // when the next slab is not a packed one (its first step is then primed by
+  // whoever starts it).
+  auto step_packed = [&](Acc& acc, auto nj, int njn) {
+    constexpr int NJ = decltype(nj)::value;
+    constexpr int NMMA = 32 * NJ;  // 8 steps x 4 x NJ
+    const SlabSrc src = top();
+    const uint8_t* cs = lds + cur * PK_STAGE;
+    cur = cur == PK_NST - 1 ? 0 : cur + 1;
+    const uint8_t* ns = lds + cur * PK_STAGE;
+    uint32_t scn[8];
+    static_for<0, 8>([&](auto sc_) __attribute__((always_inline)) {
+      constexpr int s = decltype(sc_)::value;
+      // codes two steps ahead
+      uint32_t C2[8];
+      if constexpr (s + 2 < 8) {
+        read_codes(cs, NJ, s + 2, C2);
+      } else {
+        if (njn) read_codes(ns, njn, s - 6, C2);
+      }
+      if constexpr (s == 6) {
+        if (njn) read_scales(ns, njn, scn);
+      }
+      // the next step's fragments
+      f16x8 Fn[8];
+      if constexpr (s + 1 < 8) {
+        expand_step(C, sc, (s + 1) >> 1, Fn, 4 + NJ);
+      } else {
+        if (njn) expand_step(C, scn, 0, Fn, 8);
+      }
+      // this step's MFMAs
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[i], F[4 + j], acc[i][j], 0, 0, 0);
+          const int k = s * 4 * NJ + i * NJ + j;
+#pragma unroll
+          for (int d = 0; d < PK_D; ++d)
+            if (k == (d * NMMA) / PK_D) issue(src, d);
+        }
+      if (s + 1 < 8 || njn) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) F[t] = Fn[t];
+      }
+      if (s + 2 < 8 || njn) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) C[t] = C2[t];
+      }
+      // keeps the pipeline's shape: the scheduler interleaves the next step's
+      // expansion with this step's MFMAs, but does not pull later steps forward
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (njn) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sc[t] = scn[t];
+    }
+  };
+
+  // A bf16 slab of the low-rank pass (fragments read from its stage at the top).
+  auto step_lowrank = [&](Acc& acc, auto nj, int njn) {
+    constexpr int NJ = decltype(nj)::value;
+    constexpr int NMMA = 8 * NJ;
+    const SlabSrc src = top();
+    const uint8_t* cs = lds + cur * PK_STAGE;
+    cur = cur == PK_NST - 1 ? 0 : cur + 1;
+    const uint8_t* ns = lds + cur * PK_STAGE;
+    static_for<0, 2>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      bf16x8 fw[4], fx[NJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fw[i] = Bf16Mma::read(cs + PK_CODES, frow(i, NJ), u, lane);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) fx[j] = Bf16Mma::read(cs, frow(4 + j, NJ), u, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc[i][j] = Bf16Mma::mma(fw[i], fx[j], acc[i][j]);
+          const int k = u * 4 * NJ + i * NJ + j;
+#pragma unroll
+          for (int d = 0; d < PK_D; ++d)
+            if (k == (d * NMMA) / PK_D) issue(src, d);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (njn) prime(ns, njn);
+  };
+
+  using Whole = std::integral_constant<int, 4>;
+  using Half = std::integral_constant<int, 2>;
+  const float escale = LOWRANK ? 1.0f : gscale;
+  auto run_unit = [&](int ti, auto nj) {
+    constexpr int NJ = decltype(nj)::value;
+    // x tile-rows of the next unit (0: none)
+    const int njn = ti + 1 < nt ? 4 : (ti + 1 < nu ? 2 : 0);
+    Acc acc;
+    zero_acc(acc);
+    for (int ks = 0; ks < nk1; ++ks) step_packed(acc, nj, ks + 1 < nk1 ? NJ : (nk2 > 0 ? 0 : njn));
+    if constexpr (LOWRANK) {
+      // the 4-bit product in output units; each tile goes back to its accumulator
+      // registers at once (the empty asm pins it there), so that the scaled values do
+      // not wait in ordinary registers for the low-rank MFMAs
+      static_for<0, 4 * NJ>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int q = decltype(tc)::value;
+        acc[q / NJ][q % NJ] = acc[q / NJ][q % NJ] * gscale;
+        asm volatile("" : "+a"(acc[q / NJ][q % NJ]));
+      });
+      for (int ks = 0; ks < nk2; ++ks) step_lowrank(acc, nj, ks + 1 < nk2 ? 0 : njn);
+    }
+    const Unit un = unit(ti);
+    st1 = store_tile<NJ, 4, EPI>(
+        acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return escale; },
+        [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e);
+    if (st1 == 0) st2 = 0;
+  };
+  for (int ti = 0; ti < nt; ++ti) run_unit(ti, Whole{});
+  if (has_half) run_unit(nt, Half{});
+  QPL_WAIT_VMCNT(0);
+  QPL_WAIT_LGKM0();
 }
+
 
 // ---------------------------------------------------------------------------
 // INT4 GEMM (the INT4 variant of svdq_w4a4).  The operands are the code values
@@ -803,7 +1170,7 @@ hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w
 }
 
 template <bool LR>
-static hipError_t launch_nvfp4_epi(int kind, dim3 grid, hipStream_t stream, const GemmArgs& p, float gscale,
+static hipError_t launch_nvfp4_epi(int kind, dim3 grid, hipStream_t stream, const PackedArgs& p, float gscale,
                                    uint16_t* y, const EpiArgs& e) {
   switch (kind) {
     case 0: hipLaunchKernelGGL((k_gemm_nvfp4<LR, 0>), grid, dim3(256), 0, stream, p, gscale, y, e); break;
@@ -814,27 +1181,34 @@ static hipError_t launch_nvfp4_epi(int kind, dim3 grid, hipStream_t stream, cons
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
-                             LowRank lr, const Epilogue& ep, uint16_t* y, hipStream_t stream) {
-  GemmArgs p{};
-  p.a = reinterpret_cast<const uint8_t*>(xe);
-  p.w = reinterpret_cast<const uint8_t*>(we);
+hipError_t launch_gemm_nvfp4(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* wsc,
+                             float gscale, int64_t M, int64_t K, int64_t N, LowRank lr, const Epilogue& ep, uint16_t* y,
+                             hipStream_t stream) {
+  PackedArgs p{};
+  p.xq = xq;
+  p.wq = wq;
+  p.xs = xs;
+  p.wsc = wsc;
   p.M = M;
   p.N = N;
-  p.pitch1 = (int)(2 * K);
-  p.kbytes1 = (int)(2 * K);
-  int nk = (p.kbytes1 + SROW - 1) / SROW;
+  p.cpitch = (int)(K / 2);
+  p.nk1 = (int)((K + 127) / 128);
   if (lr.kl > 0) {
     p.a2 = reinterpret_cast<const uint8_t*>(lr.t);
     p.w2 = reinterpret_cast<const uint8_t*>(lr.l2t);
     p.pitch2 = (int)(2 * lr.kl);
     p.kbytes2 = (int)(2 * lr.kl);
-    nk += (p.kbytes2 + SROW - 1) / SROW;
   }
   p.tiles_m = (int)((M + 255) / 256);
   p.tiles_n = (int)((N + 255) / 256);
   p.ntiles = p.tiles_m * p.tiles_n;
-  gemm_plan(p, nk);
+  // persistent (one workgroup per CU at most); leftover tiles of a last round of at
+  // most 128 are split into half tiles.  With the low-rank pass: one tile per workgroup.
+  p.nwg = lr.kl > 0 ? p.ntiles : (p.ntiles < 256 ? p.ntiles : 256);
+  const int tail = p.ntiles % 256;
+  const bool split = lr.kl == 0 && p.ntiles > 256 && tail > 0 && tail <= 128;
+  p.nfull = split ? p.ntiles - tail : p.ntiles;
+  p.ntail = split ? tail : 0;
   EpiArgs e;
   const int kind = epi_kind(ep, e);
   const dim3 grid((unsigned)p.nwg);

@@ -34,6 +34,26 @@ qpl_status check_gemm_dims(int64_t M, int64_t K, int64_t N) {
   return QPL_OK;
 }
 
+int64_t nvfp4_slabs(int64_t K) { return (K + 127) / 128; }
+
+// The GEMMs address a 256-row tile of an operand through one buffer descriptor with
+// 32-bit offsets, and an offset of 2^30 stands for "past the end": 256 rows times
+// the row pitch in bytes must stay below 2^30.  fp8r and INT4 rows are K bytes,
+// nvfp4 rows K/2.  The fused low-rank quantizers stage up to 128 rows of L1^T
+// (2K bytes each) the same way (K <= 2^21) and store their scales through a
+// descriptor below 2^31 bytes.
+constexpr int64_t kMaxKBytePitch = (int64_t(1) << 30) / 256;
+qpl_status check_gemm_k(qpl_scheme scheme, int64_t M, int64_t K, int64_t R) {
+  const int64_t pitch = scheme == QPL_NVFP4 ? K / 2 : K;
+  if (pitch >= kMaxKBytePitch) return QPL_ERR_SHAPE;
+  if (R > 0) {
+    if (K > (int64_t(1) << 21)) return QPL_ERR_SHAPE;
+    const int64_t sc = scheme == QPL_NVFP4 ? 8 * nvfp4_slabs(K) : 4 * (K / 64);
+    if (M >= (int64_t(1) << 31) / sc) return QPL_ERR_SHAPE;
+  }
+  return QPL_OK;
+}
+
 // The current device must be a gfx950; the answer is cached per device ordinal.
 std::atomic<int> g_device_state[64];
 
@@ -60,8 +80,9 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 int64_t rank_pad(int64_t R) { return (R + 31) / 32 * 32; }
 
-// Workspace layout.  fp8r: [xq: M*K bytes][xs: 4*M bytes].  nvfp4: [xe: 2*M*K]
-// [we: 2*N*K] (bf16 expansions of the quantized activations and weights).  INT4:
+// Workspace layout.  fp8r: [xq: M*K bytes][xs: 4*M bytes].  nvfp4: [xq: M*K/2 packed
+// E2M1 codes][xs: 8*M*S block scales slab-major [S, M, 8]], S = ceil(K/128), and, as
+// part 5, [wsl: 8*N*S] the weight's block scales in the same layout.  INT4:
 // [xq: M*K][w8: N*K] (code values as E4M3 bytes) and, as parts 5 and 6, the
 // group-major scales [xs: 4*M*K/64][ws: 4*N*K/64].
 // nvfp4 and INT4 then, when R > 0, [l1t: 2*rpad*K][t: 2*M*KL][l2t: 2*N*KL] with
@@ -78,18 +99,21 @@ Layout layout(qpl_scheme scheme, int64_t M, int64_t K, int64_t N, int64_t R) {
     parts[0] = size_t(M) * size_t(K);
     parts[1] = size_t(4) * size_t(M);
   } else {
-    const size_t eb = scheme == QPL_INT4 ? 1 : 2;  // bytes per expanded element
-    parts[0] = eb * size_t(M) * size_t(K);
-    parts[1] = eb * size_t(N) * size_t(K);
+    if (scheme == QPL_NVFP4) {
+      parts[0] = size_t(M) * size_t(K / 2);
+      parts[1] = size_t(8) * size_t(M) * size_t(nvfp4_slabs(K));
+      parts[5] = size_t(8) * size_t(N) * size_t(nvfp4_slabs(K));
+    } else {
+      parts[0] = size_t(M) * size_t(K);
+      parts[1] = size_t(N) * size_t(K);
+      parts[5] = size_t(4) * size_t(M) * size_t(K / 64);
+      parts[6] = size_t(4) * size_t(N) * size_t(K / 64);
+    }
     if (R > 0) {
       const int64_t rp = rank_pad(R), kl = 2 * rp;
       parts[2] = size_t(2) * size_t(rp) * size_t(K);
       parts[3] = size_t(2) * size_t(M) * size_t(kl);
       parts[4] = size_t(2) * size_t(N) * size_t(kl);
-    }
-    if (scheme == QPL_INT4) {
-      parts[5] = size_t(4) * size_t(M) * size_t(K / 64);
-      parts[6] = size_t(4) * size_t(N) * size_t(K / 64);
     }
   }
   size_t o = 0;
@@ -199,6 +223,7 @@ qpl_status fp8r_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const
     return QPL_ERR_ALIGN;
   qpl_status s = check_gemm_dims(M, K, N);
   if (s != QPL_OK) return s;
+  if ((s = check_gemm_k(QPL_FP8R, M, K, 0)) != QPL_OK) return s;
   qpl::Epilogue ep;
   if ((s = epilogue_of(epi, M, N, y, ep)) != QPL_OK) return s;
   const Layout L = layout(QPL_FP8R, M, K, N, 0);
@@ -227,43 +252,46 @@ qpl_status check_nvfp4_layer(const uint8_t* weight, const uint8_t* weight_scale,
   if (R > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return QPL_ERR_ALIGN;
   if (!positive_finite(weight_scale_2) || !positive_finite(input_scale) || !positive_finite(6.0f * input_scale))
     return QPL_ERR_ARG;
-  if (!std::isfinite(input_scale * weight_scale_2)) return QPL_ERR_ARG;
+  // the product scales the fp32 4-bit product: finite and normal
+  const float g = input_scale * weight_scale_2;
+  if (!(g >= 0x1p-126f && g <= 0x1.fffffep127f)) return QPL_ERR_ARG;
   return QPL_OK;
 }
 
 // The steps of an nvfp4 linear before its GEMM, in the workspace laid out by L at
-// base: the activation quantize (fused with T = x L1 when R > 0) into xe and the
-// weight expansion into we.
-qpl_status nvfp4_operands(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
-                          const uint8_t* weight_scale, float gscale, float input_scale, const float* smooth,
-                          const uint16_t* lora_down, const uint16_t* lora_up, int64_t R, const Layout& L,
-                          uint8_t* base, hipStream_t st, qpl::LowRank& lr) {
+// base: one preparation launch (the weight's block scales into the GEMM's layout,
+// and the low-rank factor layouts when R > 0), then the activation quantize into
+// packed codes and slab-major block scales (fused with T = x L1 when R > 0).
+qpl_status nvfp4_operands(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight_scale,
+                          float input_scale, const float* smooth, const uint16_t* lora_down, const uint16_t* lora_up,
+                          int64_t R, const Layout& L, uint8_t* base, hipStream_t st, qpl::LowRank& lr) {
   qpl_status s;
-  uint16_t* xe = reinterpret_cast<uint16_t*>(base + L.off[0]);
-  uint16_t* we = reinterpret_cast<uint16_t*>(base + L.off[1]);
+  uint8_t* xq = base + L.off[0];
+  uint8_t* xs = base + L.off[1];
+  uint8_t* wsl = base + L.off[5];
   lr = qpl::LowRank{};
   if (R > 0) {
-    // SVDQuant branch: the weight expansion, which also writes the factor layouts,
-    // then the activation quantize fused with T = x L1 (it reads L1^T)
+    // SVDQuant branch: the factor layouts come with the preparation; the quantizer
+    // fused with T = x L1 reads L1^T
     const int64_t kl = 2 * rank_pad(R);
     uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.off[2]);
     uint16_t* t = reinterpret_cast<uint16_t*>(base + L.off[3]);
     uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
     const qpl::LowRankPrep prep{lora_down, lora_up, K, N, R, kl / 2, kl, l1t, l2t};
-    if ((s = launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(
-             qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st, &prep)))) != QPL_OK)
+    if ((s = launched(Timed(QPL_KERNEL_NVFP4_PREP, st)(
+             qpl::launch_nvfp4_prep(weight_scale, N, K, wsl, M, xs, &prep, st)))) != QPL_OK)
       return s;
     lr.t = t;
     lr.l2t = l2t;
     lr.kl = kl;
     return launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
-        qpl::launch_quant_nvfp4_expand_lowrank(x, M, K, input_scale, smooth, l1t, kl, gscale, xe, t, st)));
+        qpl::launch_quant_nvfp4_lowrank(x, M, K, input_scale, smooth, l1t, kl, xq, xs, t, st)));
   }
-  if ((s = launched(Timed(QPL_KERNEL_QUANT_NVFP4_BF16, st)(
-           qpl::launch_quant_nvfp4_expand(x, M, K, input_scale, smooth, xe, st)))) != QPL_OK)
+  if ((s = launched(Timed(QPL_KERNEL_NVFP4_PREP, st)(
+           qpl::launch_nvfp4_prep(weight_scale, N, K, wsl, M, xs, nullptr, st)))) != QPL_OK)
     return s;
-  // weight values e2m1(code) * dec(sf) in bf16 (exact); weight_scale_2 goes to the epilogue
-  return launched(Timed(QPL_KERNEL_WEIGHT_BF16, st)(qpl::launch_dequant_nvfp4(weight, weight_scale, 1.0f, N, K, we, st)));
+  return launched(Timed(QPL_KERNEL_QUANT_NVFP4_LINEAR, st)(
+      qpl::launch_quant_nvfp4_slab(x, M, K, input_scale, smooth, xq, xs, st)));
 }
 
 qpl_status nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
@@ -275,6 +303,7 @@ qpl_status nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, cons
   qpl_status s = check_nvfp4_layer(weight, weight_scale, weight_scale_2, input_scale, smooth, lora_down, lora_up, R);
   if (s != QPL_OK) return s;
   if ((s = check_gemm_dims(M, K, N)) != QPL_OK) return s;
+  if ((s = check_gemm_k(QPL_NVFP4, M, K, R)) != QPL_OK) return s;
   qpl::Epilogue ep;
   if ((s = epilogue_of(epi, M, N, y, ep)) != QPL_OK) return s;
   const float gscale = input_scale * weight_scale_2;
@@ -284,13 +313,12 @@ qpl_status nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   qpl::LowRank lr;
-  if ((s = nvfp4_operands(x, M, K, N, weight, weight_scale, gscale, input_scale, smooth, lora_down, lora_up, R, L,
-                          base, st, lr)) != QPL_OK)
+  if ((s = nvfp4_operands(x, M, K, N, weight_scale, input_scale, smooth, lora_down, lora_up, R, L, base, st, lr)) !=
+      QPL_OK)
     return s;
-  const uint16_t* xe = reinterpret_cast<const uint16_t*>(base + L.off[0]);
-  const uint16_t* we = reinterpret_cast<const uint16_t*>(base + L.off[1]);
   return launched(Timed(gemm_kind(ep, R > 0 ? QPL_KERNEL_GEMM_NVFP4_LOWRANK : QPL_KERNEL_GEMM_NVFP4), st)(
-      qpl::launch_gemm_nvfp4(xe, we, gscale, M, K, N, lr, ep, y, st)));
+      qpl::launch_gemm_nvfp4(base + L.off[0], base + L.off[1], weight, base + L.off[5], gscale, M, K, N, lr, ep, y,
+                             st)));
 }
 
 }  // namespace
@@ -344,6 +372,7 @@ QPL_EXPORT size_t qlinear_workspace_bytes(qpl_scheme scheme, int64_t M, int64_t 
   if (check_gemm_dims(M, K, N) != QPL_OK || R < 0 || R > kMaxRank) return 0;
   if (scheme == QPL_INT4 && K % 64 != 0) return 0;
   if (scheme == QPL_FP8R && R != 0) return 0;
+  if (check_gemm_k(scheme, M, K, R) != QPL_OK) return 0;
   return layout(scheme, M, K, N, R).total;
 }
 
@@ -404,9 +433,9 @@ namespace {
 
 // GELU MLP: fc1 with the GELU epilogue writes h, then fc2 runs on h (its quantize,
 // fused with x L1 when it has a low-rank branch, then its GEMM).  Workspace:
-// [fc2's nvfp4 layout for (M, H, N, R2), whose first part is fc2's expanded
-// operand][h: 2 M H][fc1's nvfp4 layout for (M, K, H, R1)], each part rounded up
-// to 256 bytes.
+// [fc2's nvfp4 layout for (M, H, N, R2), whose first parts are fc2's packed
+// activation codes and slab-major block scales][h: 2 M H][fc1's nvfp4 layout for
+// (M, K, H, R1)], each part rounded up to 256 bytes.
 struct MlpLayout {
   size_t h = 0, fc1 = 0, total = 0;
   Layout l1, l2;
@@ -428,6 +457,7 @@ QPL_EXPORT size_t qlinear_mlp_nvfp4_workspace_bytes(int64_t M, int64_t K, int64_
                                                     int64_t R2) {
   if (check_gemm_dims(M, K, H) != QPL_OK || check_gemm_dims(M, H, N) != QPL_OK) return 0;
   if (R1 < 0 || R1 > kMaxRank || R2 < 0 || R2 > kMaxRank) return 0;
+  if (check_gemm_k(QPL_NVFP4, M, K, R1) != QPL_OK || check_gemm_k(QPL_NVFP4, M, H, R2) != QPL_OK) return 0;
   return mlp_layout(M, K, H, N, R1, R2).total;
 }
 
@@ -443,6 +473,8 @@ QPL_EXPORT qpl_status qlinear_mlp_nvfp4(const uint16_t* x, int64_t M, int64_t K,
                              fc2->lora_down, fc2->lora_up, fc2->R)) != QPL_OK)
     return s;
   if ((s = check_gemm_dims(M, K, H)) != QPL_OK || (s = check_gemm_dims(M, H, N)) != QPL_OK) return s;
+  if ((s = check_gemm_k(QPL_NVFP4, M, K, fc1->R)) != QPL_OK || (s = check_gemm_k(QPL_NVFP4, M, H, fc2->R)) != QPL_OK)
+    return s;
   const MlpLayout L = mlp_layout(M, K, H, N, fc1->R, fc2->R);
   if (ws_bytes < L.total) return QPL_ERR_WORKSPACE;
   if ((s = check_device()) != QPL_OK) return s;
@@ -513,6 +545,7 @@ qpl_status int4_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const
   if (s != QPL_OK) return s;
   if (K % 64 != 0) return QPL_ERR_SHAPE;
   if (R < 0 || R > kMaxRank) return QPL_ERR_SHAPE;
+  if ((s = check_gemm_k(QPL_INT4, M, K, R)) != QPL_OK) return s;
   if (R > 0 && (!lora_down || !lora_up)) return QPL_ERR_NULL;
   if (R == 0 && (lora_down || lora_up)) return QPL_ERR_ARG;
   if (R > 0 && (!aligned16(lora_down) || !aligned16(lora_up))) return QPL_ERR_ALIGN;

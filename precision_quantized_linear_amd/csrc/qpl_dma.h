@@ -33,10 +33,13 @@ __device__ __forceinline__ u32x4 make_desc(const void* base, int64_t bytes) {
 // [lds_addr + 16 l, + 16); an offset past the descriptor's size writes zeros.  It
 // is inline assembly so that the compiler does not wait for these loads at every
 // LDS read: the pipelines count them themselves (QPL_WAIT_VMCNT).
+// The LDS address and soffset are wave-uniform; readfirstlane makes them scalar
+// operands even where the compiler keeps a uniform value in a vector register.
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, u32x4 desc, int soffset) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soffset)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(desc),
+                 "s"(__builtin_amdgcn_readfirstlane(soffset))
                : "memory");
 }
 
@@ -46,7 +49,8 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, u32x4 de
 __device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, u32x4 desc, int soffset) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soffset)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(desc),
+                 "s"(__builtin_amdgcn_readfirstlane(soffset))
                : "memory");
 }
 

@@ -22,18 +22,18 @@ hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t
 // lam: SVDQuant smoothing factors [K] (x is divided by them first) or nullptr.
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
                               uint8_t* xbs, hipStream_t stream);
-// nvfp4 quantization that writes each quantized value e2m1(q) * dec(sf) as bf16
-// (exact: at most 6 significant bits) instead of packed codes.
-hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
-                                     uint16_t* xe, hipStream_t stream);
+// The nvfp4 quantizer of the linear layer: packed codes [M, K/2] (as quant_act_nvfp4)
+// and block scales slab-major [ceil(K/128), M, 8] (the GEMM's layout; bytes past
+// K/16 are written as zeros by launch_nvfp4_prep).
+hipError_t launch_quant_nvfp4_slab(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
+                                   uint8_t* xs, hipStream_t stream);
 // The same, fused with the low-rank down-projection: t [M, kl] bf16 receives
-// T / tdiv (T = x L1, fp32, one correctly rounded division) as [hi | lo] halves of
-// kl / 2 columns each; l1t [kl / 2, K] is L1 transposed (zero past R); kl / 2 is
-// a multiple of 32, at most 128.  With lam, both the quantized values and T are
-// computed from the smoothed activation.
-hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
-                                             const uint16_t* l1t, int64_t kl, float tdiv, uint16_t* xe, uint16_t* t,
-                                             hipStream_t stream);
+// T = x L1 (fp32) as [hi | lo] bf16 halves of kl / 2 columns each; l1t [kl / 2, K]
+// is L1 transposed (zero past R); kl / 2 is a multiple of 32, at most 128.  With
+// lam, both the codes and T are computed from the smoothed activation.
+hipError_t launch_quant_nvfp4_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                      const uint16_t* l1t, int64_t kl, uint8_t* xq, uint8_t* xs, uint16_t* t,
+                                      hipStream_t stream);
 // INT4 (svdq_w4a4 INT4 variant): group-wise quantizer, writing packed codes and
 // scales [M, K/64], or (f8, for the GEMM) the E4M3 bytes of the code values and
 // scales group-major [K/64, M]; and the packed -> E4M3 byte expansion of a weight,
@@ -43,7 +43,7 @@ hipError_t launch_quant_int4(const uint16_t* x, int64_t M, int64_t K, const floa
 hipError_t launch_expand_int4(const uint8_t* wq, const float* ws, int64_t N, int64_t K, uint8_t* w8, float* wst,
                               hipStream_t stream);
 // The INT4 quantizer (E4M3 code bytes, group-major scales) fused with T = x L1,
-// stored as in launch_quant_nvfp4_expand_lowrank with tdiv = 1.
+// stored as in launch_quant_nvfp4_lowrank.
 hipError_t launch_quant_int4_lowrank(const uint16_t* x, int64_t M, int64_t K, const float* lam, const uint16_t* l1t,
                                      int64_t kl, uint8_t* xq, float* xs, uint16_t* t, hipStream_t stream);
 
@@ -65,9 +65,15 @@ struct LowRankPrep {
   uint16_t* l1t = nullptr;
   uint16_t* l2t = nullptr;
 };
-// lr: also write those layouts, in the same launch.
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K,
-                                uint16_t* out, hipStream_t stream, const LowRankPrep* lr = nullptr);
+                                uint16_t* out, hipStream_t stream);
+// What an nvfp4 linear prepares before its quantizer, in one launch: the weight
+// block scales [N, K/16] copied into the GEMM's slab-major layout wsl
+// [ceil(K/128), N, 8] (zero past K/16), zeros over the activation scales' last
+// slab xs [ceil(K/128) - 1, M, 8] when K/16 is not a multiple of 8, and (lr) the
+// factor layouts of the low-rank branch.
+hipError_t launch_nvfp4_prep(const uint8_t* wbs, int64_t N, int64_t K, uint8_t* wsl, int64_t M, uint8_t* xs,
+                             const LowRankPrep* lr, hipStream_t stream);
 
 // What a GEMM's epilogue writes (default: y = bf16 result, row-major [M, N]).
 // gelu: the tanh form of GELU on the fp32 result before the bf16 rounding.
@@ -83,7 +89,7 @@ struct Epilogue {
 hipError_t launch_gemm_fp8r(const uint8_t* xq, const float* xs, const uint8_t* w, const float* ws,
                             int64_t M, int64_t K, int64_t N, const Epilogue& ep, uint16_t* y, hipStream_t stream);
 
-// Low-rank operands for the nvfp4 GEMM epilogue: t [M, KL] bf16 holds T = x L1 split
+// Low-rank operands of the GEMMs' second pass: t [M, KL] bf16 holds T = x L1 split
 // into hi and lo bf16 halves, l2t [N, KL] bf16 holds L2^T twice; KL = 2 * ceil(R/32) * 32.
 struct LowRank {
   const uint16_t* t = nullptr;
@@ -91,18 +97,20 @@ struct LowRank {
   int64_t kl = 0;
 };
 
-// xe [M,K] and we [N,K] are the bf16 expansions e2m1(code) * dec(sf) of the
-// quantized activations and weights; y = bf16(gscale * xe we^T [+ low-rank term]).
-hipError_t launch_gemm_nvfp4(const uint16_t* xe, const uint16_t* we, float gscale, int64_t M, int64_t K, int64_t N,
-                             LowRank lr, const Epilogue& ep, uint16_t* y, hipStream_t stream);
+// The nvfp4 GEMM on packed operands: xq [M, K/2] and wq [N, K/2] E2M1 codes, xs
+// [S, M, 8] and wsc [S, N, 8] E4M3 block scales (S = ceil(K/128), zero past K/16);
+// y = bf16(gscale xq wq^T [+ T L2]).
+hipError_t launch_gemm_nvfp4(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* wsc,
+                             float gscale, int64_t M, int64_t K, int64_t N, LowRank lr, const Epilogue& ep, uint16_t* y,
+                             hipStream_t stream);
 
-// Factor layouts for the low-rank branch: l1t [kl / 2, K] = L1^T and l2t [N, kl] =
-// [L2^T | L2^T], both zero past R.
 // INT4 GEMM: x8 [M, K] and w8 [N, K] code values as E4M3 bytes, xs [K/64, M] and
 // ws [K/64, N] fp32 group scales (group-major), K % 64 == 0; optional low-rank
-// pass (tdiv 1).
+// pass.
 hipError_t launch_gemm_int4(const uint8_t* x8, const float* xs, const uint8_t* w8, const float* ws, int64_t M,
                             int64_t K, int64_t N, LowRank lr, const Epilogue& ep, uint16_t* y, hipStream_t stream);
+// Factor layouts for the low-rank branch: l1t [kl / 2, K] = L1^T and l2t [N, kl] =
+// [L2^T | L2^T], both zero past R.
 hipError_t launch_lowrank_prep(const uint16_t* l1, const uint16_t* l2, int64_t K, int64_t N, int64_t R, int64_t kl,
                                uint16_t* l1t, uint16_t* l2t, hipStream_t stream);
 

@@ -158,11 +158,13 @@ __device__ __forceinline__ void smooth_block(uint32_t (&p)[8], const float* __re
 }
 
 
-// SMOOTH: the block is first smoothed by lam (kb = K / 16 blocks per row).
-template <bool SMOOTH>
+// SMOOTH: the block is first smoothed by lam (kb = K / 16 blocks per row).  SLAB:
+// the scales go slab-major [ceil(K/128), rows, 8] (the GEMM's operand layout;
+// byte 8 s + i of a row's scales is block 8 s + i) instead of row-major [rows, kb].
+template <bool SMOOTH, bool SLAB>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict__ x, int64_t nblocks,
                                                      float c6g, float rc6g, Nvfp4ScaleTable tab,
-                                                     const float* __restrict__ lam, int64_t kb,
+                                                     const float* __restrict__ lam, int64_t kb, int64_t rows,
                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xbs) {
   __shared__ float tab_d[128], tab_rd[128];
   load_scale_table(tab, tab_d, tab_rd);
@@ -173,63 +175,15 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict_
   smooth_block<SMOOTH>(p, lam, b, kb);
   const Nvfp4Block s = nvfp4_scale(block_absmax(p, 8), c6g, rc6g, tab_d, tab_rd);
   reinterpret_cast<u32x2*>(xq)[b] = u32x2{nvfp4_word<true>(p, s), nvfp4_word<true>(p + 4, s)};
-  xbs[b] = (uint8_t)s.sf;
-}
-
-// Same quantization; each quantized value e2m1(code) * dec(sf) is written as bf16.
-// The product has at most 6 significant bits, so the bf16 value is exact.
-//
-// Layout: the tensor is a flat array of 16-byte vectors (eight bf16); vector j is
-// half j % 2 of block j / 2, so lanes l and l ^ 1 hold one block and every load and
-// store instruction of a wavefront covers 1 KB of consecutive bytes.  The block's
-// largest magnitude meets across the lane pair through DPP (quad_perm 1,0,3,2).  A
-// workgroup takes EXPAND_U runs of 256 consecutive vectors and issues all its loads
-// before it fills the scale table, so the table's latency overlaps theirs.  Stores
-// are plain: the GEMM reads this output next, and streaming (nontemporal) stores
-// made that GEMM measurably slower.
-constexpr int EXPAND_U = 4;
-
-template <bool SMOOTH>
-__global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __restrict__ x, int64_t nvec,
-                                                            float c6g, float rc6g, Nvfp4ScaleTable tab,
-                                                            const float* __restrict__ lam, int64_t kv,
-                                                            uint16_t* __restrict__ xe) {
-  __shared__ float tab_d[128], tab_rd[128];
-  const int64_t base = (int64_t)blockIdx.x * 256 * EXPAND_U + threadIdx.x;
-  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  u32x4 v[EXPAND_U];
-#pragma unroll
-  for (int u = 0; u < EXPAND_U; ++u) {
-    const int64_t j = base + 256 * u;
-    v[u] = j < nvec ? __builtin_nontemporal_load(xv + j) : u32x4{0u, 0u, 0u, 0u};
-  }
-  load_scale_table(tab, tab_d, tab_rd);
-#pragma unroll
-  for (int u = 0; u < EXPAND_U; ++u) {
-    // nvec is even, so both lanes of a pair are in range or neither is, and every
-    // lane takes part in the DPP exchange
-    const int64_t j = base + 256 * u;
-    uint32_t p[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-    if constexpr (SMOOTH) {
-      if (j < nvec) {
-        const f32x4* l = reinterpret_cast<const f32x4*>(lam + (j % kv) * 8);
-        const f32x4 a = l[0], b = l[1];
-        p[0] = smooth_pair(p[0], a[0], a[1]);
-        p[1] = smooth_pair(p[1], a[2], a[3]);
-        p[2] = smooth_pair(p[2], b[0], b[1]);
-        p[3] = smooth_pair(p[3], b[2], b[3]);
-      }
-    }
-    uint32_t m = absmax_acc(absmax_acc(absmax_acc(absmax_acc(0u, p[0]), p[1]), p[2]), p[3]);
-    m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
-    const Nvfp4Block s = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
-    uint32_t o[4];
-    expand_word(nvfp4_word<false>(p, s), s.dsf, o);
-    if (j < nvec) reinterpret_cast<u32x4*>(xe)[j] = u32x4{o[0], o[1], o[2], o[3]};
+  if constexpr (SLAB) {
+    const int64_t row = b / kb, j = b - row * kb;
+    xbs[((j >> 3) * rows + row) * 8 + (j & 7)] = (uint8_t)s.sf;
+  } else {
+    xbs[b] = (uint8_t)s.sf;
   }
 }
 
-// nvfp4 quantize-and-expand fused with the SVDQuant low-rank down-projection
+// nvfp4 quantization fused with the SVDQuant low-rank down-projection
 // T = x L1 (the pages fuse the down-projection into the quantization kernel so
 // that the 16-bit branch does not read x a second time: "Bringing Nunchaku 4-bit
 // Diffusion Inference to Diffusers", section "Background: SVDQuant and
@@ -241,14 +195,14 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_expand(const uint16_t* __re
 // staging, S - 1 tiles ahead; a load instruction covers whole 512- or 256-byte row
 // segments, so HBM sees full lines.  Per tile, the wavefronts
 //   1. quantize their eighth of the x tile from LDS (lane l holds eight values,
-//      lanes l and l ^ 1 one 16-element block) and store the bf16 expansion
-//      straight to global memory, again as whole row segments;
+//      lanes l and l ^ 1 one 16-element block) and store the packed codes (4 bytes
+//      per lane) and, from the block's first lane, its scale byte in the GEMM's
+//      slab-major layout [K/128][M][8];
 //   2. run the bf16 MFMA 32x32x16 over their eighth of the tile's k range,
 //      reading both operands from LDS, into per-wave partial sums of T.
 // Two wavefronts per SIMD keep the quantizer's arithmetic busy.  The eight partial
-// sums meet in LDS at the end, in a fixed order; T / tdiv is stored as [hi | lo]
-// bf16 halves (row stride kl = 2 rpad) for the GEMM's low-rank pass (tdiv is the
-// GEMM's output scale, which the pass's result is multiplied by again).
+// sums meet in LDS at the end, in a fixed order; T is stored as [hi | lo] bf16
+// halves (row stride kl = 2 rpad) for the GEMM's low-rank pass.
 //
 // LDS layout: 16-byte chunk c of tile row r sits at chunk slot c ^ (r & 15) of
 // the row, so the MFMA operand reads (16 rows, one chunk) hit 16 different bank
@@ -280,17 +234,18 @@ struct LrTile {
   static constexpr int XI = XB / 1024 / NW;         // x loads (and xe stores) per wave per tile, 1 KB each
   static constexpr int LI = LB / 1024 / NW;         // L1^T loads per wave per tile
   static constexpr int DW = XI + LI + (SMOOTH ? 1 : 0);  // loads per wave per tile
-  static constexpr int SPT = INT4 ? 2 * XI : XI;          // stores per wave per tile
+  static constexpr int SPT = 2 * XI;                      // stores per wave per tile (codes, scales)
 };
 
-// xq: the bf16 expansion [M, K] (nvfp4) or the E4M3 code bytes [M, K] (INT4);
-// xs: the INT4 group scales [M, K/64] (unused for nvfp4).
+// xq: the packed E2M1 codes [M, K/2] (nvfp4) or the E4M3 code bytes [M, K] (INT4);
+// xs: the nvfp4 block scales slab-major [ceil(K/128), M, 8] (bytes) or the INT4
+// group scales group-major [K/64, M] (floats).
 template <int NCT, bool SMOOTH, bool INT4>
 __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                            float c6g, float rc6g, Nvfp4ScaleTable tab,
                                                            const uint16_t* __restrict__ l1t, int64_t kl,
-                                                           const float* __restrict__ lam, int rpw, float tdiv,
-                                                           uint8_t* __restrict__ xq, float* __restrict__ xs,
+                                                           const float* __restrict__ lam, int rpw,
+                                                           uint8_t* __restrict__ xq, void* __restrict__ xs,
                                                            uint16_t* __restrict__ t_out) {
   using C = LrTile<NCT, SMOOTH, INT4>;
   constexpr int TK = C::TK, CPR = C::CPR, S = C::S, XI = C::XI, LI = C::LI, NW = C::NW;
@@ -305,12 +260,14 @@ __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __res
   const u32x4 dx = make_desc(x + m0 * K, rows * pitch);
   const u32x4 dl = make_desc(l1t, (int64_t)32 * NCT * pitch);
   const u32x4 df = make_desc(lam, SMOOTH ? K * 4 : 0);
-  const int64_t qpitch = INT4 ? K : 2 * K;  // bytes per row of xq
+  const int64_t qpitch = INT4 ? K : K / 2;  // bytes per row of xq
   const int64_t ng = K / 64;
   const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(xq + m0 * qpitch, (short)0,
                                                                       (int)(rows * qpitch), (int)kRawBufferWord3);
-  // INT4 scales group-major [K/64, M] (the GEMM's layout); M K / 16 < 2^31 bytes
-  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(xs, (short)0, INT4 ? (int)(M * ng * 4) : 0,
+  // scales: INT4 group-major [K/64, M] floats, nvfp4 slab-major [ceil(K/128), M, 8]
+  // bytes (the GEMMs' layouts); both below 2^31 bytes (checked by the host)
+  const int64_t sc_bytes = INT4 ? M * ng * 4 : ((K + 127) / 128) * M * 8;
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(xs, (short)0, (int)sc_bytes,
                                                                        (int)kRawBufferWord3);
   const uint32_t lbase = lds_address(lds);
   const int ntiles = (int)((K + TK - 1) / TK);
@@ -375,7 +332,8 @@ __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __res
           __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, re, (int)kOutOfRange, 0, 0);
           __builtin_amdgcn_raw_buffer_store_b32(0u, rsc, (int)kOutOfRange, 0, 0);
         } else {
-          __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, re, (int)kOutOfRange, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(0u, re, (int)kOutOfRange, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, rsc, (int)kOutOfRange, 0, 0);
         }
         continue;
       }
@@ -428,12 +386,15 @@ __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __res
             in_k && (c & 7) == 0 && r < rows ? (int)(((k0 / 64) * M + m0 + r) * 4) : (int)kOutOfRange, 0, 0);
       } else {
         const Nvfp4Block sc = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
-        uint32_t o[4];
-        expand_word(nvfp4_word<false>(p, sc), sc.dsf, o);
-        const uint32_t so = voff(r, c, kt);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, re,
-                                               so == kOutOfRange ? (int)kOutOfRange : (int)(so + (uint32_t)kt * TK * 2),
-                                               0, 0);
+        const int64_t k0 = (int64_t)kt * TK + 8 * c;
+        const bool in_k = k0 < K;
+        __builtin_amdgcn_raw_buffer_store_b32(nvfp4_word<true>(p, sc), re,
+                                              in_k ? (int)(r * qpitch + k0 / 2) : (int)kOutOfRange, 0, 0);
+        // the block's scale, from the lane holding its first half (even chunk)
+        const int64_t jb = k0 / 16;
+        __builtin_amdgcn_raw_buffer_store_b8(
+            (uint8_t)sc.sf, rsc,
+            in_k && (c & 1) == 0 && r < rows ? (int)(((jb >> 3) * M + m0 + r) * 8 + (jb & 7)) : (int)kOutOfRange, 0, 0);
       }
     }
 
@@ -492,7 +453,7 @@ __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __res
       const int mr = q * 8 + (l >> 5) * 4 + i;
       if (mr >= rows) continue;
       const int64_t m = m0 + mr;
-      const float tv = v[i] / tdiv;
+      const float tv = v[i];
       const uint32_t hi = f32_to_bf16(tv);
       const uint32_t lo = f32_to_bf16(tv - __uint_as_float(hi << 16));
       t_out[m * kl + 32 * c + (l & 31)] = (uint16_t)hi;
@@ -637,56 +598,53 @@ Nvfp4ScaleTable nvfp4_scale_table(float g) {
   return t;
 }
 
-hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
-                              uint8_t* xbs, hipStream_t stream) {
+template <bool SLAB>
+static hipError_t launch_nvfp4_blocks(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
+                                      uint8_t* xbs, hipStream_t stream) {
   const int64_t nb = M * (K / 16);
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
   const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
   if (lam)
-    hipLaunchKernelGGL(k_quant_nvfp4<true>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g), lam,
-                       K / 16, xq, xbs);
+    hipLaunchKernelGGL((k_quant_nvfp4<true, SLAB>), grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
+                       lam, K / 16, M, xq, xbs);
   else
-    hipLaunchKernelGGL(k_quant_nvfp4<false>, grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g), lam,
-                       K / 16, xq, xbs);
+    hipLaunchKernelGGL((k_quant_nvfp4<false, SLAB>), grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
+                       lam, K / 16, M, xq, xbs);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_nvfp4_expand(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
-                                     uint16_t* xe, hipStream_t stream) {
-  const int64_t nb = M * (K / 16);
-  const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  const int64_t nvec = 2 * nb;
-  const dim3 grid((unsigned)((nvec + 256 * EXPAND_U - 1) / (256 * EXPAND_U))), block(256);
-  if (lam)
-    hipLaunchKernelGGL(k_quant_nvfp4_expand<true>, grid, block, 0, stream, x, nvec, c6g, rc6g,
-                       nvfp4_scale_table(g), lam, K / 8, xe);
-  else
-    hipLaunchKernelGGL(k_quant_nvfp4_expand<false>, grid, block, 0, stream, x, nvec, c6g, rc6g,
-                       nvfp4_scale_table(g), lam, K / 8, xe);
-  return hipGetLastError();
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
+                              uint8_t* xbs, hipStream_t stream) {
+  return launch_nvfp4_blocks<false>(x, M, K, g, lam, xq, xbs, stream);
+}
+
+hipError_t launch_quant_nvfp4_slab(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
+                                   uint8_t* xs, hipStream_t stream) {
+  return launch_nvfp4_blocks<true>(x, M, K, g, lam, xq, xs, stream);
 }
 
 template <int NCT, bool SMOOTH, bool INT4>
 static void launch_act_lr(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K, float c6g,
                           float rc6g, const Nvfp4ScaleTable& tab, const uint16_t* l1t, int64_t kl, const float* lam,
-                          int rpw, float tdiv, uint8_t* xq, float* xs, uint16_t* t) {
+                          int rpw, uint8_t* xq, void* xs, uint16_t* t) {
   hipLaunchKernelGGL((k_quant_act_lowrank<NCT, SMOOTH, INT4>), grid, dim3(512), 0, stream, x, M, K, c6g, rc6g, tab,
-                     l1t, kl, lam, rpw, tdiv, xq, xs, t);
+                     l1t, kl, lam, rpw, xq, xs, t);
 }
 
 template <bool INT4>
 static hipError_t launch_act_lowrank(const uint16_t* x, int64_t M, int64_t K, float c6g, float rc6g,
                                      const Nvfp4ScaleTable& tab, const float* lam, const uint16_t* l1t, int64_t kl,
-                                     float tdiv, uint8_t* xq, float* xs, uint16_t* t, hipStream_t stream) {
-  // buffer offsets are 32-bit: the L1^T tile rows (at most 128) times the pitch
+                                     uint8_t* xq, void* xs, uint16_t* t, hipStream_t stream) {
+  // buffer offsets are 32-bit: the L1^T tile rows (at most 128) times the pitch (the
+  // host checks this and the scale buffer's size before anything is queued)
   if (K > (int64_t{1} << 21)) return hipErrorInvalidValue;
   // about one workgroup per CU (256 on MI355X), at most 32 rows each
   const int64_t rpw64 = (M + 255) / 256;
   const int rpw = (int)(rpw64 < 32 ? rpw64 : 32);
   const dim3 grid((unsigned)((M + rpw - 1) / rpw));
-#define QPL_ACT_LR(NCT)                                                                                        \
-  (lam ? launch_act_lr<NCT, true, INT4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xq, xs, t) \
-       : launch_act_lr<NCT, false, INT4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, tdiv, xq, xs, t))
+#define QPL_ACT_LR(NCT)                                                                                   \
+  (lam ? launch_act_lr<NCT, true, INT4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, xq, xs, t) \
+       : launch_act_lr<NCT, false, INT4>(grid, stream, x, M, K, c6g, rc6g, tab, l1t, kl, lam, rpw, xq, xs, t))
   switch (kl / 64) {  // rpad / 32
     case 1: QPL_ACT_LR(1); break;
     case 2: QPL_ACT_LR(2); break;
@@ -698,18 +656,17 @@ static hipError_t launch_act_lowrank(const uint16_t* x, int64_t M, int64_t K, fl
   return hipGetLastError();
 }
 
-hipError_t launch_quant_nvfp4_expand_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
-                                             const uint16_t* l1t, int64_t kl, float tdiv, uint16_t* xe, uint16_t* t,
-                                             hipStream_t stream) {
+hipError_t launch_quant_nvfp4_lowrank(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                      const uint16_t* l1t, int64_t kl, uint8_t* xq, uint8_t* xs, uint16_t* t,
+                                      hipStream_t stream) {
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  return launch_act_lowrank<false>(x, M, K, c6g, rc6g, nvfp4_scale_table(g), lam, l1t, kl, tdiv,
-                                   reinterpret_cast<uint8_t*>(xe), nullptr, t, stream);
+  return launch_act_lowrank<false>(x, M, K, c6g, rc6g, nvfp4_scale_table(g), lam, l1t, kl, xq, xs, t, stream);
 }
 
 hipError_t launch_quant_int4_lowrank(const uint16_t* x, int64_t M, int64_t K, const float* lam, const uint16_t* l1t,
                                      int64_t kl, uint8_t* xq, float* xs, uint16_t* t, hipStream_t stream) {
   if (M * (K / 64) * 4 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
-  return launch_act_lowrank<true>(x, M, K, 0.0f, 0.0f, Nvfp4ScaleTable{}, lam, l1t, kl, 1.0f, xq, xs, t, stream);
+  return launch_act_lowrank<true>(x, M, K, 0.0f, 0.0f, Nvfp4ScaleTable{}, lam, l1t, kl, xq, xs, t, stream);
 }
 
 hipError_t launch_quant_int4(const uint16_t* x, int64_t M, int64_t K, const float* lam, bool f8, uint8_t* xq,
@@ -793,23 +750,16 @@ __global__ __launch_bounds__(256) void k_dequant_fp8r(const uint8_t* __restrict_
 // nvfp4 weight to bf16.  Output vector j (eight bf16) is half j % 2 of block j / 2:
 // one dword of packed codes in, one 16-byte vector out per lane and step, so loads
 // and stores of a wavefront are consecutive; DEQUANT_U steps per lane, loads first.
-// The hardware FP4 converter gives the code values exactly.  G1 (weight_scale_2 = 1,
-// the GEMM's expansion): the products with dec(sf) are exact in bf16 (at most 6
-// significant bits), so they are truncated into place.  Otherwise
+// The hardware FP4 converter gives the code values exactly; each value is
 // bf16_rne(fp32(e2m1 * dec(sf)) * g2).
 constexpr int DEQUANT_U = 4;
 
-template <bool G1>
 __device__ __forceinline__ void dequant_half(uint32_t w, float dsf, float g2, uint32_t* o) {
-  if constexpr (G1) {
-    expand_word(w, dsf, o);
-  } else {
-    auto out2 = [&](f32x2 v) { return pack_bf16((v[0] * dsf) * g2, (v[1] * dsf) * g2); };
-    o[0] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0));
-    o[1] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1));
-    o[2] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2));
-    o[3] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3));
-  }
+  auto out2 = [&](f32x2 v) { return pack_bf16((v[0] * dsf) * g2, (v[1] * dsf) * g2); };
+  o[0] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0));
+  o[1] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1));
+  o[2] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2));
+  o[3] = out2(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3));
 }
 
 // Factor layouts of the SVDQuant low-rank branch, one element per thread:
@@ -831,19 +781,9 @@ __global__ __launch_bounds__(256) void k_lowrank_transpose(LowRankPrep q) {
   lowrank_layout(q, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
-// LR: the first lr_blocks workgroups write the factor layouts instead (one launch
-// fewer per low-rank layer; their scattered reads overlap the expansion's stream).
-template <bool G1, bool LR>
 __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict__ w, const uint8_t* __restrict__ wbs,
-                                                       float g2, int64_t nvec, uint16_t* __restrict__ out,
-                                                       LowRankPrep q, unsigned lr_blocks) {
-  if constexpr (LR) {
-    if (blockIdx.x < lr_blocks) {
-      lowrank_layout(q, (int64_t)blockIdx.x * 256 + threadIdx.x);
-      return;
-    }
-  }
-  const int64_t base = (int64_t)(blockIdx.x - (LR ? lr_blocks : 0u)) * 256 * DEQUANT_U + threadIdx.x;
+                                                       float g2, int64_t nvec, uint16_t* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * 256 * DEQUANT_U + threadIdx.x;
   uint32_t c[DEQUANT_U], sc[DEQUANT_U];
 #pragma unroll
   for (int u = 0; u < DEQUANT_U; ++u) {
@@ -856,9 +796,48 @@ __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict
     const int64_t j = base + 256 * u;
     if (j < nvec) {
       uint32_t o[4];
-      dequant_half<G1>(c[u], e4m3_decode(sc[u]), g2, o);
+      dequant_half(c[u], e4m3_decode(sc[u]), g2, o);
       reinterpret_cast<u32x4*>(out)[j] = u32x4{o[0], o[1], o[2], o[3]};
     }
+  }
+}
+
+// Preparation of an nvfp4 linear (one launch, three kinds of workgroup):
+// * the weight's block scales [N, kb] (kb = K/16) into the GEMM's slab-major layout
+//   [S, N, 8] (S = ceil(kb/8)), zeros past kb: one thread per 8-byte unit, slab
+//   index fastest so that a wavefront reads consecutive bytes of a row;
+// * zeros over the activation scales' last slab [S - 1, M, 8] when kb % 8 != 0 (the
+//   quantizer then writes the bytes of the real blocks);
+// * with a low-rank branch, its factor layouts (lowrank_layout).
+struct Nvfp4Prep {
+  const uint8_t* wbs;
+  uint8_t* wsl;
+  uint8_t* xs;
+  int64_t N, M, kb, S;
+  unsigned wblocks, xblocks;
+};
+
+template <bool LR>
+__global__ __launch_bounds__(256) void k_nvfp4_prep(Nvfp4Prep a, LowRankPrep q) {
+  const unsigned blk = blockIdx.x;
+  if (blk < a.wblocks) {
+    const int64_t u = (int64_t)blk * 256 + threadIdx.x;
+    if (u >= a.N * a.S) return;
+    const int64_t n = u / a.S, sl = u - n * a.S;
+    const uint8_t* src = a.wbs + n * a.kb + 8 * sl;
+    const int64_t left = a.kb - 8 * sl;  // >= 1
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < left) lo |= (uint32_t)src[i] << (8 * i);
+      if (i + 4 < left) hi |= (uint32_t)src[i + 4] << (8 * i);
+    }
+    *reinterpret_cast<u32x2*>(a.wsl + (sl * a.N + n) * 8) = u32x2{lo, hi};
+  } else if (blk < a.wblocks + a.xblocks) {
+    const int64_t m = (int64_t)(blk - a.wblocks) * 256 + threadIdx.x;
+    if (m < a.M) *reinterpret_cast<u32x2*>(a.xs + ((a.S - 1) * a.M + m) * 8) = u32x2{0u, 0u};
+  } else if constexpr (LR) {
+    lowrank_layout(q, (int64_t)(blk - a.wblocks - a.xblocks) * 256 + threadIdx.x);
   }
 }
 
@@ -882,23 +861,32 @@ hipError_t launch_dequant_fp8r(const uint8_t* w, const float* ws, int64_t N, int
 }
 
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K, uint16_t* out,
-                                hipStream_t stream, const LowRankPrep* lr) {
+                                hipStream_t stream) {
   const int64_t nvec = N * K / 8;
-  const unsigned deq = (unsigned)((nvec + 256 * DEQUANT_U - 1) / (256 * DEQUANT_U));
+  const dim3 grid((unsigned)((nvec + 256 * DEQUANT_U - 1) / (256 * DEQUANT_U))), block(256);
+  hipLaunchKernelGGL(k_dequant_nvfp4, grid, block, 0, stream, w, wbs, g2, nvec, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_prep(const uint8_t* wbs, int64_t N, int64_t K, uint8_t* wsl, int64_t M, uint8_t* xs,
+                             const LowRankPrep* lr, hipStream_t stream) {
+  Nvfp4Prep a;
+  a.wbs = wbs;
+  a.wsl = wsl;
+  a.xs = xs;
+  a.N = N;
+  a.M = M;
+  a.kb = K / 16;
+  a.S = (a.kb + 7) / 8;
+  a.wblocks = (unsigned)((N * a.S + 255) / 256);
+  a.xblocks = a.kb % 8 != 0 ? (unsigned)((M + 255) / 256) : 0u;
   const LowRankPrep q = lr ? *lr : LowRankPrep{};
   const unsigned nlr = lr ? lowrank_blocks(q) : 0u;
-  const dim3 grid(deq + nlr), block(256);
-  if (g2 == 1.0f) {
-    if (lr)
-      hipLaunchKernelGGL((k_dequant_nvfp4<true, true>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
-    else
-      hipLaunchKernelGGL((k_dequant_nvfp4<true, false>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
-  } else {
-    if (lr)
-      hipLaunchKernelGGL((k_dequant_nvfp4<false, true>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
-    else
-      hipLaunchKernelGGL((k_dequant_nvfp4<false, false>), grid, block, 0, stream, w, wbs, g2, nvec, out, q, nlr);
-  }
+  const dim3 grid(a.wblocks + a.xblocks + nlr), block(256);
+  if (lr)
+    hipLaunchKernelGGL(k_nvfp4_prep<true>, grid, block, 0, stream, a, q);
+  else
+    hipLaunchKernelGGL(k_nvfp4_prep<false>, grid, block, 0, stream, a, q);
   return hipGetLastError();
 }
 

@@ -46,3 +46,28 @@ def adversarial_rows(K, seed=0):
     b[2::5] = 0x8000
     rows.append(b)                                                         # exact +-0 among normal values
     return np.stack(rows)
+
+
+def r256(b):
+    return (b + 255) // 256 * 256
+
+
+def nvfp4_workspace_parts(M, K, N, R=0):
+    """Byte offsets of qlinear_nvfp4's workspace parts (as include/qpl.h lays them
+    out): activation codes, activation block scales [S, M, 8], and the weight's
+    block scales [S, N, 8] (after the low-rank parts when R > 0)."""
+    S = (K + 127) // 128
+    off_xs = r256(M * K // 2)
+    end = off_xs + r256(8 * M * S)
+    if R > 0:
+        rp = (R + 31) // 32 * 32
+        end += r256(2 * rp * K) + r256(2 * M * 2 * rp) + r256(2 * N * 2 * rp)
+    return dict(xq=0, xs=off_xs, ws=end, S=S)
+
+
+def slab_scales_to_rows(buf, rows, K):
+    """uint8 [S, rows, 8] (slab-major block scales) -> ([rows, K/16] row-major, the
+    bytes past K/16).  Data movement only."""
+    S = (K + 127) // 128
+    a = np.asarray(buf, np.uint8).reshape(S, rows, 8).transpose(1, 0, 2).reshape(rows, S * 8)
+    return a[:, : K // 16], a[:, K // 16:]

@@ -48,9 +48,12 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     M, K, N = 4608, 3072, 12288
     assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, M, K, N) == M * K + M * 4
-    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N) == 2 * M * K + 2 * N * K
+    # nvfp4: packed codes of x, its block scales slab-major [K/128, M, 8], then (R > 0)
+    # L1^T, T and [L2^T | L2^T], then the weight's block scales [K/128, N, 8]
+    S = K // 128
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N) == M * K // 2 + 8 * M * S + 8 * N * S
     r = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, 3072, 32)
-    assert r == 2 * M * K + 2 * 3072 * K + 2 * 32 * K + 2 * M * 64 + 2 * 3072 * 64
+    assert r == M * K // 2 + 8 * M * S + 2 * 32 * K + 2 * M * 64 + 2 * 3072 * 64 + 8 * 3072 * S
     assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 24, 4) == 0      # K % 16 != 0
     assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 32, 4, 129) == 0  # rank too large
     assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, 4, 32, 4, 1) == 0     # fp8r has no low rank
@@ -60,6 +63,51 @@ def test_workspace_sizes(lib):
     assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, M, K, N) == (r256(M * K) + r256(N * K) + r256(4 * M * K // 64) +
                                                                  r256(4 * N * K // 64))
     assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, 4, 96, 4) == 0  # K % 64 != 0
+
+
+def test_nvfp4_workspace_ragged_k(lib):
+    # K = 400: ceil(400 / 128) = 4 scale slabs; every part rounded up to 256 bytes
+    r256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    M, K, N = 300, 400, 520
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N) == r256(M * K // 2) + r256(8 * M * 4) + r256(8 * N * 4)
+
+
+def test_k_limits(lib):
+    # 256 rows of an operand are addressed with 32-bit offsets below 2^30 (the
+    # out-of-range marker): fp8r and INT4 rows are K bytes, nvfp4 rows K/2 bytes
+    ws = 1 << 62
+    big = (1 << 22)
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, 4, big, 8) == 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_FP8R, 4, big - 16, 8) > 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, 4, big, 8) == 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, 4, big - 64, 8) > 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 2 * big, 8) == 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 2 * big - 16, 8) > 0
+    # with a low-rank branch the fused quantizer stages L1^T rows of 2K bytes: K <= 2^21
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, (1 << 21) + 16, 8, 32) == 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 4, 1 << 21, 8, 32) > 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, 4, (1 << 21) + 64, 8, 32) == 0
+    # ... and stores the activation's scales through a descriptor below 2^31 bytes
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, 1 << 17, 1 << 18, 8, 32) == 0   # 8 M K/128 = 2^31
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, (1 << 17) - 1, 1 << 18, 8, 32) > 0
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, 1 << 19, 1 << 16, 8, 32) == 0    # 4 M K/64 = 2^31
+    assert qpl.qlinear_workspace_bytes(qpl.QPL_INT4, (1 << 19) - 1, 1 << 16, 8, 32) > 0
+    # the linears refuse them before touching a device
+    assert lib.qlinear_fp8r(A, 4, big, 8, B, C, D, A, ws, None) == SHAPE
+    assert lib.qlinear_nvfp4(A, 4, 2 * big, 8, B, C, 1.0, 1.0, None, None, None, 0, D, A, ws, None) == SHAPE
+    assert lib.qlinear_nvfp4(A, 4, (1 << 21) + 16, 8, B, C, 1.0, 1.0, None, A, B, 32, D, A, ws, None) == SHAPE
+    assert lib.qlinear_int4(A, 4, big, 8, B, C, None, None, None, 0, D, A, ws, None) == SHAPE
+    assert lib.qlinear_int4(A, 4, (1 << 21) + 64, 8, B, C, None, A, B, 32, D, A, ws, None) == SHAPE
+
+
+def test_nvfp4_global_scale_product(lib):
+    # input_scale * weight_scale_2 scales the fp32 4-bit product: a normal fp32 number
+    ws = 1 << 30
+    args = (A, 4, 32, 8, B, C)
+    assert lib.qlinear_nvfp4(*args, 1e-20, 1e-20, None, None, None, 0, D, A, ws, None) == ARG   # 1e-40, subnormal
+    assert lib.qlinear_nvfp4(*args, 1e20, 1e20, None, None, None, 0, D, A, ws, None) == ARG     # overflows
+    assert lib.qlinear_nvfp4(*args, 1e-19, 1e-19, None, A, B, 4, D, A, ws, None) == ARG         # 1e-38 < 2^-126
+    assert lib.qlinear_nvfp4(*args, 1e-19, 1e-18, None, A, B, 4, D, A, ws, None) != ARG         # 1e-37 is normal
 
 
 def test_global_scale(lib):

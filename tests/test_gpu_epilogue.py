@@ -17,27 +17,25 @@
   low-rank branch, the non-unique h) can have; and y must be bit-identical to the
   two layers run as separate calls.
 """
-import math
 
 import numpy as np
 import pytest
 import torch
 
 import precision_quantized_linear_amd as qpl
-from helpers import bf16_bits, to_dev, to_dev_bf16
+from helpers import bf16_bits, host, nvfp4_workspace_parts, slab_scales_to_rows, to_dev, to_dev_bf16
 from oracle.epilogue import (bf16_interval, check_nvfp4_expanded, expanded_nominal_and_width, gelu_bf16_ref,
                              gelu_interval, gelu_tanh, pre_activation_error, qkv_split_ref, smooth_interval)
 from oracle.formats import bf16_bits_to_f32, f32_to_bf16_bits
 from oracle.int4 import dequant_int4, quant_int4
 from oracle.quant import amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4, smooth_bf16
-from oracle.reference import (FROB_ARITH, check_gemm, dequant_fp8r, dequant_nvfp4, gemm_gamma, lowrank_abs,
-                              lowrank_ref, ulp_bf16)
+from oracle.reference import (FROB_ARITH, check_gemm, dequant_fp8r, dequant_nvfp4, gemm_gamma, gemm_gamma_fp8_dot,
+                              lowrank_abs, lowrank_ref, ulp_bf16)
 from synthetic import calibration_batches, make, smooth_factors
 
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
-FP8_MFMA_GAMMA = 2.0 ** -11  # the fp8r GEMM's accumulation floor (pinned in test_gpu_gemm)
 
 
 def say(*a):
@@ -163,7 +161,7 @@ def test_gelu_fp8r(M, K, N):
     y = call(act="gelu_tanh")
     torch.cuda.synchronize()
     r = check_gelu(bf16_bits(y[torch.from_numpy(rows).cuda()]), ref, absum, K,
-                   gamma=FP8_MFMA_GAMMA + math.ceil(K / 64) * 2.0 ** -24)
+                   gamma=gemm_gamma_fp8_dot(K))
     say(r)
     assert r["ok"], r
 
@@ -200,7 +198,7 @@ def run_qkv(scheme, d, heads, hd, tokens, off, rows):
         gamma = None
     elif scheme == "fp8r":
         ref, absum, extra, call = fp8r_pre(d, rows)
-        gamma = FP8_MFMA_GAMMA + math.ceil(K / 64) * 2.0 ** -24
+        gamma = gemm_gamma_fp8_dot(K)
     else:
         ref, absum, extra, call = int4_pre(d, rows)
         gamma = None
@@ -279,7 +277,13 @@ def mlp_case(M, K, H, N, lr1, lr2, smooth1, smooth2, rows):
     y2 = qpl.qlinear_nvfp4(h, fc2["weight"], fc2["weight_scale"], g_w2, g2, smooth=fc2["smooth"], **kw2)
     torch.cuda.synchronize()
     r_rows = torch.from_numpy(rows).cuda()
-    he = ws[:2 * M * H].view(torch.bfloat16).view(M, H)[r_rows]
+    # fc2's quantized input, left at the start of the workspace: packed codes, then
+    # slab-major block scales; decoded here to the values e2m1(code) * dec(sf)
+    parts = nvfp4_workspace_parts(M, H, N, R2)
+    wsh = host(ws[:parts["xs"] + 8 * M * parts["S"]])
+    hq = wsh[:M * H // 2].reshape(M, H // 2)[rows]
+    hs = slab_scales_to_rows(wsh[parts["xs"]:], M, H)[0][rows]
+    he_bits = f32_to_bf16_bits(dequant_nvfp4(hq, hs, 1.0).astype(F32))
     h_off = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, H, N, R2)
     hw = ws[h_off:h_off + 2 * M * H].view(torch.bfloat16).view(M, H)[r_rows]
     yb = bf16_bits(y)
@@ -291,7 +295,7 @@ def mlp_case(M, K, H, N, lr1, lr2, smooth1, smooth2, rows):
     lo, hi = gelu_interval(ref1, pre_activation_error(ref1, absum1, K, extra1))
     hlb, hhb = bf16_interval(lo, hi)
     lb, hb = (hlb, hhb) if lam2 is None else smooth_interval(hlb, hhb, lam2)
-    rq = check_nvfp4_expanded(bf16_bits(he), lb, hb, g2)
+    rq = check_nvfp4_expanded(he_bits, lb, hb, g2)
 
     # y against the oracle's fc2 on its nominal operand, widened by the ambiguous codes
     # (and, with fc2's low-rank branch, by the ambiguous smoothed h it reads)

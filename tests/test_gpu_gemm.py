@@ -5,19 +5,16 @@ Acceptance (written in oracle.reference.check_gemm): relative Frobenius error
 <= 2e-3 over the compared outputs, and per element |y - ref| <= 4 bf16 ulps of ref
 plus an accumulation floor gamma * sum_k |a_k w_k|:
 
-* nvfp4 runs on the bf16 MFMA, whose dot products behave like fp32 sums:
-  gamma = ceil(K/16) * 2^-24.
-* fp8r runs on the full-rate f8f6f4 MFMA, whose 64-product dot unit keeps a
-  limited number of bits below the largest product of a group (it does not sum
-  like IEEE fp32).  Its floor is FP8_MFMA_GAMMA + ceil(K/64) * 2^-24: twice the
-  largest per-instruction error measured on inputs spread over the whole E4M3
-  range (2.1e-4 of sum |a w|), plus fp32 accumulation across instructions.
-  test_fp8_mfma_accumulation_bound pins that bound through qlinear_fp8r.
+* nvfp4 multiplies exact f16 expansions of the codes on the f16 MFMA, whose dot
+  products behave like fp32 sums: gamma = ceil(K/16) * 2^-24 (gemm_gamma).
+* fp8r runs on the full-rate f8f6f4 MFMA, whose dot unit truncates products within
+  groups of 8 and adds with truncation (oracle.reference.gemm_gamma_fp8_dot derives
+  gamma = 7 * 2^-13 + 8 ceil(K/64) 2^-23 from that model).  The fp8r tests also
+  report how many outputs the fp32 floor alone would fail and the largest error in
+  bf16 ulps, and hold them to the figures measured with this kernel.
 
 Small shapes compare every output; full-size workloads compare sampled rows (all
 columns), including the first and last rows of edge tiles."""
-
-import math
 
 import numpy as np
 import pytest
@@ -28,16 +25,11 @@ from helpers import bf16_bits, to_dev, to_dev_bf16
 from oracle.formats import bf16_bits_to_f32
 from oracle.quant import (amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4,
                           smooth_bf16)
-from oracle.reference import (check_gemm, dequant_fp8r, dequant_nvfp4, lowrank_abs, lowrank_ref)
-from synthetic import calibration_batches, make, smooth_factors
+from oracle.reference import (check_gemm, dequant_fp8r, dequant_nvfp4, gemm_gamma_fp8_dot, lowrank_abs,
+                              lowrank_ref)
+from synthetic import bf16_round, calibration_batches, make, smooth_factors
 
 pytestmark = pytest.mark.gpu
-
-FP8_MFMA_GAMMA = 2.0 ** -11
-
-
-def fp8_gamma(K):
-    return FP8_MFMA_GAMMA + math.ceil(K / 64) * 2.0 ** -24
 
 
 def say(*a):
@@ -54,6 +46,8 @@ def sample_rows(M, n=64, seed=0):
 
 
 def fp8r_case(d, rows):
+    """The fp8r acceptance (fp8 dot-unit floor), plus the same outputs held to the
+    fp32 floor alone: its failure count is reported as fails_fp32_floor."""
     x, w = d["x"], d["w"]
     K = x.shape[1]
     xq, xs = quant_fp8_row(x[rows])
@@ -62,7 +56,10 @@ def fp8r_case(d, rows):
     ref, absum = a @ b.T, np.abs(a) @ np.abs(b).T
     y = qpl.qlinear_fp8r(to_dev_bf16(x), to_dev(wq), to_dev(ws))
     torch.cuda.synchronize()
-    return check_gemm(bf16_bits(y)[rows], ref, absum, K, gamma=fp8_gamma(K))
+    yb = bf16_bits(y)[rows]
+    r = check_gemm(yb, ref, absum, K, gamma=gemm_gamma_fp8_dot(K))
+    r["fails_fp32_floor"] = check_gemm(yb, ref, absum, K)["fails"]
+    return r
 
 
 def nvfp4_case(d, rows, g_in, lam=None):
@@ -102,16 +99,45 @@ def test_qlinear_fp8r_small(name, M, K, N):
     d = make(name, M=M, K=K, N=N)
     say("qlinear_fp8r", name, d["M"], d["K"], d["N"])
     r = fp8r_case(d, np.arange(d["M"]))
+    say(r)
     assert r["ok"], r
+
+
+# Measured with this kernel on the seeded workloads (deterministic): outputs that the
+# fp32 floor alone fails, the largest error in bf16 ulps of the reference, and the
+# outputs that pass only because of the fp8 dot-unit floor.  A change of the
+# kernel's arithmetic that makes any of them worse fails here.
+FP8R_RECORDED = {
+    "fp8r_tiny": dict(fails_fp32_floor=17, max_ulp_err=683.4, only_floor=19),       # all 32768 outputs
+    "fp8r_dit_n3072": dict(fails_fp32_floor=0, max_ulp_err=3773.9, only_floor=556),  # 256 rows x 3072
+    "fp8r_dit_n12288": dict(fails_fp32_floor=0, max_ulp_err=3773.9, only_floor=2297),  # 256 rows x 12288
+}
+
+
+def check_recorded(name, r):
+    for k, v in FP8R_RECORDED[name].items():
+        if v is not None:
+            assert r[k] <= v, (name, k, r[k], v)
+
+
+def test_qlinear_fp8r_tiny_figures():
+    # the 64 x 256 x 512 workload, every output
+    d = make("fp8r_tiny")
+    r = fp8r_case(d, np.arange(d["M"]))
+    say("fp8r_tiny figures", {k: r[k] for k in ("fails_fp32_floor", "max_ulp_err", "only_floor", "frob")})
+    assert r["ok"], r
+    check_recorded("fp8r_tiny", r)
 
 
 @pytest.mark.parametrize("name", ["fp8r_dit_n3072", "fp8r_dit_n12288"])
 def test_qlinear_fp8r_full(name):
+    # 256 sampled rows (all columns) of the 4608-row workload
     d = make(name)
     say("qlinear_fp8r full", name, d["M"], d["K"], d["N"])
-    r = fp8r_case(d, sample_rows(d["M"]))
-    say(r)
+    r = fp8r_case(d, sample_rows(d["M"], n=256))
+    say(name, "figures", {k: r[k] for k in ("fails_fp32_floor", "max_ulp_err", "only_floor", "frob")})
     assert r["ok"], r
+    check_recorded(name, r)
 
 
 NVFP4_SHAPES = [
@@ -219,6 +245,39 @@ def test_qlinear_nvfp4_lowrank_ranks(R, M, K):
     assert r["ok"], r
 
 
+def _scaled_bits(bits, e):
+    """bf16 bit array times 2^e (exact: every scaled value stays a normal bf16)."""
+    f = bf16_bits_to_f32(bits).astype(np.float64) * 2.0 ** e
+    assert np.all((f == 0) | ((np.abs(f) >= 2.0 ** -126) & (np.abs(f) < 2.0 ** 127)))
+    return bf16_round(f.astype(np.float32))
+
+
+@pytest.mark.parametrize("target", [-126, -125, 64, 100])
+def test_qlinear_nvfp4_lowrank_global_scale_edges(target):
+    # input_scale * weight_scale_2 at the ends of the accepted range: x and W are
+    # scaled by powers of two so the product lands in [2^target, 2^(target+1));
+    # L2 carries W's factor so the low-rank term stays comparable to the 4-bit one.
+    # The 4-bit product is scaled before the low-rank term joins it, so the output is
+    # finite wherever the reference is, and subnormal bf16 outputs are compared too.
+    M, K, N, R = 130, 256, 200, 32
+    d = make("svdq_w4a4", M=M, K=K, N=N)
+    g0 = float(global_scale(amax_bf16(d["x"]))) * float(global_scale(amax_bf16(d["w"])))
+    shift = int(np.ceil(target - np.log2(g0)))
+    ex = shift // 2
+    ew = shift - ex
+    d["x"], d["w"] = _scaled_bits(d["x"], ex), _scaled_bits(d["w"], ew)
+    rng = np.random.default_rng(11)
+    d["l1"] = bf16_round((rng.standard_normal((K, R)) * 0.05).astype(np.float32))
+    d["l2"] = _scaled_bits(bf16_round((rng.standard_normal((R, N)) * 0.05).astype(np.float32)), ew)
+    g_in = global_scale(amax_bf16(d["x"]))
+    g = np.float32(g_in) * np.float32(global_scale(amax_bf16(d["w"])))
+    assert 2.0 ** target <= g < 2.0 ** (target + 1), (g, target)
+    say("qlinear_nvfp4 global scale product", g, "x 2^%d, w 2^%d" % (ex, ew))
+    r = nvfp4_case(d, np.arange(M), g_in)
+    say(r)
+    assert r["ok"], r
+
+
 def test_qlinear_one_hot_weight_fp8r():
     # W row n is one-hot at k = n (code 1.0, scale 1): y[:, n] = bf16(dec(xq[:, n]) * s_x)
     d = make("fp8r_tiny")
@@ -245,19 +304,19 @@ def test_qlinear_deterministic():
     assert np.array_equal(y1, y2)
 
 
-def test_fp8_mfma_accumulation_bound():
+def test_fp8_dot_floor_random_codes():
     # Activations and weights are exact E4M3 values spread over the whole exponent
     # range, with row amax 448 (so the row scale is 1 and the kernel's codes are the
-    # chosen values).  The per-element error of the product, relative to
-    # sum_k |a_k w_k|, must stay below FP8_MFMA_GAMMA; it also shows the floor is
-    # needed (the fp32 floor alone is exceeded).
+    # chosen values).  The per-element error of the product must stay within the
+    # dot-unit floor; the fp32 floor alone is exceeded (the floor is needed).
     from oracle.formats import e4m3_decode
+    from oracle.reference import gemm_gamma, ulp_bf16
+    from synthetic import bf16_round
     rng = np.random.default_rng(17)
     M, N, K = 256, 256, 64
     codes = rng.integers(0, 0x7F, (M + N, K)).astype(np.uint8) | (rng.integers(0, 2, (M + N, K)).astype(np.uint8) << 7)
     codes[:, 0] = 0x7E                      # every row holds 448, so its scale is exactly 1
     vals = e4m3_decode(codes)
-    from synthetic import bf16_round
     xa = bf16_round(vals[:M].astype(np.float32))
     wq = codes[M:]
     y = qpl.qlinear_fp8r(to_dev_bf16(xa), to_dev(wq), to_dev(np.ones(N, np.float32)))
@@ -265,10 +324,32 @@ def test_fp8_mfma_accumulation_bound():
     a, b = vals[:M], vals[M:]
     ref, absum = a @ b.T, np.abs(a) @ np.abs(b).T
     yb = bf16_bits_to_f32(bf16_bits(y)).astype(np.float64)
-    from oracle.reference import ulp_bf16
     excess = np.maximum(np.abs(yb - ref) - 4 * ulp_bf16(ref), 0) / absum
-    say("fp8 MFMA excess error / sum|aw|: max", excess.max())
-    assert excess.max() <= FP8_MFMA_GAMMA
+    say("fp8 dot unit: excess error / sum|aw|: max", excess.max(), "floor", gemm_gamma_fp8_dot(K))
+    assert excess.max() <= gemm_gamma_fp8_dot(K)
+    assert excess.max() > gemm_gamma(K)
+
+
+def test_fp8_dot_floor_cancellation():
+    # Row m of x is [448, 448, 15, 15, ...] and row n of W is [448, -448, 1, 1, ...]:
+    # the two large products cancel and leave 62 * 15 = 930.  The six small products in
+    # the first group of eight lie 13 to 14 binades below its largest product, at the
+    # group's cut, so the dot unit truncates them: the result falls short of 930 by far
+    # more than fp32 summation could, and within the dot-unit floor.
+    from oracle.reference import gemm_gamma, ulp_bf16
+    K = 64
+    x = np.full((32, K), 0x4170, np.uint16)   # bf16 15.0
+    x[:, 0] = x[:, 1] = 0x43E0                # bf16 448.0
+    wq = np.full((32, K), 0x38, np.uint8)      # E4M3 1.0
+    wq[:, 0], wq[:, 1] = 0x7E, 0xFE            # E4M3 448, -448
+    y = qpl.qlinear_fp8r(to_dev_bf16(x), to_dev(wq), to_dev(np.ones(32, np.float32)))
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(bf16_bits(y)).astype(np.float64)
+    ref, absum = 930.0, 2 * 448.0 * 448.0 + 62 * 15.0
+    say("fp8 dot unit, cancellation: got", np.unique(got), "exact", ref)
+    err = np.abs(got - ref)
+    assert np.all(err > gemm_gamma(K) * absum + 4 * ulp_bf16(ref))
+    assert np.all(err <= gemm_gamma_fp8_dot(K) * absum + 4 * ulp_bf16(ref))
 
 
 @pytest.mark.parametrize("scheme", ["fp8r", "nvfp4"])
@@ -288,7 +369,7 @@ def test_output_past_2_31_elements(scheme):
         wq, ws = quant_fp8_row(w)
         a, b = dequant_fp8r(xq, xs), dequant_fp8r(wq, ws)
         qpl.qlinear_fp8r(to_dev_bf16(x), to_dev(wq), to_dev(ws), y=y)
-        gamma = fp8_gamma(K)
+        gamma = gemm_gamma_fp8_dot(K)
     else:
         g_in = calibrate_input_scale(calibration_batches("nvfp4_dit", M=64, K=K))
         g_w = global_scale(amax_bf16(w))

@@ -5,11 +5,12 @@ import pytest
 import torch
 
 import precision_quantized_linear_amd as qpl
-from helpers import adversarial_rows, bf16_bits, host, to_dev, to_dev_bf16
-from oracle.formats import bf16_bits_to_f32, f32_to_bf16_bits
+from helpers import (adversarial_rows, bf16_bits, host, nvfp4_workspace_parts, slab_scales_to_rows, to_dev,
+                     to_dev_bf16)
+from oracle.formats import bf16_bits_to_f32
 from oracle.quant import (amax_bf16, calibrate_input_scale, global_scale, quant_fp8_row, quant_nvfp4,
                           smooth_bf16)
-from oracle.reference import dequant_nvfp4, dequant_weight_fp8r, dequant_weight_nvfp4
+from oracle.reference import dequant_weight_fp8r, dequant_weight_nvfp4
 from synthetic import bf16_round, calibration_batches, make, smooth_factors
 
 pytestmark = pytest.mark.gpu
@@ -211,41 +212,48 @@ def test_quant_deterministic():
     assert all(np.array_equal(p, q) for p, q in zip(a, b))
 
 
-# ---- the GEMM's operands: bf16 expansions of the quantized activation and weight ----
-
-def expanded_bits(packed, block_scale):
-    """bf16 bits of e2m1(code) * dec(sf): exact (at most 6 significant bits)."""
-    return f32_to_bf16_bits(dequant_nvfp4(packed, block_scale, 1.0).astype(np.float32))
-
-
-def unsigned_zero(b):
-    b = b.copy()
-    b[b == 0x8000] = 0
-    return b
+# ---- the GEMM's operands: what qlinear_nvfp4 leaves in its workspace ----
+# The activation quantize inside the linear (plain, or fused with x L1 when R > 0)
+# writes packed codes [M, K/2] and block scales in the GEMM's slab-major layout; the
+# preparation copies the weight's block scales into that layout.  All of it must be
+# bit-exact: the codes equal to quant_act_nvfp4's (signed zeros included).
 
 
-def run_expansions(x_bits, g_in, wq, wb, lam=None):
+def run_linear_operands(x_bits, g_in, wq, wb, lam=None, R=0, seed=0):
     M, K = x_bits.shape
     N = wq.shape[0]
-    ws = torch.empty((qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N, 0),), dtype=torch.uint8, device="cuda")
-    qpl.qlinear_nvfp4(to_dev_bf16(x_bits), to_dev(wq), to_dev(wb), 1.0, g_in, workspace=ws,
-                      smooth=None if lam is None else to_dev(lam))
+    kw = {}
+    if R:
+        rng = np.random.default_rng(seed)
+        kw["lora_down"] = to_dev_bf16(bf16_round((rng.standard_normal((K, R)) * 0.05).astype(np.float32)))
+        kw["lora_up"] = to_dev_bf16(bf16_round((rng.standard_normal((R, N)) * 0.05).astype(np.float32)))
+    if lam is not None:
+        kw["smooth"] = to_dev(lam)
+    ws = torch.zeros((qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, M, K, N, R),), dtype=torch.uint8, device="cuda")
+    # a first call leaves non-zero bytes behind; the second must write every byte it owns
+    ws.fill_(0xA5)
+    qpl.qlinear_nvfp4(to_dev_bf16(x_bits), to_dev(wq), to_dev(wb), 1.0, g_in, workspace=ws, **kw)
     torch.cuda.synchronize()
-    w_off = (2 * M * K + 255) // 256 * 256
-    xe = bf16_bits(ws[:2 * M * K].view(torch.bfloat16))
-    we = bf16_bits(ws[w_off:w_off + 2 * N * K].view(torch.bfloat16))
-    return xe.reshape(M, K), we.reshape(N, K)
+    parts = nvfp4_workspace_parts(M, K, N, R)
+    h = host(ws)
+    S = parts["S"]
+    xq = h[:M * K // 2].reshape(M, K // 2)
+    xs, xpad = slab_scales_to_rows(h[parts["xs"]:parts["xs"] + 8 * M * S], M, K)
+    wsr, wpad = slab_scales_to_rows(h[parts["ws"]:parts["ws"] + 8 * N * S], N, K)
+    return xq, xs, xpad, wsr, wpad
 
 
-def assert_expanded_equal(x_bits, g_in, wq, wb, lam=None):
-    xe, we = run_expansions(x_bits, g_in, wq, wb, lam)
+def assert_operands_equal(x_bits, g_in, wq, wb, lam=None, R=0):
+    xq, xs, xpad, wsr, wpad = run_linear_operands(x_bits, g_in, wq, wb, lam, R)
     xin = x_bits if lam is None else smooth_bf16(x_bits, lam)
     cq, cs = quant_nvfp4(xin, g_in)
-    ref_x = unsigned_zero(expanded_bits(cq, cs))
-    bad = np.argwhere(unsigned_zero(xe) != ref_x)
-    assert bad.size == 0, f"{len(bad)} expanded activations differ, first at {bad[:3].tolist()}"
-    bad = np.argwhere(we != expanded_bits(wq, wb))
-    assert bad.size == 0, f"{len(bad)} expanded weights differ, first at {bad[:3].tolist()}"
+    bad = np.argwhere(xq != cq)
+    assert bad.size == 0, f"{len(bad)} activation code bytes differ, first at {bad[:3].tolist()}"
+    bad = np.argwhere(xs != cs)
+    assert bad.size == 0, f"{len(bad)} activation block scales differ, first at {bad[:3].tolist()}"
+    assert not xpad.any(), "activation scale bytes past K/16 are not zero"
+    assert np.array_equal(wsr, wb), "weight block scales moved wrongly"
+    assert not wpad.any(), "weight scale bytes past K/16 are not zero"
 
 
 def random_weight(N, K, seed):
@@ -255,30 +263,41 @@ def random_weight(N, K, seed):
             rng.integers(0, 127, (N, K // 16)).astype(np.uint8))
 
 
-@pytest.mark.parametrize("name,M,K,N,smoothed", [
-    ("nvfp4_dit", None, None, 40, False),     # 4608 x 3072 activation, full size
-    ("svdq_w4a4", 300, 400, 48, False),       # ragged: 7500 vectors, a partial last workgroup
-    ("svdq_w4a4", 37, 272, 33, True),         # smoothed, odd rows
-    ("nvfp4_dit", 1, 16, 1, False),           # one block
+@pytest.mark.parametrize("name,M,K,N,smoothed,R", [
+    ("nvfp4_dit", None, None, 40, False, 0),     # 4608 x 3072 activation, full size
+    ("svdq_w4a4", 300, 400, 48, False, 0),       # ragged: K % 128 != 0 (a partial last scale slab)
+    ("svdq_w4a4", 37, 272, 33, True, 0),         # smoothed, odd rows
+    ("nvfp4_dit", 1, 16, 1, False, 0),           # one block
+    ("svdq_w4a4", None, None, 64, False, 32),    # the SVDQuant workload at full size, fused x L1 quantizer
+    ("svdq_w4a4", None, None, 64, True, 32),     # the same with smoothing
+    ("svdq_w4a4", 300, 400, 48, False, 32),      # ragged M and K
+    ("svdq_w4a4", 37, 272, 33, True, 20),        # smoothed, odd rows, K % 32 == 16, rank 20
+    ("svdq_w4a4", 1, 16, 1, False, 1),           # one block, rank 1
+    ("svdq_w4a4", 256, 256, 16, False, 64),      # 1 row per quantizer workgroup, two T groups
+    ("svdq_w4a4", 512, 208, 16, True, 100),      # 2 rows per workgroup, four T groups
+    ("svdq_w4a4", 5120, 256, 16, False, 32),     # 20 rows per workgroup
+    ("svdq_w4a4", 6000, 256, 16, True, 32),      # 24 rows per workgroup
+    ("svdq_w4a4", 8192, 128, 16, False, 128),    # 32 rows per workgroup, rank 128
 ])
-def test_qlinear_nvfp4_expanded_operands(name, M, K, N, smoothed):
+def test_qlinear_nvfp4_operands(name, M, K, N, smoothed, R):
     d = make(name, M=M, K=K)
     K = d["K"]
     lam = smooth_factors("svdq_w4a4", K=K) if smoothed else None
-    batches = calibration_batches(name, M=64 if M is None else M, K=K)
+    batches = calibration_batches(name, M=64 if M is None else min(M, 512), K=K)
     if lam is not None:
         batches = (smooth_bf16(b, lam) for b in batches)
     g = calibrate_input_scale(batches)
     wq, wb = random_weight(N, K, seed=K + N)
-    say("qlinear_nvfp4 expanded operands", name, d["x"].shape, N, "smoothed" if smoothed else "", g)
-    assert_expanded_equal(d["x"], g, wq, wb, lam)
+    say("qlinear_nvfp4 operands", name, d["x"].shape, N, "R", R, "smoothed" if smoothed else "", g)
+    assert_operands_equal(d["x"], g, wq, wb, lam, R)
 
 
+@pytest.mark.parametrize("R", [0, 32])
 @pytest.mark.parametrize("g", [1e-30, 1e-4, 0.25, 1e6, 5e37])
-def test_qlinear_nvfp4_expanded_adversarial(g):
+def test_qlinear_nvfp4_operands_adversarial(g, R):
     # block scales saturated at 448 (small g) or underflowed to 0 (huge g), signed
-    # zeros, subnormal inputs
+    # zeros, subnormal inputs, exact ties; plain and fused quantizer
     x = adversarial_rows(256, seed=7)
     wq, wb = random_weight(24, 256, seed=8)
-    say("qlinear_nvfp4 expanded operands, adversarial", x.shape, g)
-    assert_expanded_equal(x, np.float32(g), wq, wb)
+    say("qlinear_nvfp4 operands, adversarial", x.shape, g, "R", R)
+    assert_operands_equal(x, np.float32(g), wq, wb, R=R)
