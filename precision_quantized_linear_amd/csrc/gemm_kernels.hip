@@ -462,13 +462,13 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
     const Unit un = unit(ti);
     if constexpr (ROWCOL) {
       const float* ls = reinterpret_cast<const float*>(lsc + (ti & 1) * SCALE_BUF);
-      st1 = store_tile<NJ, 4, EPI>(
+      st1 = __builtin_amdgcn_readfirstlane(store_tile<NJ, 4, EPI>(
           acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int r) { return ls[r]; },
-          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); }, e);
+          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); }, e));
     } else {
-      st1 = store_tile<NJ, 4, EPI>(
+      st1 = __builtin_amdgcn_readfirstlane(store_tile<NJ, 4, EPI>(
           acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return gscale; },
-          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e);
+          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e));
     }
     if (st1 == 0) st2 = st3 = 0;
   };
@@ -644,33 +644,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int kb, koff, stage;
     bool pass2;
   };
+  // The slab stream's sources change only where it enters a unit or the unit's
+  // low-rank pass: then the code descriptors, the row count and the first slab's
+  // scale address are worked out; from slab to slab only the scale address moves
+  // (by one slab of scales) with the stage and the K offset.
   int s_ti = 0, s_ks = 0, s_stage = 0;
   Unit s_u{0, 0, 256};
-  if (nu > 0) s_u = unit(0);
-  auto next_src = [&]() {
-    SlabSrc r;
-    const bool valid = s_ti < nu;
-    const bool pass2 = LOWRANK && s_ks >= nk1;
-    r.stage = s_stage;
-    r.pass2 = pass2;
+  u32x4 s_dx{}, s_dw{};
+  const uint8_t* s_sc = nullptr;  // scale bytes of the next slab (this wave's rows)
+  int64_t s_scb = 0;              // their count: 8 per row present, 0 in a low-rank pass
+  int s_kb = 0;
+  const int64_t sstride = 8 * (sc_x ? p.M : p.N);
+  auto enter = [&](bool pass2) {
     const int pitch = pass2 ? p.pitch2 : p.cpitch;
-    r.kb = valid ? (pass2 ? p.kbytes2 : p.cpitch) : 0;
-    r.koff = (pass2 ? s_ks - nk1 : s_ks) * SROW;
     const int64_t left = p.M - s_u.m0;
     const int64_t rm = left < 0 ? 0 : (left < s_u.rows ? left : s_u.rows);
     const int64_t rn = M_rows(p.N - s_u.n0);
-    r.dx = make_desc((pass2 ? p.a2 : p.xq) + s_u.m0 * pitch, rm * pitch);
-    r.dw = make_desc((pass2 ? p.w2 : p.wq) + s_u.n0 * pitch, rn * pitch);
+    s_dx = make_desc((pass2 ? p.a2 : p.xq) + s_u.m0 * pitch, rm * pitch);
+    s_dw = make_desc((pass2 ? p.w2 : p.wq) + s_u.n0 * pitch, rn * pitch);
+    s_kb = pass2 ? p.kbytes2 : p.cpitch;
     const int64_t lim = (sc_x ? rm : rn) - sc_r0;
-    const int64_t nrow = (valid && !pass2) ? (lim < 0 ? 0 : (lim < 128 ? lim : 128)) : 0;
-    const int64_t srows = sc_x ? p.M : p.N;
-    const int64_t row0 = (sc_x ? s_u.m0 : s_u.n0) + sc_r0;
-    r.ds = make_desc((sc_x ? p.xs : p.wsc) + ((int64_t)(pass2 ? 0 : s_ks) * srows + row0) * 8, nrow * 8);
+    s_scb = pass2 ? 0 : 8 * (lim < 0 ? 0 : (lim < 128 ? lim : 128));
+    s_sc = (sc_x ? p.xs : p.wsc) + ((sc_x ? s_u.m0 : s_u.n0) + sc_r0) * 8;
+  };
+  if (nu > 0) {
+    s_u = unit(0);
+    enter(false);
+  }
+  auto next_src = [&]() {
+    SlabSrc r;
+    r.stage = s_stage;
+    r.pass2 = LOWRANK && s_ks >= nk1;
+    r.kb = s_kb;
+    r.koff = (r.pass2 ? s_ks - nk1 : s_ks) * SROW;
+    r.dx = s_dx;
+    r.dw = s_dw;
+    r.ds = make_desc(s_sc, s_scb);
+    s_sc += sstride;
     s_stage = s_stage == PK_NST - 1 ? 0 : s_stage + 1;
     if (++s_ks == nk) {
       s_ks = 0;
-      ++s_ti;
-      if (s_ti < nu) s_u = unit(s_ti);
+      if (++s_ti < nu) {
+        s_u = unit(s_ti);
+        enter(false);
+      } else {
+        s_kb = 0;  // past the last unit: every load reads zeros
+        s_scb = 0;
+      }
+    } else if (LOWRANK && s_ks == nk1) {
+      enter(true);
     }
     return r;
   };
@@ -699,13 +721,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // fragment rows of tile-row t of a unit with nj x tile-rows: t < 4 W, t >= 4 x
   auto frow = [&](int t, int nj) { return t < 4 ? wn * 128 + t * 32 + r32 : wm * 32 * nj + (t - 4) * 32 + r32; };
-  // code dword s (step s) of every tile-row of the slab in stage st: bytes 32 h + 4 s
-  // of the row, i.e. chunk 2 h + s / 4 at offset 4 (s % 4)
-  auto read_codes = [&](const uint8_t* st, int nj, int s, uint32_t (&dst)[8]) {
+  // Codes of step group g (steps 4 g .. 4 g + 3) of tile-rows t0 .. t0 + 3 of the slab
+  // in stage st: one 16-byte chunk 2 h + g per row, dword s % 4 of it for step s
+  auto read_codes = [&](const uint8_t* st, int nj, int g, int t0, int ntr, u32x4 (&dst)[8]) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      dst[t] = *reinterpret_cast<const uint32_t*>(st + (t < 4 ? PK_CODES : 0) + soff(frow(t, nj), 2 * h + (s >> 2)) +
-                                                  4 * (s & 3));
+    for (int t = t0; t < t0 + 4; ++t)
+      if (t < ntr) dst[t] = *reinterpret_cast<const u32x4*>(st + (t < 4 ? PK_CODES : 0) + soff(frow(t, nj), 2 * h + g));
   };
   // block-scale dword (blocks 4 h .. 4 h + 3) of every tile-row of the slab in stage st
   auto read_scales = [&](const uint8_t* st, int nj, uint32_t (&dst)[8]) {
@@ -713,24 +734,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int t = 0; t < 8; ++t)
       dst[t] = *reinterpret_cast<const uint32_t*>(st + 2 * PK_CODES + (t < 4 ? PK_SC : 0) + frow(t, nj) * 8 + 4 * h);
   };
-  // The expansion runs one MFMA step ahead and the code reads two: while step s of
-  // a slab is multiplied (fragments F), step s + 1 is expanded (from codes C) and the
-  // codes of step s + 2 are read.  Across slabs, the last two steps of a slab do this
-  // for the first steps of the next one when it is a packed slab.
-  f16x8 F[8];             // fragments of the step being multiplied (t < 4: W, t >= 4: x)
-  uint32_t C[8], sc[8];   // codes of the next step, scales of the current slab
-  auto expand_step = [&](const uint32_t (&c)[8], const uint32_t (&scd)[8], int blk, f16x8 (&dst)[8], int ntr) {
+  // Two fragment sets alternate: while step s is multiplied from F[s % 2], step s + 1
+  // is expanded into F[(s + 1) % 2], so no fragment is copied.  Codes come a group of
+  // four steps at a time into CW[g % 2]; the next group's reads are issued during the
+  // first two steps of the current one.  Across slabs, the second half of a slab
+  // reads the next packed slab's first group and scales, and its last step expands
+  // the next slab's first step.
+  f16x8 F[2][8];
+  u32x4 CW[2][8];
+  uint32_t sc[8];
+  auto expand_step = [&](int s, const uint32_t (&scd)[8], f16x8 (&dst)[8], int ntr) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      if (t < ntr) dst[t] = fp4_expand(c[t], e4m3_pair(scd[t], blk));
+      if (t < ntr) dst[t] = fp4_expand(CW[(s >> 2) & 1][t][s & 3], e4m3_pair(scd[t], (s >> 1) & 3));
   };
   // first step of the slab in stage st (a unit with nj x tile-rows), unpipelined
   auto prime = [&](const uint8_t* st, int nj) {
-    uint32_t c0[8];
-    read_codes(st, nj, 0, c0);
+    read_codes(st, nj, 0, 0, 8, CW[0]);
+    read_codes(st, nj, 0, 4, 8, CW[0]);
     read_scales(st, nj, sc);
-    read_codes(st, nj, 1, C);
-    expand_step(c0, sc, 0, F, 8);
+    expand_step(0, sc, F[0], 8);
   };
   prime(lds, nt > 0 ? 4 : 2);
 
@@ -766,52 +789,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     cur = cur == PK_NST - 1 ? 0 : cur + 1;
     const uint8_t* ns = lds + cur * PK_STAGE;
     uint32_t scn[8];
+    // The next slab's first group is read and expanded whether or not it is a packed
+    // slab (without branches, so the expansion stays among this slab's MFMAs); when it
+    // is not, the values are not used, and whoever starts that slab primes it.
+    const int njr = njn ? njn : NJ;
     static_for<0, 8>([&](auto sc_) __attribute__((always_inline)) {
       constexpr int s = decltype(sc_)::value;
-      // codes two steps ahead
-      uint32_t C2[8];
-      if constexpr (s + 2 < 8) {
-        read_codes(cs, NJ, s + 2, C2);
-      } else {
-        if (njn) read_codes(ns, njn, s - 6, C2);
-      }
-      if constexpr (s == 6) {
-        if (njn) read_scales(ns, njn, scn);
-      }
+      // the next group's codes: this slab's second group, or the next slab's first
+      if constexpr (s == 0 || s == 1) read_codes(cs, NJ, 1, 4 * s, 4 + NJ, CW[1]);
+      if constexpr (s == 4 || s == 5) read_codes(ns, njr, 0, 4 * (s - 4), 8, CW[0]);
+      if constexpr (s == 5) read_scales(ns, njr, scn);
       // the next step's fragments
-      f16x8 Fn[8];
       if constexpr (s + 1 < 8) {
-        expand_step(C, sc, (s + 1) >> 1, Fn, 4 + NJ);
+        expand_step(s + 1, sc, F[(s + 1) & 1], 4 + NJ);
       } else {
-        if (njn) expand_step(C, scn, 0, Fn, 8);
+        expand_step(0, scn, F[0], 8);
       }
-      // this step's MFMAs
+      // this step's MFMAs, with the slab loads spread among them
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[i], F[4 + j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[s & 1][i], F[s & 1][4 + j], acc[i][j], 0, 0, 0);
           const int k = s * 4 * NJ + i * NJ + j;
 #pragma unroll
           for (int d = 0; d < PK_D; ++d)
             if (k == (d * NMMA) / PK_D) issue(src, d);
         }
-      if (s + 1 < 8 || njn) {
+      // one MFMA, then a share of the expansion, in turn: the expansion of the next
+      // step hides under this step's MFMAs
 #pragma unroll
-        for (int t = 0; t < 8; ++t) F[t] = Fn[t];
+      for (int m = 0; m < 4 * NJ; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NJ == 4 ? 5 : 10, 0);
+        if (m % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      if (s + 2 < 8 || njn) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) C[t] = C2[t];
-      }
-      // keeps the pipeline's shape: the scheduler interleaves the next step's
-      // expansion with this step's MFMAs, but does not pull later steps forward
       __builtin_amdgcn_sched_barrier(0);
     });
-    if (njn) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) sc[t] = scn[t];
-    }
+    for (int t = 0; t < 8; ++t) sc[t] = scn[t];
   };
 
   // A bf16 slab of the low-rank pass (fragments read from its stage at the top).
@@ -866,9 +882,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int ks = 0; ks < nk2; ++ks) step_lowrank(acc, nj, ks + 1 < nk2 ? 0 : njn);
     }
     const Unit un = unit(ti);
-    st1 = store_tile<NJ, 4, EPI>(
+    // the store count is wave-uniform; keeping it in a scalar register keeps the wait
+    // at the next slab's top a scalar branch
+    st1 = __builtin_amdgcn_readfirstlane(store_tile<NJ, 4, EPI>(
         acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return escale; },
-        [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e);
+        [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e));
     if (st1 == 0) st2 = 0;
   };
   for (int ti = 0; ti < nt; ++ti) run_unit(ti, Whole{});
