@@ -105,6 +105,28 @@ qpl_status qlinear_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t N,
                         uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qlinear_fp8r without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, checks, kernels and
+ * results as qlinear_fp8r; the workspace is instead a static device array of
+ * QPL_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the first call
+ * on that GPU (which looks up its address) until the process ends.
+ *   Limit: the fp8r workspace, 256 ceil(M K / 256) + 256 ceil(4 M / 256) bytes, must
+ *   fit in QPL_NOALLOC_SCRATCH_BYTES (32 MiB: M K up to about 33.5 M, e.g. 9216 x 3072),
+ *   else QPL_ERR_WORKSPACE and nothing is queued.
+ *   Sharing: every call on one GPU uses that GPU's one array, so calls that overlap on
+ *   one GPU (different streams, or different threads without ordering) race and give
+ *   undefined results; calls in one stream are ordered and safe.  Nothing in the array
+ *   needs to start at zero; it keeps the last call's quantized activation.
+ * No hipMalloc, hipFree, event or other allocating call is made; kernel timing
+ * (qpl_timing_enable) does not cover this entry point.
+ */
+#define QPL_NOALLOC_SCRATCH_BYTES (32u << 20)
+qpl_status qlinear_fp8r_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                                const uint8_t* weight, const float* weight_scale,
+                                uint16_t* y, void* stream);
+
+/*
  * nvfp4 linear (guide, "Kernels" table, nvfp4 row: an activation quantize followed
  * by a block-scaled FP4 GEMM), optionally with the SVDQuant low-rank branch:
  *   y = bf16_rne( input_scale * weight_scale_2 *

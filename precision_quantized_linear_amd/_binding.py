@@ -20,7 +20,7 @@ EXPORTS = ("quant_act_fp8_row", "quant_act_nvfp4", "qlinear_fp8r", "qlinear_nvfp
            "quant_weight_awq", "qlinear_awq_w4a16", "quant_act_int4", "qlinear_int4", "qlinear_fp8r_ex",
            "qlinear_nvfp4_ex", "qlinear_int4_ex", "qlinear_mlp_nvfp4", "qlinear_mlp_nvfp4_workspace_bytes",
            "qlinear_workspace_bytes", "qpl_amax_bf16", "qpl_nvfp4_global_scale", "qpl_status_str",
-           "qpl_timing_enable", "qpl_timing_select", "qpl_timing_collect")
+           "qpl_timing_enable", "qpl_timing_select", "qpl_timing_collect", "qlinear_fp8r_noalloc")
 
 # qpl_kernel order of include/qpl.h
 KERNELS = ("quant_fp8_row", "quant_nvfp4", "quant_nvfp4_linear", "gemm_fp8r", "gemm_nvfp4", "gemm_nvfp4_lowrank",
@@ -78,6 +78,7 @@ def load():
         "qlinear_nvfp4_ex": [P, I64, I64, I64, P, P, F, F, P, P, P, I64, P, P, P, SZ, P],
         "qlinear_int4_ex": [P, I64, I64, I64, P, P, P, P, P, I64, P, P, P, SZ, P],
         "qlinear_mlp_nvfp4": [P, I64, I64, I64, I64, P, P, P, P, SZ, P],
+        "qlinear_fp8r_noalloc": [P, I64, I64, I64, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -206,6 +207,20 @@ def qlinear_fp8r(x, weight, weight_scale, y=None, workspace=None, stream=None, a
         _check("qlinear_fp8r_ex", load().qlinear_fp8r_ex(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale),
                                                          _ref(e), _ptr(y), _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+def qlinear_fp8r_noalloc(x, weight, weight_scale, y, stream=None):
+    """qlinear_fp8r into a caller-provided y [M,N] bf16 with the library's static
+    device scratch as workspace: the call itself allocates nothing."""
+    M, K = x.shape
+    N = weight.shape[0]
+    _expect(x, torch.bfloat16, (M, K), "x")
+    _expect(weight, torch.uint8, (N, K), "weight")
+    _expect(weight_scale, torch.float32, (N,), "weight_scale")
+    _expect(y, torch.bfloat16, (M, N), "y")
+    _check("qlinear_fp8r_noalloc", load().qlinear_fp8r_noalloc(_ptr(x), M, K, N, _ptr(weight), _ptr(weight_scale),
+                                                               _ptr(y), _stream(stream)))
+    return y
 
 
 def qlinear_nvfp4(x, weight, weight_scale, weight_scale_2, input_scale, lora_down=None, lora_up=None, y=None,

@@ -215,9 +215,11 @@ qpl_kernel gemm_kind(const qpl::Epilogue& ep, qpl_kernel plain) {
   return ep.gelu || ep.qkv[0] ? QPL_KERNEL_GEMM_EPILOGUE : plain;
 }
 
+// timed: record the launches for qpl_timing_collect when timing is on (the
+// allocation-free variant never does: the event pool may create events).
 qpl_status fp8r_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,
                        const float* weight_scale, const qpl_epilogue* epi, uint16_t* y, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       void* stream, bool timed = true) {
   if (!x || !weight || !weight_scale || !ws) return QPL_ERR_NULL;
   if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y) || !aligned16(ws))
     return QPL_ERR_ALIGN;
@@ -233,10 +235,46 @@ qpl_status fp8r_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* xq = base + L.off[0];
   float* xs = reinterpret_cast<float*>(base + L.off[1]);
+  if (!timed) {
+    if ((s = launched(qpl::launch_quant_fp8_row(x, M, K, xq, xs, st))) != QPL_OK) return s;
+    return launched(qpl::launch_gemm_fp8r(xq, xs, weight, weight_scale, M, K, N, ep, y, st));
+  }
   if ((s = launched(Timed(QPL_KERNEL_QUANT_FP8_ROW, st)(qpl::launch_quant_fp8_row(x, M, K, xq, xs, st)))) != QPL_OK)
     return s;
   return launched(Timed(gemm_kind(ep, QPL_KERNEL_GEMM_FP8R), st)(
       qpl::launch_gemm_fp8r(xq, xs, weight, weight_scale, M, K, N, ep, y, st)));
+}
+
+// ---- the allocation-free fp8r linear ----------------------------------------
+// Its workspace (codes, then row scales) lives in this file-scope array: each device
+// holds its own copy, at its own address, from the library's load until the process
+// ends.  Host code never passes the array's name to a kernel or a copy (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoallocScratchBytes = size_t(QPL_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[64];
+
+// Device address of the current device's scratch (nullptr on failure).
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 // Checks of one nvfp4 layer's tensors for a linear [N, K] (weight, scales, global
@@ -410,6 +448,22 @@ QPL_EXPORT qpl_status qlinear_fp8r_ex(const uint16_t* x, int64_t M, int64_t K, i
                                       const float* weight_scale, const qpl_epilogue* epi, uint16_t* y, void* ws,
                                       size_t ws_bytes, void* stream) {
   return fp8r_linear(x, M, K, N, weight, weight_scale, epi, y, ws, ws_bytes, stream);
+}
+
+QPL_EXPORT qpl_status qlinear_fp8r_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t N,
+                                           const uint8_t* weight, const float* weight_scale, uint16_t* y,
+                                           void* stream) {
+  // the checks that need no device first, so a bad call touches no device state
+  if (!x || !weight || !weight_scale || !y) return QPL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(weight_scale) || !aligned16(y)) return QPL_ERR_ALIGN;
+  qpl_status s = check_gemm_dims(M, K, N);
+  if (s != QPL_OK) return s;
+  if ((s = check_gemm_k(QPL_FP8R, M, K, 0)) != QPL_OK) return s;
+  if (layout(QPL_FP8R, M, K, N, 0).total > kNoallocScratchBytes) return QPL_ERR_WORKSPACE;
+  if ((s = check_device()) != QPL_OK) return s;
+  void* ws = scratch_of_current_device();
+  if (!ws) return QPL_ERR_DEVICE;
+  return fp8r_linear(x, M, K, N, weight, weight_scale, nullptr, y, ws, kNoallocScratchBytes, stream, false);
 }
 
 QPL_EXPORT qpl_status qlinear_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,

@@ -134,6 +134,11 @@ def test_qlinear_validation(lib):
     assert lib.qlinear_fp8r(A, 4, 32, 0, B, C, D, A, ws, None) == SHAPE
     assert lib.qlinear_fp8r(A, 4, 32, 8, B, C, D, A, 10, None) == WORKSPACE
     assert lib.qlinear_fp8r(A, 4, 32, 8, B, MIS, D, A, ws, None) == ALIGN
+    # allocation-free variant: same checks, and a workspace beyond the static scratch
+    assert lib.qlinear_fp8r_noalloc(A, 4, 32, 8, B, C, None, None) == NULL
+    assert lib.qlinear_fp8r_noalloc(A, 4, 32, 0, B, C, D, None) == SHAPE
+    assert lib.qlinear_fp8r_noalloc(A, 4, 32, 8, B, MIS, D, None) == ALIGN
+    assert lib.qlinear_fp8r_noalloc(A, 9216, 3648, 8, B, C, D, None) == WORKSPACE  # 33.6 MB of codes
     args = (A, 4, 32, 8, B, C)
     assert lib.qlinear_nvfp4(*args, 1.0, 1.0, None, None, None, 0, D, A, 10, None) == WORKSPACE
     assert lib.qlinear_nvfp4(*args, 0.0, 1.0, None, None, None, 0, D, A, ws, None) == ARG
