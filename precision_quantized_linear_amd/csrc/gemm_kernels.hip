@@ -47,9 +47,7 @@ namespace qpl {
 namespace {
 
 constexpr int SROW = 64;            // bytes per slab row
-constexpr int SLAB = 256 * SROW;    // 16 KB per operand per stage
-constexpr int STAGE = 2 * SLAB;     // x slab then W slab
-constexpr int NST = 4;              // stages in the ring
+constexpr int NST = 4;              // stages in a ring of 64-byte slabs
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int soff(int r, int c) { return r * SROW + ((c ^ swz(r)) << 4); }
@@ -74,26 +72,17 @@ __device__ __forceinline__ u32x4 tile_desc(const void* base, int64_t rows_left, 
   return make_desc(base, rows * pitch);
 }
 
-// Operand fragments.  fp8: a 32x32x64 MFMA operand (32 K-bytes per lane, two
-// chunks).  bf16: a 32x32x16 MFMA operand (8 K-values per lane, one chunk); a
-// 64-byte slab holds two of them (sub-steps).
+// MFMA operands.  fp8: a 32x32x64 MFMA operand (32 K-bytes per lane).  bf16: a
+// 32x32x16 MFMA operand (8 K-values per lane, one 16-byte chunk); a 64-byte slab
+// holds two of them (sub-steps).
 struct Fp8Mma {
-  static constexpr int SUB = 1;
   typedef i32x8 Frag;
-  static __device__ __forceinline__ Frag read(const uint8_t* slab, int row, int sub, int lane) {
-    (void)sub;
-    const int c = 2 * (lane >> 5);
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(slab + soff(row, c));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(slab + soff(row, c + 1));
-    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  }
   static __device__ __forceinline__ f32x16 mma(const Frag& w, const Frag& x, const f32x16& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, c, 0, 0, 0, 127, 0, 127);
   }
 };
 
 struct Bf16Mma {
-  static constexpr int SUB = 2;
   typedef bf16x8 Frag;
   static __device__ __forceinline__ Frag read(const uint8_t* slab, int row, int sub, int lane) {
     return *reinterpret_cast<const bf16x8*>(slab + soff(row, 2 * sub + (lane >> 5)));
@@ -264,46 +253,65 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
   return 0;
 }
 
-// Persistent GEMM: workgroup b walks its tiles (tile_seq) one after the other,
-// and the slabs of all of them form one stream through the LDS ring: the loads
-// for the next tile's first slabs are issued while the current tile's last slabs
-// are multiplied, and the current tile's output stores drain while the next
-// tile's MFMAs run.
+// Persistent GEMMs (fp8r and nvfp4 below): workgroup b walks its tiles (tile_seq)
+// one after the other, and the slabs of all of them form one stream through the
+// LDS ring: the loads for the next tile's first slabs are issued while the current
+// tile's last slabs are multiplied, and the current tile's output stores drain
+// while the next tile's MFMAs run.  A wavefront's vector memory operations retire
+// in issue order (loads and stores alike), so a wait for a slab's loads names how
+// many later operations (loads of later slabs, epilogue stores) may stay in flight.
+
+// ---------------------------------------------------------------------------
+// fp8r GEMM (guide "BFL (fp8r / nvfp4)", "Kernels" table, fp8r row: a row-wise
+// scaled FP8 GEMM).  256 x 256 tiles of 4 wavefronts (2 x 2, 128 x 128 each,
+// sixteen 32 x 32 accumulators in AGPRs), V_MFMA_SCALE_F32_32X32X64_F8F6F4 with unit
+// scales on the E4M3 codes, output scale s_x[m] s_w[n] in the epilogue.  A load moves 8 rows x
+// 128 bytes (whole 128-byte lines) instead of 16 rows x 64 bytes: a stage holds two
+// 64-byte slabs of both operands (256 rows x 128 bytes each, 64 KB), and two stages
+// ring through 128 KB of LDS.  Loading half lines made every line two requests,
+// and the load path, not the MFMAs, set the pace.
 //
-// Wait accounting (vector memory operations of a wave retire in issue order): at
-// the top of iteration g, slab g + 1 must have landed; issued after its loads are
-// the loads of slabs g + 2 and g + 3 (2 D) and the output stores of the
-// epilogues that ran after iterations g - 3 .. g - 1.
-//
-// ROWCOL: fp8r output scales s_x[m] s_w[n], moved into LDS by two extra dword
-// loads per wave per slab (real for a tile's first slab, out of range otherwise).
-// Otherwise the output scale is gscale.  LOWRANK: pass 2 continues the same
-// accumulation with T / gscale and L2 (the quantizer stores T divided by gscale),
-// so y = bf16(gscale (x_q w_q^T + (T / gscale) L2)).
-template <class T, bool ROWCOL, bool LOWRANK, int EPI>
-__device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* __restrict__ sa,
-                                                const float* __restrict__ sb, float gscale,
-                                                uint16_t* __restrict__ Y, const EpiArgs& e) {
-  constexpr int D = ROWCOL ? 10 : 8;  // loads per wave per slab
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lsc[ROWCOL ? 3 * SCALE_BUF : 16];
+// Pair P (slabs 2P, 2P + 1) of the stream, in stage P % 2:
+// * top: wait for pair P's loads (issued during pair P - 1; only the epilogue
+//   stores issued after them may stay in flight), barrier (pair P is in LDS for
+//   every wave, and every wave is done with pair P - 1, whose stage is free);
+// * slab 2P: read its fragments, multiply, and issue pair P + 1's 16 loads per wave
+//   into the free stage, one after each MFMA; read slab 2P + 1's fragments as slab
+//   2P's are used up;
+// * slab 2P + 1: multiply, and issue the next unit's output scales when pair P + 1
+//   starts a unit.
+// Within a stage row r holds its two slabs as eight 16-byte chunks; chunk c of row
+// r sits at chunk c ^ (r % 8), so the eight lanes of a 16-byte LDS read pass hit
+// eight different chunk positions.
+// ---------------------------------------------------------------------------
+constexpr int PR_ROW = 128;                      // bytes per row per stage (two slabs)
+constexpr int PR_OPER = 256 * PR_ROW;            // 32 KB per operand per stage
+constexpr int PR_STAGE = 2 * PR_OPER;            // x rows then W rows
+constexpr int PR_LOADS = 16;                     // 1 KB loads per wave per pair
+
+__device__ __forceinline__ int proff(int r, int c) { return r * PR_ROW + ((c ^ (r & 7)) << 4); }
+
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_fp8r(
+    GemmArgs p, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ Y, EpiArgs e) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PR_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lsc[3 * SCALE_BUF];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wv >> 1, wn = wv & 1;
+  const int h = lane >> 5, r32 = lane & 31;
   const int b = blockIdx.x;
   const uint32_t lbase = lds_address(lds);
   const uint32_t sbase = lds_address(lsc);
 
-  // Units of work: whole tiles at tile sequence positions tile_seq(0..nt - 1), then
-  // (has_half) half u of the tail: rows 128 (u % 2) .. + 127 of tile nfull + u / 2.
+  // units: whole tiles at tile sequence positions tile_seq(0..nt - 1), then
+  // (has_half) half u of the tail: rows 128 (u % 2) .. + 127 of tile nfull + u / 2
   int nt = 0;
   while (tile_seq(nt, b, p.nwg) < p.nfull) ++nt;
   const int hu = tile_seq(nt, b, p.nwg) - p.nfull;
   const bool has_half = hu < 2 * p.ntail;
   const int nu = nt + (has_half ? 1 : 0);
-  const int nk1 = (p.kbytes1 + SROW - 1) / SROW;
-  const int nk2 = LOWRANK ? (p.kbytes2 + SROW - 1) / SROW : 0;
-  const int nk = nk1 + nk2;
+  const int np = (p.kbytes1 + PR_ROW - 1) / PR_ROW;  // pairs per unit
   struct Unit {
     int64_t m0, n0;
     int rows;
@@ -321,188 +329,144 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& p, const float* 
     return r;
   };
 
-  // lane geometry of the slab loads: instruction q of this wave fills slab rows
-  // 16 (4 wv + q) .. + 15; lane l writes physical chunk l % 4 of row + l / 4,
-  // which holds logical chunk (l % 4) ^ swz(row)
-  int lrow[4], cb[4];
+  // load q (0..7) of an operand: rows 64 wv + 8 q .. + 7; lane l writes row + l / 8,
+  // stage chunk l % 8, which holds the row's chunk (l % 8) ^ (l / 8)
+  const int lc = (lane & 7) ^ (lane >> 3);
+  uint32_t vrow[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    lrow[q] = 16 * (4 * wv + q) + (lane >> 2);
-    cb[q] = ((lane & 3) ^ swz(lrow[q])) * 16;
-  }
+  for (int q = 0; q < 8; ++q) vrow[q] = (uint32_t)((64 * wv + 8 * q + (lane >> 3)) * p.pitch1 + 16 * lc);
 
-  // The load stream: slab ks of the workgroup's unit ti, advanced one slab per
-  // call of next_src (unit coordinates recomputed at unit boundaries only).  A half
-  // unit's x slab rows 128 .. 255 lie outside its descriptor and load zeros.
-  struct SlabSrc {
+  struct PairSrc {
     u32x4 dx, dw, ds;
-    int pitch, kb, koff, stage, tpar;
+    int kb, koff, stage, tpar;
     bool first, valid;
   };
-  int s_ti = 0, s_ks = 0, s_stage = 0;
+  int s_ti = 0, s_kp = 0, s_stage = 0;
   Unit s_u{0, 0, 256};
   if (nu > 0) s_u = unit(0);
   auto next_src = [&]() {
-    SlabSrc r;
+    PairSrc r;
     r.valid = s_ti < nu;
     r.stage = s_stage;
-    r.first = s_ks == 0;
+    r.first = s_kp == 0;
     r.tpar = s_ti & 1;
-    const bool pass2 = LOWRANK && s_ks >= nk1;
-    r.pitch = pass2 ? p.pitch2 : p.pitch1;
-    r.kb = r.valid ? (pass2 ? p.kbytes2 : p.kbytes1) : 0;
-    r.koff = (pass2 ? s_ks - nk1 : s_ks) * SROW;
+    r.kb = r.valid ? p.kbytes1 : 0;
+    r.koff = s_kp * PR_ROW;
     const int64_t left = p.M - s_u.m0;
     const int64_t rm = left < 0 ? 0 : (left < s_u.rows ? left : s_u.rows);
     const int64_t rn = M_rows(p.N - s_u.n0);
-    r.dx = make_desc((pass2 ? p.a2 : p.a) + s_u.m0 * r.pitch, rm * r.pitch);
-    r.dw = make_desc((pass2 ? p.w2 : p.w) + s_u.n0 * r.pitch, rn * r.pitch);
-    if constexpr (ROWCOL) {
-      const bool row = wv < 2;
-      r.ds = make_desc(row ? sa + s_u.m0 : sb + s_u.n0, (row ? rm : rn) * 4);
-    }
-    s_stage = s_stage == NST - 1 ? 0 : s_stage + 1;
-    if (++s_ks == nk) {
-      s_ks = 0;
+    r.dx = make_desc(p.a + s_u.m0 * p.pitch1, rm * p.pitch1);
+    r.dw = make_desc(p.w + s_u.n0 * p.pitch1, rn * p.pitch1);
+    const bool row = wv < 2;
+    r.ds = make_desc(row ? sa + s_u.m0 : sb + s_u.n0, (row ? rm : rn) * 4);
+    s_stage ^= 1;
+    if (++s_kp == np) {
+      s_kp = 0;
       ++s_ti;
       if (s_ti < nu) s_u = unit(s_ti);
     }
     return r;
   };
-  auto issue = [&](const SlabSrc& s, int d) {
-    if (d < 8) {
-      const int q = d & 3;
-      const bool wslab = d >= 4;
-      const uint32_t dst = lbase + s.stage * STAGE + (wslab ? SLAB : 0) + (4 * wv + q) * 1024;
-      const uint32_t vo = s.koff + cb[q] < s.kb ? (uint32_t)(lrow[q] * s.pitch + cb[q]) : kOutOfRange;
-      dma16(dst, vo, wslab ? s.dw : s.dx, s.koff);
-    } else {
-      // scale vectors of a unit: wave w moves 128 floats of s_x (w = 0, 1) or s_w
-      // (w = 2, 3), 64 per instruction; other slabs load nothing into a spare area
-      const int h = d - 8;
-      const bool real = s.valid && s.first;
-      const uint32_t dst = sbase + (real ? s.tpar * SCALE_BUF : 2 * SCALE_BUF) + wv * 512 + h * 256;
-      const uint32_t vo = real ? (uint32_t)(((wv & 1) * 128 + h * 64 + lane) * 4) : kOutOfRange;
-      dma4(dst, vo, s.ds, 0);
-    }
+  // load d of a pair: 0..7 x rows, 8..15 W rows
+  auto issue = [&](const PairSrc& s, int d) {
+    const int q = d & 7;
+    const bool wl = d >= 8;
+    const uint32_t dst = lbase + s.stage * PR_STAGE + (wl ? PR_OPER : 0) + (8 * wv + q) * 1024;
+    const uint32_t vo = s.koff + 16 * lc < s.kb ? vrow[q] : kOutOfRange;
+    dma16(dst, vo, wl ? s.dw : s.dx, s.koff);
+  };
+  // the unit's output scales: wave w moves 128 floats of s_x (w = 0, 1) or s_w
+  // (w = 2, 3), 64 per load.  Every pair issues the two loads (out of range into a
+  // spare area unless the pair starts a unit): a branch here would let the compiler
+  // move the MFMAs around it
+  auto issue_scales = [&](const PairSrc& s, int hh) {
+    const bool real = s.valid && s.first;
+    const uint32_t dst = sbase + (real ? s.tpar * SCALE_BUF : 2 * SCALE_BUF) + wv * 512 + hh * 256;
+    const uint32_t vo = real ? (uint32_t)(((wv & 1) * 128 + hh * 64 + lane) * 4) : kOutOfRange;
+    dma4(dst, vo, s.ds, 0);
   };
 
-  // prologue: the first NST slabs of the stream, then slab 0's fragments
+  typedef Fp8Mma::Frag Frag;
+  Frag fw[4], fx[4];
+  auto frag = [&](const uint8_t* st, int row, int u) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(st + proff(row, 4 * u + 2 * h));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(st + proff(row, 4 * u + 2 * h + 1));
+    return Frag{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  // prologue: pair 0 (and unit 0's scales)
+  int st1 = 0;  // output stores in flight from the epilogue after the previous pair
+  {
+    const PairSrc src = next_src();
 #pragma unroll
-  for (int s0 = 0; s0 < NST; ++s0) {
-    const SlabSrc src = next_src();
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue(src, d);
+    for (int d = 0; d < PR_LOADS; ++d) issue(src, d);
+    issue_scales(src, 0);
+    issue_scales(src, 1);
   }
-  QPL_WAIT_VMCNT((NST - 1) * D);
-  __builtin_amdgcn_s_barrier();
-  typename T::Frag fw[T::SUB][4], fx[T::SUB][4];
+  int cur = 0;  // stage of the pair being multiplied
 
-  int st1 = 0, st2 = 0, st3 = 0;  // stores left in flight after iterations g - 1, g - 2, g - 3
-  int cur = 0;                     // stage of the slab being multiplied
-  // NJ: 32-row blocks of x per wavefront in the current unit (4 whole, 2 half).
-  // One slab: wait for the next slab, multiply this one while reading the next
-  // one's fragments (FRAGS) and issuing the loads of slab + NST.  Before the
-  // epilogue (and the low-rank rescale) the next fragments are read afterwards
-  // instead (read_frags), so that they do not occupy registers meanwhile.
-  auto read_frags = [&](auto nj) {
+  // One pair of a unit with NJ x tile-rows per wave (4 whole, 2 half).
+  auto pair = [&](Acc& acc, auto nj) {
     constexpr int NJ = decltype(nj)::value;
-    const uint8_t* nx = lds + cur * STAGE;
-#pragma unroll
-    for (int u = 0; u < T::SUB; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
-        if (i < NJ) fx[u][i] = T::read(nx, wm * 32 * NJ + i * 32 + (lane & 31), u, lane);
-      }
-  };
-  auto step = [&](Acc& acc, auto frags, auto nj) {
-    constexpr bool FRAGS = decltype(frags)::value;
-    constexpr int NJ = decltype(nj)::value;
-    constexpr int NMMA = 4 * NJ * T::SUB;
-    QPL_WAIT_LGKM0();
-    const int extra = st1 + st2 + st3;
-    if (extra == 0) {
-      QPL_WAIT_VMCNT((NST - 2) * D);
-    } else if (extra == NSTORE) {
-      QPL_WAIT_VMCNT((NST - 2) * D + NSTORE);
+    if (st1 == NSTORE) {
+      QPL_WAIT_VMCNT(NSTORE);
     } else {
       QPL_WAIT_VMCNT(0);
     }
-    __builtin_amdgcn_s_barrier();  // the next slab is in LDS for every wave; the previous slab's stage is free
-    const SlabSrc src = next_src();
-    cur = cur == NST - 1 ? 0 : cur + 1;
-    const uint8_t* nx = lds + cur * STAGE;
-#pragma unroll
-    for (int u = 0; u < T::SUB; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          acc[i][j] = T::mma(fw[u][i], fx[u][j], acc[i][j]);
-          const int k = 4 * NJ * u + NJ * i + j;
-          if (FRAGS && i == 3) fx[u][j] = T::read(nx, wm * 32 * NJ + j * 32 + (lane & 31), u, lane);
-          if (FRAGS && j == NJ - 1) fw[u][i] = T::read(nx + SLAB, wn * 128 + i * 32 + (lane & 31), u, lane);
-          // spread the D loads of slab + NST over this slab's MFMAs
-#pragma unroll
-          for (int d = 0; d < D; ++d)
-            if (k == (d * NMMA) / D) issue(src, d);
-        }
-    st3 = st2;
-    st2 = st1;
+    __builtin_amdgcn_s_barrier();
     st1 = 0;
+    const PairSrc src = next_src();
+    const uint8_t* cs = lds + cur * PR_STAGE;
+    cur ^= 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fw[i] = frag(cs + PR_OPER, wn * 128 + i * 32 + r32, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fx[j] = frag(cs, wm * 32 * NJ + j * 32 + r32, 0);
+    // slab 2P, with pair P + 1's loads and slab 2P + 1's fragment reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        acc[i][j] = Fp8Mma::mma(fw[i], fx[j], acc[i][j]);
+        const int k = NJ * i + j;
+        if (i == 3) fx[j] = frag(cs, wm * 32 * NJ + j * 32 + r32, 1);
+        if (j == NJ - 1) fw[i] = frag(cs + PR_OPER, wn * 128 + i * 32 + r32, 1);
+        // one load after each MFMA (a half unit has 8 MFMAs per slab: two after each)
+#pragma unroll
+        for (int d = 0; d < PR_LOADS; ++d)
+          if (k == (d * 4 * NJ) / PR_LOADS) issue(src, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    // slab 2P + 1, x tile-rows outer: its first MFMAs need the fragments that slab
+    // 2P freed first (all of W's, then x's in order)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i][j] = Fp8Mma::mma(fw[i], fx[j], acc[i][j]);
+        if (i == 0 && j == 0) issue_scales(src, 0);
+        if (i == 0 && j == 1) issue_scales(src, 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
 
-  using Yes = std::integral_constant<bool, true>;
-  using No = std::integral_constant<bool, false>;
   using Whole = std::integral_constant<int, 4>;
   using Half = std::integral_constant<int, 2>;
-  auto epilogue = [&](const Acc& acc, int ti, auto nj) {
+  auto run_unit = [&](int ti, auto nj) {
     constexpr int NJ = decltype(nj)::value;
+    Acc acc;
+    zero_acc(acc);
+    for (int kp = 0; kp < np; ++kp) pair(acc, nj);
     const Unit un = unit(ti);
-    if constexpr (ROWCOL) {
-      const float* ls = reinterpret_cast<const float*>(lsc + (ti & 1) * SCALE_BUF);
-      st1 = __builtin_amdgcn_readfirstlane(store_tile<NJ, 4, EPI>(
-          acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int r) { return ls[r]; },
-          [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); }, e));
-    } else {
-      st1 = __builtin_amdgcn_readfirstlane(store_tile<NJ, 4, EPI>(
-          acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return gscale; },
-          [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e));
-    }
-    if (st1 == 0) st2 = st3 = 0;
+    const float* ls = reinterpret_cast<const float*>(lsc + (ti & 1) * SCALE_BUF);
+    st1 = __builtin_amdgcn_readfirstlane(store_tile<NJ, 4, EPI>(
+        acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int r) { return ls[r]; },
+        [&](int c) { return *reinterpret_cast<const f32x4*>(&ls[256 + c]); }, e));
   };
-
-  if (nt > 0)
-    read_frags(Whole{});
-  else
-    read_frags(Half{});
-  for (int ti = 0; ti < nt; ++ti) {
-    Acc acc;
-    zero_acc(acc);
-    for (int kt = 0; kt < nk - 1; ++kt) step(acc, Yes{}, Whole{});
-    step(acc, No{}, Whole{});
-    epilogue(acc, ti, Whole{});
-    if (ti + 1 < nt)
-      read_frags(Whole{});
-    else
-      read_frags(Half{});
-  }
-  if (has_half) {
-    Acc acc;
-    zero_acc(acc);
-    for (int kt = 0; kt < nk - 1; ++kt) step(acc, Yes{}, Half{});
-    step(acc, No{}, Half{});
-    epilogue(acc, nt, Half{});
-  }
+  for (int ti = 0; ti < nt; ++ti) run_unit(ti, Whole{});
+  if (has_half) run_unit(nt, Half{});
   QPL_WAIT_VMCNT(0);
   QPL_WAIT_LGKM0();
-}
-
-template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_fp8r(
-    GemmArgs p, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ Y, EpiArgs e) {
-  gemm_persistent<Fp8Mma, true, false, EPI>(p, sa, sb, 1.0f, Y, e);
 }
 
 // ---------------------------------------------------------------------------
@@ -518,38 +482,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // (V_MFMA_F32_32X32X16_F16, fp32 accumulation).  input_scale * weight_scale_2
 // scales the fp32 result.
 //
-// Tiling and schedule follow gemm_persistent (256 x 256 tiles, 4 wavefronts of
+// Tiling and schedule follow the fp8r GEMM (256 x 256 tiles, 4 wavefronts of
 // 128 x 128, persistent workgroups, XCD-grouped tile order, half tiles in the
-// last round, y^T epilogue), with these slabs:
-// * a slab is 128 K elements: 64 code bytes per row (16 KB per operand) and 8
-//   block-scale bytes per row (2 KB per operand, slab-major in global memory:
-//   [K/128][rows][8], zero past K/16, so one 1 KB load moves 128 rows' scales);
-//   a stage is 36 KB and four stages ring through 144 KB of LDS;
-// * lane half h of a fragment row takes blocks 4h .. 4h + 3 of the slab: code
-//   bytes 32h .. 32h + 31 (two 16-byte LDS reads) and one scale dword.  MFMA step
-//   s (0..7) multiplies nibbles 8 (s % 2) .. + 7 of block 4h + s / 2; both
-//   operands use this order, so the pairs of a product are the same k;
-// * software pipeline across slabs: the second half of a slab's codes is read
-//   from LDS when the slab starts, and once its steps 0-3 have used the first half,
-//   the first half and the scales of the next slab are read into those registers.
-//   The barrier at the top of slab g therefore waits for slab g + 1 and frees the
-//   stage of slab g - 1, into which slab g + 3 is issued (9 loads per wave: 8 of
-//   codes and 1 of scales, spread over the slab's 128 MFMAs);
+// last round, y^T epilogue, slab pairs moved as whole 128-byte lines), with these
+// slabs and pairs:
+// * a slab is 128 K elements: 64 code bytes per row and 8 block-scale bytes per row
+//   (slab-major in global memory: [K/128][rows][8], zero past K/16, so one 1 KB
+//   load moves 128 rows' scales of one slab); a stage holds a pair of slabs of both
+//   operands (codes 256 rows x 128 bytes per operand, scales two planes of 256 rows
+//   x 8 bytes per operand, 72 KB), and two stages ring through 144 KB of LDS;
+// * lane half h of a fragment row takes blocks 4h .. 4h + 3 of a slab: code bytes
+//   32h .. 32h + 31 (two 16-byte LDS reads, four MFMA steps each) and one scale
+//   dword.  MFMA step s (0..7) multiplies nibbles 8 (s % 2) .. + 7 of block
+//   4h + s / 2; both operands use this order, so the pairs of a product are the
+//   same k;
+// * each step expands the next step's eight fragments while its 16 MFMAs run,
+//   one MFMA then a share of the expansion in turn, into the other of two fragment
+//   sets; the codes of the next group of four steps are read during the current
+//   group, and each slab's scales one slab ahead;
+// * pair P (16 steps) issues pair P + 1's loads during its first six steps (16 of
+//   codes and 2 of scales per wave) into the other stage; at step 12 every wave
+//   waits for them and meets at a barrier, after which pair P + 1 is in LDS for
+//   every wave and every wave is done reading pair P's stage, so steps 12 .. 15
+//   read pair P + 1's first codes and scales and expand its first step;
 // * blocks past K have scale 0 (they multiply to 0 whatever codes straddle the row
 //   end), rows past M or N read zeros through the buffer range check.
-// LOWRANK: after the packed slabs of a tile the accumulators are multiplied by
-// gscale, then bf16 slabs of [T_hi | T_lo] and [L2^T | L2^T] (64 bytes per row)
-// continue the same accumulation on the bf16 MFMA, so y = bf16(gscale x_q w_q^T
-// + T L2) with T unscaled.
+// LOWRANK: after the packed pairs of a tile the accumulators are multiplied by
+// gscale, then bf16 pairs of [T_hi | T_lo] and [L2^T | L2^T] (128 bytes per row, four
+// 32 x 32 x 16 steps) continue the same accumulation on the bf16 MFMA, so
+// y = bf16(gscale x_q w_q^T + T L2) with T unscaled.
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int PK_CODES = 256 * SROW;                // code bytes per operand per stage
-constexpr int PK_SC = 256 * 8;                      // block-scale bytes per operand per stage
+constexpr int PK_CODES = 256 * PR_ROW;              // code bytes per operand per stage (two slabs)
+constexpr int PK_PLANE = 256 * 8;                   // one slab's block scales per operand
+constexpr int PK_SC = 2 * PK_PLANE;                 // both slabs' block scales per operand
 constexpr int PK_STAGE = 2 * PK_CODES + 2 * PK_SC;  // [x codes][w codes][x scales][w scales]
-constexpr int PK_NST = 4;
-constexpr int PK_D = 9;                             // loads per wave per slab
+constexpr int PK_LOADS = 18;                        // loads per wave per pair: 16 of codes, 2 of scales
 
 struct PackedArgs {
   const uint8_t* xq;   // activation codes [M, K/2]
@@ -583,7 +553,7 @@ __device__ __forceinline__ f16x8 fp4_expand(uint32_t cw, f16x2 s) {
 template <bool LOWRANK, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
     PackedArgs p, float gscale, uint16_t* __restrict__ Y, EpiArgs e) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[PK_NST * PK_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * PK_STAGE];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wv >> 1, wn = wv & 1;
@@ -603,9 +573,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int hu = LOWRANK ? 0 : tile_seq(nt, b, p.nwg) - p.nfull;
   const bool has_half = !LOWRANK && hu < 2 * p.ntail;
   const int nu = nt + (has_half ? 1 : 0);
-  const int nk1 = p.nk1;
-  const int nk2 = LOWRANK ? (p.kbytes2 + SROW - 1) / SROW : 0;
-  const int nk = nk1 + nk2;
+  const int np1 = (p.nk1 + 1) >> 1;                             // packed pairs per unit
+  const int np2 = LOWRANK ? (p.kbytes2 + PR_ROW - 1) / PR_ROW : 0;  // low-rank pairs
+  const int npu = np1 + np2;
   struct Unit {
     int64_t m0, n0;
     int rows;
@@ -623,35 +593,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return r;
   };
 
-  // row loads: instruction q of this wave fills slab rows 16 (4 wv + q) .. + 15;
-  // lane l writes physical chunk l % 4 of row + l / 4 (logical chunk (l % 4) ^ swz),
-  // at byte offset vo1 (packed rows) or vo2 (low-rank rows) of the tile
-  int cb[4];
-  uint32_t vo1[4], vo2[4];
+  // code loads q (0..7) of an operand: rows 64 wv + 8 q .. + 7 of the pair; lane l
+  // writes row + l / 8, stage chunk l % 8, which holds the row's chunk (l % 8) ^ (l / 8)
+  const int lc = (lane & 7) ^ (lane >> 3);
+  uint32_t vo1[8], vo2[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int lrow = 16 * (4 * wv + q) + (lane >> 2);
-    cb[q] = ((lane & 3) ^ swz(lrow)) * 16;
-    vo1[q] = (uint32_t)(lrow * p.cpitch + cb[q]);
-    vo2[q] = LOWRANK ? (uint32_t)(lrow * p.pitch2 + cb[q]) : 0u;
+  for (int q = 0; q < 8; ++q) {
+    const int lrow = 64 * wv + 8 * q + (lane >> 3);
+    vo1[q] = (uint32_t)(lrow * p.cpitch + 16 * lc);
+    vo2[q] = LOWRANK ? (uint32_t)(lrow * p.pitch2 + 16 * lc) : 0u;
   }
-  // scale loads: wave wv moves rows 128 (wv % 2) .. + 127 of operand wv / 2 (x, W)
+  // scale loads: wave wv moves rows 128 (wv % 2) .. + 127 of operand wv / 2 (x, W),
+  // one load per slab of the pair
   const bool sc_x = wv < 2;
   const int sc_r0 = 128 * (wv & 1);
 
-  struct SlabSrc {
-    u32x4 dx, dw, ds;
+  // The pair stream.  Its sources change only where it enters a unit or the unit's
+  // low-rank pass: the code descriptors and the scale rows are worked out there;
+  // from pair to pair the scale address moves by two slabs of scales.
+  struct PairSrc {
+    u32x4 dx, dw, ds0, ds1;
     int kb, koff, stage;
     bool pass2;
   };
-  // The slab stream's sources change only where it enters a unit or the unit's
-  // low-rank pass: then the code descriptors, the row count and the first slab's
-  // scale address are worked out; from slab to slab only the scale address moves
-  // (by one slab of scales) with the stage and the K offset.
-  int s_ti = 0, s_ks = 0, s_stage = 0;
+  int s_ti = 0, s_kp = 0, s_stage = 0;
   Unit s_u{0, 0, 256};
   u32x4 s_dx{}, s_dw{};
-  const uint8_t* s_sc = nullptr;  // scale bytes of the next slab (this wave's rows)
+  const uint8_t* s_sc = nullptr;  // this wave's scale bytes of the next pair's first slab
   int64_t s_scb = 0;              // their count: 8 per row present, 0 in a low-rank pass
   int s_kb = 0;
   const int64_t sstride = 8 * (sc_x ? p.M : p.N);
@@ -672,18 +640,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     enter(false);
   }
   auto next_src = [&]() {
-    SlabSrc r;
+    PairSrc r;
     r.stage = s_stage;
-    r.pass2 = LOWRANK && s_ks >= nk1;
+    r.pass2 = LOWRANK && s_kp >= np1;
     r.kb = s_kb;
-    r.koff = (r.pass2 ? s_ks - nk1 : s_ks) * SROW;
+    r.koff = (r.pass2 ? s_kp - np1 : s_kp) * PR_ROW;
     r.dx = s_dx;
     r.dw = s_dw;
-    r.ds = make_desc(s_sc, s_scb);
-    s_sc += sstride;
-    s_stage = s_stage == PK_NST - 1 ? 0 : s_stage + 1;
-    if (++s_ks == nk) {
-      s_ks = 0;
+    // the pair's second slab exists unless the unit has an odd number of slabs
+    const bool two = r.pass2 || 2 * s_kp + 1 < p.nk1;
+    r.ds0 = make_desc(s_sc, s_scb);
+    r.ds1 = make_desc(s_sc + sstride, two ? s_scb : 0);
+    s_sc += 2 * sstride;
+    s_stage ^= 1;
+    if (++s_kp == npu) {
+      s_kp = 0;
       if (++s_ti < nu) {
         s_u = unit(s_ti);
         enter(false);
@@ -691,121 +662,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         s_kb = 0;  // past the last unit: every load reads zeros
         s_scb = 0;
       }
-    } else if (LOWRANK && s_ks == nk1) {
+    } else if (LOWRANK && s_kp == np1) {
       enter(true);
     }
     return r;
   };
-  auto issue = [&](const SlabSrc& s, int d) {
+  auto issue = [&](const PairSrc& s, int d) {
     const uint32_t st = lbase + s.stage * PK_STAGE;
-    if (d < 8) {
-      const int q = d & 3;
-      const bool wslab = d >= 4;
-      const uint32_t vo = s.koff + cb[q] < s.kb ? (LOWRANK && s.pass2 ? vo2[q] : vo1[q]) : kOutOfRange;
-      dma16(st + (wslab ? PK_CODES : 0) + (4 * wv + q) * 1024, vo, wslab ? s.dw : s.dx, s.koff);
+    if (d < 16) {
+      const int q = d & 7;
+      const bool wl = d >= 8;
+      const uint32_t vo = s.koff + 16 * lc < s.kb ? (LOWRANK && s.pass2 ? vo2[q] : vo1[q]) : kOutOfRange;
+      dma16(st + (wl ? PK_CODES : 0) + (8 * wv + q) * 1024, vo, wl ? s.dw : s.dx, s.koff);
     } else {
-      // 1 KB of scales (128 rows x 8 bytes); rows past the unit read zero
-      dma16(st + 2 * PK_CODES + (sc_x ? 0 : PK_SC) + sc_r0 * 8, (uint32_t)lane * 16u, s.ds, 0);
+      // 1 KB of one slab's scales (128 rows x 8 bytes); rows past the unit read zero
+      const int u = d - 16;
+      dma16(st + 2 * PK_CODES + (sc_x ? 0 : PK_SC) + u * PK_PLANE + sc_r0 * 8, (uint32_t)lane * 16u,
+            u ? s.ds1 : s.ds0, 0);
     }
   };
-
-  // prologue: slabs 0 .. 2, then slab 0's first code half and scales
-#pragma unroll
-  for (int s0 = 0; s0 < PK_NST - 1; ++s0) {
-    const SlabSrc src = next_src();
-#pragma unroll
-    for (int d = 0; d < PK_D; ++d) issue(src, d);
-  }
-  QPL_WAIT_VMCNT(2 * PK_D);
-  __builtin_amdgcn_s_barrier();
 
   // fragment rows of tile-row t of a unit with nj x tile-rows: t < 4 W, t >= 4 x
   auto frow = [&](int t, int nj) { return t < 4 ? wn * 128 + t * 32 + r32 : wm * 32 * nj + (t - 4) * 32 + r32; };
-  // Codes of step group g (steps 4 g .. 4 g + 3) of tile-rows t0 .. t0 + 3 of the slab
-  // in stage st: one 16-byte chunk 2 h + g per row, dword s % 4 of it for step s
-  auto read_codes = [&](const uint8_t* st, int nj, int g, int t0, int ntr, u32x4 (&dst)[8]) {
+  // codes of group g (steps 4 g .. 4 g + 3) of slab u of the pair in stage st, for
+  // tile-rows t0 .. t0 + 3: one 16-byte chunk 4 u + 2 h + g per row
+  auto read_codes = [&](const uint8_t* st, int nj, int u, int g, int t0, int ntr, u32x4 (&dst)[8]) {
 #pragma unroll
     for (int t = t0; t < t0 + 4; ++t)
-      if (t < ntr) dst[t] = *reinterpret_cast<const u32x4*>(st + (t < 4 ? PK_CODES : 0) + soff(frow(t, nj), 2 * h + g));
+      if (t < ntr)
+        dst[t] = *reinterpret_cast<const u32x4*>(st + (t < 4 ? PK_CODES : 0) + proff(frow(t, nj), 4 * u + 2 * h + g));
   };
-  // block-scale dword (blocks 4 h .. 4 h + 3) of every tile-row of the slab in stage st
-  auto read_scales = [&](const uint8_t* st, int nj, uint32_t (&dst)[8]) {
+  // block-scale dword (blocks 4 h .. 4 h + 3) of slab u of every tile-row
+  auto read_scales = [&](const uint8_t* st, int nj, int u, uint32_t (&dst)[8]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      dst[t] = *reinterpret_cast<const uint32_t*>(st + 2 * PK_CODES + (t < 4 ? PK_SC : 0) + frow(t, nj) * 8 + 4 * h);
+      dst[t] = *reinterpret_cast<const uint32_t*>(st + 2 * PK_CODES + (t < 4 ? PK_SC : 0) + u * PK_PLANE +
+                                                  frow(t, nj) * 8 + 4 * h);
   };
-  // Two fragment sets alternate: while step s is multiplied from F[s % 2], step s + 1
-  // is expanded into F[(s + 1) % 2], so no fragment is copied.  Codes come a group of
-  // four steps at a time into CW[g % 2]; the next group's reads are issued during the
-  // first two steps of the current one.  Across slabs, the second half of a slab
-  // reads the next packed slab's first group and scales, and its last step expands
-  // the next slab's first step.
+  // Fragment sets F[s % 2], code groups CW[g % 2] (group g of the pair: slab g / 2,
+  // steps 4 (g % 2) ..), scale dwords SC[u] of the pair's slab u.
   f16x8 F[2][8];
   u32x4 CW[2][8];
-  uint32_t sc[8];
-  auto expand_step = [&](int s, const uint32_t (&scd)[8], f16x8 (&dst)[8], int ntr) {
+  uint32_t SC[2][8];
+  // expand step s (0..15) of the pair into dst
+  auto expand_step = [&](int s, f16x8 (&dst)[8], int ntr) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      if (t < ntr) dst[t] = fp4_expand(CW[(s >> 2) & 1][t][s & 3], e4m3_pair(scd[t], (s >> 1) & 3));
+      if (t < ntr) dst[t] = fp4_expand(CW[(s >> 2) & 1][t][s & 3], e4m3_pair(SC[s >> 3][t], (s >> 1) & 3));
   };
-  // first step of the slab in stage st (a unit with nj x tile-rows), unpipelined
+  // first step of the pair in stage st (a unit with nj x tile-rows), unpipelined
   auto prime = [&](const uint8_t* st, int nj) {
-    read_codes(st, nj, 0, 0, 8, CW[0]);
-    read_codes(st, nj, 0, 4, 8, CW[0]);
-    read_scales(st, nj, sc);
-    expand_step(0, sc, F[0], 8);
+    read_codes(st, nj, 0, 0, 0, 8, CW[0]);
+    read_codes(st, nj, 0, 0, 4, 8, CW[0]);
+    read_scales(st, nj, 0, SC[0]);
+    expand_step(0, F[0], 8);
   };
-  prime(lds, nt > 0 ? 4 : 2);
-
-  int cur = 0;                // stage of the slab being multiplied
-  int st1 = 0, st2 = 0;       // stores left in flight after iterations g - 1, g - 2
-  // Top of a slab: slab g + 1 has landed (issued after it: slab g + 2's loads and
-  // the stores of the epilogues after iterations g - 2 and g - 1), every wave is
-  // done with slab g - 1, whose stage receives slab g + 3.
-  auto top = [&]() {
-    QPL_WAIT_LGKM0();
-    const int extra = st1 + st2;
-    if (extra == 0) {
-      QPL_WAIT_VMCNT(PK_D);
-    } else if (extra == NSTORE) {
-      QPL_WAIT_VMCNT(PK_D + NSTORE);
-    } else {
-      QPL_WAIT_VMCNT(0);
-    }
+  // every wave's loads of the pair issued last have landed, and every wave is done
+  // with the stage read before it
+  auto sync = [&]() {
+    QPL_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
-    st2 = st1;
-    st1 = 0;
-    return next_src();
   };
 
-  // A packed slab.  njn: x tile-rows of the unit the next slab belongs to, or 0
-  // when the next slab is not a packed one (its first step is then primed by
-  // whoever starts it).
-  auto step_packed = [&](Acc& acc, auto nj, int njn) {
+  // prologue: pair 0, then its first step
+  {
+    const PairSrc src = next_src();
+#pragma unroll
+    for (int d = 0; d < PK_LOADS; ++d) issue(src, d);
+  }
+  sync();
+  prime(lds, nt > 0 ? 4 : 2);
+  int cur = 0;  // stage of the pair being multiplied
+
+  // A packed pair.  njn: x tile-rows of the unit the next pair belongs to, or 0 when
+  // the next pair is not a packed one (its first step is then primed by whoever
+  // starts it).  The next pair's first group and scales are read and expanded
+  // whether or not it is packed (without branches, so the expansion stays among
+  // this pair's MFMAs); when it is not, the values are not used.
+  auto pair_packed = [&](Acc& acc, auto nj, int njn) {
     constexpr int NJ = decltype(nj)::value;
-    constexpr int NMMA = 32 * NJ;  // 8 steps x 4 x NJ
-    const SlabSrc src = top();
+    const PairSrc src = next_src();
     const uint8_t* cs = lds + cur * PK_STAGE;
-    cur = cur == PK_NST - 1 ? 0 : cur + 1;
+    cur ^= 1;
     const uint8_t* ns = lds + cur * PK_STAGE;
-    uint32_t scn[8];
-    // The next slab's first group is read and expanded whether or not it is a packed
-    // slab (without branches, so the expansion stays among this slab's MFMAs); when it
-    // is not, the values are not used, and whoever starts that slab primes it.
     const int njr = njn ? njn : NJ;
-    static_for<0, 8>([&](auto sc_) __attribute__((always_inline)) {
+    static_for<0, 16>([&](auto sc_) __attribute__((always_inline)) {
       constexpr int s = decltype(sc_)::value;
-      // the next group's codes: this slab's second group, or the next slab's first
-      if constexpr (s == 0 || s == 1) read_codes(cs, NJ, 1, 4 * s, 4 + NJ, CW[1]);
-      if constexpr (s == 4 || s == 5) read_codes(ns, njr, 0, 4 * (s - 4), 8, CW[0]);
-      if constexpr (s == 5) read_scales(ns, njr, scn);
+      if constexpr (s == 12) sync();
+      // the next group's codes: groups 1 .. 3 of this pair, then group 0 of the next
+      if constexpr (s % 4 < 2 && s < 12) read_codes(cs, NJ, ((s >> 2) + 1) >> 1, ((s >> 2) + 1) & 1, 4 * (s % 4), 4 + NJ,
+                                                   CW[((s >> 2) + 1) & 1]);
+      if constexpr (s == 12 || s == 13) read_codes(ns, njr, 0, 0, 4 * (s - 12), 8, CW[0]);
+      if constexpr (s == 5) read_scales(cs, NJ, 1, SC[1]);
+      if constexpr (s == 13) read_scales(ns, njr, 0, SC[0]);
       // the next step's fragments
-      if constexpr (s + 1 < 8) {
-        expand_step(s + 1, sc, F[(s + 1) & 1], 4 + NJ);
+      if constexpr (s + 1 < 16) {
+        expand_step(s + 1, F[(s + 1) & 1], 4 + NJ);
       } else {
-        expand_step(0, scn, F[0], 8);
+        expand_step(0, F[0], 8);
       }
-      // this step's MFMAs, with the slab loads spread among them
+      // this step's MFMAs; pair P + 1's loads after some of them in steps 0 .. 5
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -813,11 +769,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[s & 1][i], F[s & 1][4 + j], acc[i][j], 0, 0, 0);
           const int k = s * 4 * NJ + i * NJ + j;
 #pragma unroll
-          for (int d = 0; d < PK_D; ++d)
-            if (k == (d * NMMA) / PK_D) issue(src, d);
+          for (int d = 0; d < PK_LOADS; ++d)
+            if (k == d * (NJ == 4 ? 5 : 2) + 1) issue(src, d);
         }
-      // one MFMA, then a share of the expansion, in turn: the expansion of the next
-      // step hides under this step's MFMAs
+      // one MFMA, then a share of the expansion, in turn
 #pragma unroll
       for (int m = 0; m < 4 * NJ; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -826,25 +781,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-#pragma unroll
-    for (int t = 0; t < 8; ++t) sc[t] = scn[t];
   };
 
-  // A bf16 slab of the low-rank pass (fragments read from its stage at the top).
-  auto step_lowrank = [&](Acc& acc, auto nj, int njn) {
+  // A bf16 pair of the low-rank pass: four 32 x 32 x 16 steps, fragments read from
+  // its stage; the next pair's loads after some MFMAs of steps 0 .. 1, the sync
+  // before step 3, and the next unit's first step primed at the end.
+  auto pair_lowrank = [&](Acc& acc, auto nj, int njn) {
     constexpr int NJ = decltype(nj)::value;
-    constexpr int NMMA = 8 * NJ;
-    const SlabSrc src = top();
+    const PairSrc src = next_src();
     const uint8_t* cs = lds + cur * PK_STAGE;
-    cur = cur == PK_NST - 1 ? 0 : cur + 1;
+    cur ^= 1;
     const uint8_t* ns = lds + cur * PK_STAGE;
-    static_for<0, 2>([&](auto uc) __attribute__((always_inline)) {
+    static_for<0, 4>([&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
+      if constexpr (u == 3) sync();
       bf16x8 fw[4], fx[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fw[i] = Bf16Mma::read(cs + PK_CODES, frow(i, NJ), u, lane);
+      for (int i = 0; i < 4; ++i)
+        fw[i] = *reinterpret_cast<const bf16x8*>(cs + PK_CODES + proff(frow(i, NJ), 2 * u + h));
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) fx[j] = Bf16Mma::read(cs, frow(4 + j, NJ), u, lane);
+      for (int j = 0; j < NJ; ++j)
+        fx[j] = *reinterpret_cast<const bf16x8*>(cs + proff(frow(4 + j, NJ), 2 * u + h));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -852,8 +809,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           acc[i][j] = Bf16Mma::mma(fw[i], fx[j], acc[i][j]);
           const int k = u * 4 * NJ + i * NJ + j;
 #pragma unroll
-          for (int d = 0; d < PK_D; ++d)
-            if (k == (d * NMMA) / PK_D) issue(src, d);
+          for (int d = 0; d < PK_LOADS; ++d)
+            if (k == d) issue(src, d);
         }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -869,7 +826,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int njn = ti + 1 < nt ? 4 : (ti + 1 < nu ? 2 : 0);
     Acc acc;
     zero_acc(acc);
-    for (int ks = 0; ks < nk1; ++ks) step_packed(acc, nj, ks + 1 < nk1 ? NJ : (nk2 > 0 ? 0 : njn));
+    for (int kp = 0; kp < np1; ++kp) pair_packed(acc, nj, kp + 1 < np1 ? NJ : (np2 > 0 ? 0 : njn));
     if constexpr (LOWRANK) {
       // the 4-bit product in output units; each tile goes back to its accumulator
       // registers at once (the empty asm pins it there), so that the scaled values do
@@ -879,15 +836,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         acc[q / NJ][q % NJ] = acc[q / NJ][q % NJ] * gscale;
         asm volatile("" : "+a"(acc[q / NJ][q % NJ]));
       });
-      for (int ks = 0; ks < nk2; ++ks) step_lowrank(acc, nj, ks + 1 < nk2 ? 0 : njn);
+      for (int kp = 0; kp < np2; ++kp) pair_lowrank(acc, nj, kp + 1 < np2 ? 0 : njn);
     }
     const Unit un = unit(ti);
-    // the store count is wave-uniform; keeping it in a scalar register keeps the wait
-    // at the next slab's top a scalar branch
-    st1 = __builtin_amdgcn_readfirstlane(store_tile<NJ, 4, EPI>(
+    store_tile<NJ, 4, EPI>(
         acc, wm, wn, lane, un.m0, un.n0, p.M, p.N, Y, [&](int) { return escale; },
-        [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e));
-    if (st1 == 0) st2 = 0;
+        [&](int) { return f32x4{1.0f, 1.0f, 1.0f, 1.0f}; }, e);
   };
   for (int ti = 0; ti < nt; ++ti) run_unit(ti, Whole{});
   if (has_half) run_unit(nt, Half{});
