@@ -196,12 +196,10 @@ __device__ __forceinline__ uint16_t* out_ptr(uint16_t* __restrict__ y, int64_t m
 // n0 + 128 wn + ..., wn in 0..1; 2: n0 + 64 wn + ..., wn in 0..3).  Returns the
 // number of store instructions left in flight: 2 NJ NI on the interior path, 0 on
 // the edge path (which checks every element and drains its stores).
-template <int NJ, int NI = 4, int EPI = 0, class RowScale, class ColScale>
-__device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
-                                          int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
-                                          const ColScale& cs, const EpiArgs& e = EpiArgs{}) {
-  // interior: the wavefront's rows and columns all inside the matrix
-  const bool fast = m0 + (wm + 1) * 32 * NJ <= M && n0 + (wn + 1) * 32 * NI <= N && (N & 7) == 0;
+template <int NJ, int NI, int EPI, bool FAST, class RowScale, class ColScale>
+__device__ __forceinline__ void store_tile_path(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
+                                                int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
+                                                const ColScale& cs, const EpiArgs& e) {
   // unrolled at compile time: with a heavy epilogue the body exceeds what the
   // unroll pragma accepts, and a rolled loop would index acc dynamically (scratch)
   static_for<0, NJ>([&](auto jc) __attribute__((always_inline)) {
@@ -234,7 +232,7 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
         const int64_t n = n0 + wn * 32 * NI + i * 32 + (2 * gp + (lane >> 5)) * 8;
         // the segment's eight columns stay inside one head (head_dim >= 8, n % 8 == 0)
         uint16_t* dst = out_ptr<EPI>(y, m, n, N, e);
-        if (fast) {
+        if constexpr (FAST) {
           *reinterpret_cast<u32x4*>(dst) = v;
         } else if (m < M) {
           const uint32_t el[4] = {v.x, v.y, v.z, v.w};
@@ -248,7 +246,20 @@ __device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int la
         }
       }
   });
-  if (fast) return 2 * NJ * NI;
+}
+
+template <int NJ, int NI = 4, int EPI = 0, class RowScale, class ColScale>
+__device__ __forceinline__ int store_tile(const Acc& acc, int wm, int wn, int lane, int64_t m0, int64_t n0,
+                                          int64_t M, int64_t N, uint16_t* __restrict__ y, const RowScale& rs,
+                                          const ColScale& cs, const EpiArgs& e = EpiArgs{}) {
+  // interior: the wavefront's rows and columns all inside the matrix; the two paths
+  // are separate code, so the interior one has no per-segment branches
+  const bool fast = m0 + (wm + 1) * 32 * NJ <= M && n0 + (wn + 1) * 32 * NI <= N && (N & 7) == 0;
+  if (fast) {
+    store_tile_path<NJ, NI, EPI, true>(acc, wm, wn, lane, m0, n0, M, N, y, rs, cs, e);
+    return 2 * NJ * NI;
+  }
+  store_tile_path<NJ, NI, EPI, false>(acc, wm, wn, lane, m0, n0, M, N, y, rs, cs, e);
   QPL_WAIT_VMCNT(0);
   return 0;
 }
