@@ -216,6 +216,22 @@ def main():
                  "quant_nvfp4_linear": gbs("quant_nvfp4_linear", 2.5625 * lin["nvfp4"]["M"] * lin["nvfp4"]["K"]),
                  "quant_nvfp4_lowrank": gbs("quant_nvfp4_lowrank", 2.5625 * lin["svdq"]["M"] * lin["svdq"]["K"] +
                                             4.0 * lin["svdq"]["M"] * 32 * ((lin["svdq"]["R"] + 31) // 32))}
+    # reference: a plain device copy of the same activation tensor (read once, written
+    # once), timed like the quantizers with events around each launch, so that the
+    # figures above can be read against what a copy of that size reaches
+    src_x = lin["fp8r"]["x"]
+    dst_x = torch.empty_like(src_x)
+    copy_ev = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst_x.copy_(src_x)
+        b.record()
+        copy_ev.append((a, b))
+    torch.cuda.synchronize()
+    copy_ms = sum(a.elapsed_time(b) for a, b in copy_ev) / len(copy_ev)
+    quant_gbs["copy_reference"] = round(2.0 * src_x.numel() * src_x.element_size() / (copy_ms * 1e-3) / 1e9, 1)
+    del dst_x
 
     cold = measure_cold(args, qpl, torch, lin, order, total_flops)
     extras = None if args.no_extras else measure_extras(args, qpl, torch, dev, bf16, lin, kern, make, smooth_factors)

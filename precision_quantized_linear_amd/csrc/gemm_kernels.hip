@@ -715,11 +715,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   f16x8 F[2][8];
   u32x4 CW[2][8];
   uint32_t SC[2][8];
-  // expand step s (0..15) of the pair into dst
+  // expand step s (0..15) of the pair into dst: the scale of the step's block is
+  // one half of an f16 pair converted from two scale bytes, broadcast to both halves
   auto expand_step = [&](int s, f16x8 (&dst)[8], int ntr) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      if (t < ntr) dst[t] = fp4_expand(CW[(s >> 2) & 1][t][s & 3], e4m3_pair(SC[s >> 3][t], (s >> 1) & 3));
+      if (t < ntr) {
+        const f16x2 two = ((s >> 2) & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SC[s >> 3][t], 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SC[s >> 3][t], 1.0f, false);
+        const _Float16 sv = two[(s >> 1) & 1];
+        dst[t] = fp4_expand(CW[(s >> 2) & 1][t][s & 3], f16x2{sv, sv});
+      }
   };
   // first step of the pair in stage st (a unit with nj x tile-rows), unpipelined
   auto prime = [&](const uint8_t* st, int nj) {
