@@ -16,10 +16,10 @@ timing by the library's own quantizers, as a pre-quantized checkpoint would
 arrive.  Inputs are seeded synthetic data (see synthetic/workloads.py).
 
 The roofline object covers the dominant kernel (the nvfp4 GEMM at 4608 x 3072 x
-12288): after the timed region, a second pass of the same steps times every launch
-with HIP events on the launch stream (the library's event timing); the roofline
-takes that kernel's average over all of them, and `parts` and `kernels` come from
-the same pass.  The
+12288): after the timed region, a pass of the same steps times every launch with
+HIP events on the launch stream (the library's event timing), and the roofline
+takes that kernel's average over all of them (`kernels` lists every kind).  `parts`
+comes from another pass with one event pair around each linear and none inside it.  The
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload
 (rank 0, one GPU only).  `cold` times the same step with its tensors rotated over three
 copies (working set above the 256 MB last-level cache).  `extras` times what lies beyond the step: the svdq linear
@@ -162,9 +162,9 @@ def main():
     total_flops = sum(lin[k]["flops"] for k in order)
     value = total_flops / (ms_step * 1e-3) / 1e12
 
-    # ---------------------------------------------------------------- breakdown pass
+    # ---------------------------------------------------------------- breakdown passes
+    # per linear: an event pair around each call, nothing inside it
     ev = {k: [] for k in order}
-    qpl.timing_enable(True)
     for _ in range(args.steps):
         for k in order:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -172,6 +172,13 @@ def main():
             run(k)
             b.record()
             ev[k].append((a, b))
+    torch.cuda.synchronize()
+    # per kernel: the library's events around each of its launches (a pass of its own,
+    # since those events lengthen the linear they sit in)
+    qpl.timing_enable(True)
+    for _ in range(args.steps):
+        for k in order:
+            run(k)
     torch.cuda.synchronize()
     qpl.timing_enable(False)
     kern = qpl.timing_collect()
@@ -207,13 +214,15 @@ def main():
                 "frac_of_fp4_peak": round(achieved / PEAK_TFLOPS["fp4"], 4)}
     # the quantizers against HBM on their algorithmic bytes: fp8r 2 B in + 1 B out per
     # element (+ 4 B per row); nvfp4 2 B in + 0.5 B codes + 1/16 B scales per element
-    # (+ T out for the fused low-rank quantizer)
+    # (+ the weight's block scales read and written again in the GEMM's layout, which
+    # the linear quantizer's launch also does; + T out for the fused low-rank quantizer)
     def gbs(kind, nbytes):
         n, t = kern[kind]
         return round(nbytes / (t / n * 1e-3) / 1e9, 1) if n else None
     mk = lin["fp8r"]["M"] * lin["fp8r"]["K"]
     quant_gbs = {"quant_fp8_row": gbs("quant_fp8_row", 3.0 * mk + 4.0 * lin["fp8r"]["M"]),
-                 "quant_nvfp4_linear": gbs("quant_nvfp4_linear", 2.5625 * lin["nvfp4"]["M"] * lin["nvfp4"]["K"]),
+                 "quant_nvfp4_linear": gbs("quant_nvfp4_linear", 2.5625 * lin["nvfp4"]["M"] * lin["nvfp4"]["K"] +
+                                           2.0 * lin["nvfp4"]["N"] * lin["nvfp4"]["K"] / 16),
                  "quant_nvfp4_lowrank": gbs("quant_nvfp4_lowrank", 2.5625 * lin["svdq"]["M"] * lin["svdq"]["K"] +
                                             4.0 * lin["svdq"]["M"] * 32 * ((lin["svdq"]["R"] + 31) // 32))}
     # reference: a plain device copy of the same activation tensor (read once, written

@@ -345,15 +345,16 @@ float qpl_nvfp4_global_scale(float amax);
 typedef enum {
   QPL_KERNEL_QUANT_FP8_ROW = 0,     /* fp8r activation / weight quantize */
   QPL_KERNEL_QUANT_NVFP4 = 1,       /* nvfp4 quantize to packed codes */
-  QPL_KERNEL_QUANT_NVFP4_LINEAR = 2, /* nvfp4 quantize inside qlinear_nvfp4 (R = 0; slab-major scales) */
+  QPL_KERNEL_QUANT_NVFP4_LINEAR = 2, /* nvfp4 quantize inside qlinear_nvfp4 (R = 0; slab-major scales),
+                                        with the weight's block scales into the GEMM's layout */
   QPL_KERNEL_GEMM_FP8R = 3,
   QPL_KERNEL_GEMM_NVFP4 = 4,
   QPL_KERNEL_GEMM_NVFP4_LOWRANK = 5, /* nvfp4 GEMM with the low-rank epilogue */
   QPL_KERNEL_LOWRANK_PREP = 6,      /* low-rank factor transposes (qlinear_int4) */
   QPL_KERNEL_DEQUANT = 7,
   QPL_KERNEL_AMAX = 8,
-  QPL_KERNEL_NVFP4_PREP = 9,        /* qlinear_nvfp4's preparation: the weight's block scales into the
-                                       GEMM's layout and, with R > 0, the low-rank factor layouts */
+  QPL_KERNEL_NVFP4_PREP = 9,        /* qlinear_nvfp4's preparation when R > 0: the weight's block scales
+                                       into the GEMM's layout and the low-rank factor layouts */
   QPL_KERNEL_QUANT_NVFP4_LOWRANK = 10, /* nvfp4 quantize fused with x L1 (qlinear_nvfp4, R > 0) */
   QPL_KERNEL_QUANT_W4G = 11,        /* quant_weight_awq */
   QPL_KERNEL_GEMV_W4A16 = 12,       /* qlinear_awq_w4a16 */

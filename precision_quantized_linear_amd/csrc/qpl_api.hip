@@ -297,9 +297,11 @@ qpl_status check_nvfp4_layer(const uint8_t* weight, const uint8_t* weight_scale,
 }
 
 // The steps of an nvfp4 linear before its GEMM, in the workspace laid out by L at
-// base: one preparation launch (the weight's block scales into the GEMM's layout,
-// and the low-rank factor layouts when R > 0), then the activation quantize into
-// packed codes and slab-major block scales (fused with T = x L1 when R > 0).
+// base.  R = 0: one launch, the activation quantize into packed codes and
+// slab-major block scales, whose extra workgroups relay the weight's block scales
+// into the GEMM's layout.  R > 0: a preparation launch (that relay and the
+// low-rank factor layouts), then the activation quantize fused with T = x L1,
+// which reads L1 in the prepared layout.
 qpl_status nvfp4_operands(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight_scale,
                           float input_scale, const float* smooth, const uint16_t* lora_down, const uint16_t* lora_up,
                           int64_t R, const Layout& L, uint8_t* base, hipStream_t st, qpl::LowRank& lr) {
@@ -317,7 +319,7 @@ qpl_status nvfp4_operands(const uint16_t* x, int64_t M, int64_t K, int64_t N, co
     uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.off[4]);
     const qpl::LowRankPrep prep{lora_down, lora_up, K, N, R, kl / 2, kl, l1t, l2t};
     if ((s = launched(Timed(QPL_KERNEL_NVFP4_PREP, st)(
-             qpl::launch_nvfp4_prep(weight_scale, N, K, wsl, M, xs, &prep, st)))) != QPL_OK)
+             qpl::launch_nvfp4_prep(weight_scale, N, K, wsl, M, xs, prep, st)))) != QPL_OK)
       return s;
     lr.t = t;
     lr.l2t = l2t;
@@ -325,11 +327,8 @@ qpl_status nvfp4_operands(const uint16_t* x, int64_t M, int64_t K, int64_t N, co
     return launched(Timed(QPL_KERNEL_QUANT_NVFP4_LOWRANK, st)(
         qpl::launch_quant_nvfp4_lowrank(x, M, K, input_scale, smooth, l1t, kl, xq, xs, t, st)));
   }
-  if ((s = launched(Timed(QPL_KERNEL_NVFP4_PREP, st)(
-           qpl::launch_nvfp4_prep(weight_scale, N, K, wsl, M, xs, nullptr, st)))) != QPL_OK)
-    return s;
   return launched(Timed(QPL_KERNEL_QUANT_NVFP4_LINEAR, st)(
-      qpl::launch_quant_nvfp4_slab(x, M, K, input_scale, smooth, xq, xs, st)));
+      qpl::launch_quant_nvfp4_linear(x, M, K, input_scale, smooth, xq, xs, weight_scale, N, wsl, st)));
 }
 
 qpl_status nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, int64_t N, const uint8_t* weight,

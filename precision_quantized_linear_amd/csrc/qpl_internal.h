@@ -22,11 +22,13 @@ hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t
 // lam: SVDQuant smoothing factors [K] (x is divided by them first) or nullptr.
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
                               uint8_t* xbs, hipStream_t stream);
-// The nvfp4 quantizer of the linear layer: packed codes [M, K/2] (as quant_act_nvfp4)
-// and block scales slab-major [ceil(K/128), M, 8] (the GEMM's layout; bytes past
-// K/16 are written as zeros by launch_nvfp4_prep).
-hipError_t launch_quant_nvfp4_slab(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
-                                   uint8_t* xs, hipStream_t stream);
+// The nvfp4 quantizer of the linear layer without a low-rank branch: packed codes
+// [M, K/2] (as quant_act_nvfp4) and block scales slab-major [ceil(K/128), M, 8]
+// (the GEMM's layout, zeros past K/16), and in the same launch the weight's block
+// scales wbs [N, K/16] relaid into wsl [ceil(K/128), N, 8] (zeros past K/16).
+hipError_t launch_quant_nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                     uint8_t* xq, uint8_t* xs, const uint8_t* wbs, int64_t N, uint8_t* wsl,
+                                     hipStream_t stream);
 // The same, fused with the low-rank down-projection: t [M, kl] bf16 receives
 // T = x L1 (fp32) as [hi | lo] bf16 halves of kl / 2 columns each; l1t [kl / 2, K]
 // is L1 transposed (zero past R); kl / 2 is a multiple of 32, at most 128.  With
@@ -67,13 +69,13 @@ struct LowRankPrep {
 };
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, int64_t N, int64_t K,
                                 uint16_t* out, hipStream_t stream);
-// What an nvfp4 linear prepares before its quantizer, in one launch: the weight
-// block scales [N, K/16] copied into the GEMM's slab-major layout wsl
-// [ceil(K/128), N, 8] (zero past K/16), zeros over the activation scales' last
-// slab xs [ceil(K/128) - 1, M, 8] when K/16 is not a multiple of 8, and (lr) the
-// factor layouts of the low-rank branch.
+// What an nvfp4 linear with a low-rank branch prepares before its quantizer, in
+// one launch: the weight block scales [N, K/16] copied into the GEMM's slab-major
+// layout wsl [ceil(K/128), N, 8] (zero past K/16), zeros over the bytes past K/16
+// of the activation scales' last slab xs [ceil(K/128) - 1, M, 8], and the factor
+// layouts of the low-rank branch.
 hipError_t launch_nvfp4_prep(const uint8_t* wbs, int64_t N, int64_t K, uint8_t* wsl, int64_t M, uint8_t* xs,
-                             const LowRankPrep* lr, hipStream_t stream);
+                             const LowRankPrep& lr, hipStream_t stream);
 
 // What a GEMM's epilogue writes (default: y = bf16 result, row-major [M, N]).
 // gelu: the tanh form of GELU on the fp32 result before the bf16 rounding.

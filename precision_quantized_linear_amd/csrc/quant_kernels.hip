@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void k_quant_fp8_row(const uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int64_t j = lane + 64 * i;
-      if (j < nv) qr[j] = fp8_vec(v[i], d);
+      if (j < nv) __builtin_nontemporal_store(fp8_vec(v[i], d), qr + j);
     }
   } else {
     for (int64_t j = lane; j < nv; j += 64) am = vec_absmax(xr[j], am);
@@ -124,6 +124,21 @@ hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t M, int64_t K, uint8_t
 // codes and one scale byte out).  Blocks never straddle rows (K % 16 == 0), so
 // the tensor is processed as a flat array of blocks.
 // ---------------------------------------------------------------------------
+
+// nvfp4_scale with d = dec(sf) g and RN(1 / d) formed in place, as the host forms
+// its table (one fp32 product, one correctly rounded division; code 0x7F, which
+// only a NaN block maximum reaches, gives d = 0), for kernels that do not stage
+// the table in LDS.
+__device__ __forceinline__ Nvfp4Block nvfp4_scale_g(float bmax, float c6g, float rc6g, float g) {
+  const float u = div_rn_ok(c6g) ? div_rn(bmax, c6g, rc6g) : bmax / c6g;
+  Nvfp4Block b;
+  b.sf = e4m3_pack2(u, 0.0f) & 0xFFu;
+  b.dsf = e4m3_decode(b.sf);
+  b.d = b.sf == 0x7Fu ? 0.0f : b.dsf * g;
+  b.rd = 1.0f / b.d;
+  b.fast = div_rn_ok(b.d) && bmax * b.rd < 0x1p126f;
+  return b;
+}
 
 // Copy the per-code table from the kernel arguments into LDS (whole workgroup).
 __device__ __forceinline__ void load_scale_table(const Nvfp4ScaleTable& t, float* tab_d, float* tab_rd) {
@@ -158,22 +173,87 @@ __device__ __forceinline__ void smooth_block(uint32_t (&p)[8], const float* __re
 }
 
 
+// The scale work that every nvfp4 linear does before its GEMM, in whole workgroups
+// (256 threads) numbered blk < wblocks + xblocks:
+// * blk < wblocks: the weight's block scales [N, kb] (kb = K/16) into the GEMM's
+//   slab-major layout [S, N, 8] (S = ceil(kb/8)), zeros past kb: one thread per
+//   8-byte unit, slab index fastest so that a wavefront reads consecutive bytes;
+// * the rest (only when kb % 8 != 0): zeros over the bytes past kb of every
+//   activation row's last slab [S - 1, M, 8], so that the GEMM multiplies the codes
+//   it reads as zeros there by a finite scale.  Only the pad bytes are written: the
+//   quantizer may be writing the real blocks' bytes of the same slab at the same time.
+struct Nvfp4Prep {
+  const uint8_t* wbs;
+  uint8_t* wsl;
+  uint8_t* xs;
+  int64_t N, M, kb, S;
+  unsigned wblocks, xblocks;
+};
+
+__device__ __forceinline__ void nvfp4_prep_block(const Nvfp4Prep& a, unsigned blk) {
+  if (blk < a.wblocks) {
+    const int64_t u = (int64_t)blk * 256 + threadIdx.x;
+    if (u >= a.N * a.S) return;
+    const int64_t n = u / a.S, sl = u - n * a.S;
+    const uint8_t* src = a.wbs + n * a.kb + 8 * sl;
+    const int64_t left = a.kb - 8 * sl;  // >= 1
+    u32x2 v;
+    if (left >= 8 && (reinterpret_cast<uintptr_t>(src) & 7u) == 0) {
+      v = *reinterpret_cast<const u32x2*>(src);  // a whole, aligned group of eight scales
+    } else {
+      v = u32x2{0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < left) v.x |= (uint32_t)src[i] << (8 * i);
+        if (i + 4 < left) v.y |= (uint32_t)src[i + 4] << (8 * i);
+      }
+    }
+    *reinterpret_cast<u32x2*>(a.wsl + (sl * a.N + n) * 8) = v;
+  } else {
+    const int64_t m = (int64_t)(blk - a.wblocks) * 256 + threadIdx.x;
+    if (m >= a.M) return;
+    uint8_t* row = a.xs + ((a.S - 1) * a.M + m) * 8;
+    for (int j = (int)(a.kb & 7); j < 8; ++j) row[j] = 0;
+  }
+}
+
+Nvfp4Prep nvfp4_prep_args(const uint8_t* wbs, int64_t N, int64_t K, uint8_t* wsl, int64_t M, uint8_t* xs) {
+  Nvfp4Prep a;
+  a.wbs = wbs;
+  a.wsl = wsl;
+  a.xs = xs;
+  a.N = N;
+  a.M = M;
+  a.kb = K / 16;
+  a.S = (a.kb + 7) / 8;
+  a.wblocks = (unsigned)((N * a.S + 255) / 256);
+  a.xblocks = a.kb % 8 != 0 ? (unsigned)((M + 255) / 256) : 0u;
+  return a;
+}
+
 // SMOOTH: the block is first smoothed by lam (kb = K / 16 blocks per row).  SLAB:
 // the scales go slab-major [ceil(K/128), rows, 8] (the GEMM's operand layout;
 // byte 8 s + i of a row's scales is block 8 s + i) instead of row-major [rows, kb].
+// Each lane forms its block's d and RN(1 / d) from g itself: a division per block
+// costs less than staging the 128-entry table per workgroup.  Workgroups past the
+// qblocks that quantize do the linear's scale preparation (nvfp4_prep_block), so
+// that it needs no launch of its own.
 template <bool SMOOTH, bool SLAB>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict__ x, int64_t nblocks,
-                                                     float c6g, float rc6g, Nvfp4ScaleTable tab,
+                                                     float c6g, float rc6g, float g,
                                                      const float* __restrict__ lam, int64_t kb, int64_t rows,
-                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xbs) {
-  __shared__ float tab_d[128], tab_rd[128];
-  load_scale_table(tab, tab_d, tab_rd);
+                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xbs,
+                                                     unsigned qblocks, Nvfp4Prep prep) {
+  if (blockIdx.x >= qblocks) {
+    nvfp4_prep_block(prep, blockIdx.x - qblocks);
+    return;
+  }
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   uint32_t p[8];
   load_block(x, b, p);
   smooth_block<SMOOTH>(p, lam, b, kb);
-  const Nvfp4Block s = nvfp4_scale(block_absmax(p, 8), c6g, rc6g, tab_d, tab_rd);
+  const Nvfp4Block s = nvfp4_scale_g(block_absmax(p, 8), c6g, rc6g, g);
   reinterpret_cast<u32x2*>(xq)[b] = u32x2{nvfp4_word<true>(p, s), nvfp4_word<true>(p + 4, s)};
   if constexpr (SLAB) {
     const int64_t row = b / kb, j = b - row * kb;
@@ -600,27 +680,31 @@ Nvfp4ScaleTable nvfp4_scale_table(float g) {
 
 template <bool SLAB>
 static hipError_t launch_nvfp4_blocks(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
-                                      uint8_t* xbs, hipStream_t stream) {
+                                      uint8_t* xbs, const Nvfp4Prep& prep, hipStream_t stream) {
   const int64_t nb = M * (K / 16);
   const float c6g = 6.0f * g, rc6g = 1.0f / c6g;
-  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  const unsigned qblocks = (unsigned)((nb + 255) / 256);
+  const dim3 grid(qblocks + prep.wblocks + prep.xblocks), block(256);
   if (lam)
-    hipLaunchKernelGGL((k_quant_nvfp4<true, SLAB>), grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
-                       lam, K / 16, M, xq, xbs);
+    hipLaunchKernelGGL((k_quant_nvfp4<true, SLAB>), grid, block, 0, stream, x, nb, c6g, rc6g, g, lam, K / 16, M,
+                       xq, xbs, qblocks, prep);
   else
-    hipLaunchKernelGGL((k_quant_nvfp4<false, SLAB>), grid, block, 0, stream, x, nb, c6g, rc6g, nvfp4_scale_table(g),
-                       lam, K / 16, M, xq, xbs);
+    hipLaunchKernelGGL((k_quant_nvfp4<false, SLAB>), grid, block, 0, stream, x, nb, c6g, rc6g, g, lam, K / 16, M,
+                       xq, xbs, qblocks, prep);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
                               uint8_t* xbs, hipStream_t stream) {
-  return launch_nvfp4_blocks<false>(x, M, K, g, lam, xq, xbs, stream);
+  Nvfp4Prep none{};
+  none.wblocks = none.xblocks = 0u;
+  return launch_nvfp4_blocks<false>(x, M, K, g, lam, xq, xbs, none, stream);
 }
 
-hipError_t launch_quant_nvfp4_slab(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam, uint8_t* xq,
-                                   uint8_t* xs, hipStream_t stream) {
-  return launch_nvfp4_blocks<true>(x, M, K, g, lam, xq, xs, stream);
+hipError_t launch_quant_nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, float g, const float* lam,
+                                     uint8_t* xq, uint8_t* xs, const uint8_t* wbs, int64_t N, uint8_t* wsl,
+                                     hipStream_t stream) {
+  return launch_nvfp4_blocks<true>(x, M, K, g, lam, xq, xs, nvfp4_prep_args(wbs, N, K, wsl, M, xs), stream);
 }
 
 template <int NCT, bool SMOOTH, bool INT4>
@@ -802,43 +886,14 @@ __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t* __restrict
   }
 }
 
-// Preparation of an nvfp4 linear (one launch, three kinds of workgroup):
-// * the weight's block scales [N, kb] (kb = K/16) into the GEMM's slab-major layout
-//   [S, N, 8] (S = ceil(kb/8)), zeros past kb: one thread per 8-byte unit, slab
-//   index fastest so that a wavefront reads consecutive bytes of a row;
-// * zeros over the activation scales' last slab [S - 1, M, 8] when kb % 8 != 0 (the
-//   quantizer then writes the bytes of the real blocks);
-// * with a low-rank branch, its factor layouts (lowrank_layout).
-struct Nvfp4Prep {
-  const uint8_t* wbs;
-  uint8_t* wsl;
-  uint8_t* xs;
-  int64_t N, M, kb, S;
-  unsigned wblocks, xblocks;
-};
-
-template <bool LR>
+// Preparation of an nvfp4 linear with a low-rank branch (one launch): the scale
+// work of nvfp4_prep_block, then the branch's factor layouts (lowrank_layout).
 __global__ __launch_bounds__(256) void k_nvfp4_prep(Nvfp4Prep a, LowRankPrep q) {
   const unsigned blk = blockIdx.x;
-  if (blk < a.wblocks) {
-    const int64_t u = (int64_t)blk * 256 + threadIdx.x;
-    if (u >= a.N * a.S) return;
-    const int64_t n = u / a.S, sl = u - n * a.S;
-    const uint8_t* src = a.wbs + n * a.kb + 8 * sl;
-    const int64_t left = a.kb - 8 * sl;  // >= 1
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i < left) lo |= (uint32_t)src[i] << (8 * i);
-      if (i + 4 < left) hi |= (uint32_t)src[i + 4] << (8 * i);
-    }
-    *reinterpret_cast<u32x2*>(a.wsl + (sl * a.N + n) * 8) = u32x2{lo, hi};
-  } else if (blk < a.wblocks + a.xblocks) {
-    const int64_t m = (int64_t)(blk - a.wblocks) * 256 + threadIdx.x;
-    if (m < a.M) *reinterpret_cast<u32x2*>(a.xs + ((a.S - 1) * a.M + m) * 8) = u32x2{0u, 0u};
-  } else if constexpr (LR) {
+  if (blk < a.wblocks + a.xblocks)
+    nvfp4_prep_block(a, blk);
+  else
     lowrank_layout(q, (int64_t)(blk - a.wblocks - a.xblocks) * 256 + threadIdx.x);
-  }
 }
 
 static unsigned lowrank_blocks(const LowRankPrep& q) {
@@ -869,24 +924,10 @@ hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* wbs, float g2, 
 }
 
 hipError_t launch_nvfp4_prep(const uint8_t* wbs, int64_t N, int64_t K, uint8_t* wsl, int64_t M, uint8_t* xs,
-                             const LowRankPrep* lr, hipStream_t stream) {
-  Nvfp4Prep a;
-  a.wbs = wbs;
-  a.wsl = wsl;
-  a.xs = xs;
-  a.N = N;
-  a.M = M;
-  a.kb = K / 16;
-  a.S = (a.kb + 7) / 8;
-  a.wblocks = (unsigned)((N * a.S + 255) / 256);
-  a.xblocks = a.kb % 8 != 0 ? (unsigned)((M + 255) / 256) : 0u;
-  const LowRankPrep q = lr ? *lr : LowRankPrep{};
-  const unsigned nlr = lr ? lowrank_blocks(q) : 0u;
-  const dim3 grid(a.wblocks + a.xblocks + nlr), block(256);
-  if (lr)
-    hipLaunchKernelGGL(k_nvfp4_prep<true>, grid, block, 0, stream, a, q);
-  else
-    hipLaunchKernelGGL(k_nvfp4_prep<false>, grid, block, 0, stream, a, q);
+                             const LowRankPrep& lr, hipStream_t stream) {
+  const Nvfp4Prep a = nvfp4_prep_args(wbs, N, K, wsl, M, xs);
+  const dim3 grid(a.wblocks + a.xblocks + lowrank_blocks(lr)), block(256);
+  hipLaunchKernelGGL(k_nvfp4_prep, grid, block, 0, stream, a, lr);
   return hipGetLastError();
 }
 

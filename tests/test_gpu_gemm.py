@@ -304,6 +304,31 @@ def test_qlinear_deterministic():
     assert np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("name,M,K,N", [("nvfp4_dit", 300, 400, 520), ("svdq_w4a4", 37, 272, 72),
+                                         ("nvfp4_dit", 1, 16, 1)])
+def test_qlinear_nvfp4_workspace_contents_ignored(name, M, K, N):
+    # K / 16 not a multiple of 8: the GEMM reads scale bytes past K / 16 in the last
+    # slab of both operands' scale layouts, which the library writes as zeros.  A
+    # workspace full of 0xFF (NaN as E4M3) and one full of zeros must give the same
+    # bits, with and without the low-rank branch.
+    d = make(name, M=M, K=K, N=N)
+    R = d.get("R", 0)
+    g_w = global_scale(amax_bf16(d["w"]))
+    wp, wb = quant_nvfp4(d["w"], g_w)
+    args = (to_dev_bf16(d["x"]), to_dev(wp), to_dev(wb), g_w, 0.01)
+    kw = dict(lora_down=to_dev_bf16(d["l1"]), lora_up=to_dev_bf16(d["l2"])) if R else {}
+    need = qpl.qlinear_workspace_bytes(qpl.QPL_NVFP4, d["M"], K, N, R)
+    say("workspace contents", name, d["M"], K, N, "R", R)
+    out = []
+    for fill in (0xFF, 0x00):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        y = qpl.qlinear_nvfp4(*args, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        out.append(bf16_bits(y))
+    assert np.isfinite(bf16_bits_to_f32(out[0])).all()
+    assert np.array_equal(out[0], out[1])
+
+
 def test_fp8_dot_floor_random_codes():
     # Activations and weights are exact E4M3 values spread over the whole exponent
     # range, with row amax 448 (so the row scale is 1 and the kernel's codes are the
