@@ -269,20 +269,29 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict_
 // Diffusion Inference to Diffusers", section "Background: SVDQuant and
 // Nunchaku").  The branch takes the unquantized x.
 //
-// A workgroup (eight wavefronts) owns rpw <= 32 consecutive rows, rpw chosen so that
+// A workgroup (sixteen wavefronts) owns rpw <= 32 consecutive rows, rpw chosen so that
 // there is about one workgroup per CU, and walks K in tiles of TK columns.  Each tile of x
 // (32 x TK bf16) and of L1^T (rpad x TK) moves global -> LDS without register
 // staging, S - 1 tiles ahead; a load instruction covers whole 512- or 256-byte row
-// segments, so HBM sees full lines.  Per tile, the wavefronts
-//   1. quantize their eighth of the x tile from LDS (lane l holds eight values,
-//      lanes l and l ^ 1 one 16-element block) and store the packed codes (4 bytes
-//      per lane) and, from the block's first lane, its scale byte in the GEMM's
-//      slab-major layout [K/128][M][8];
-//   2. run the bf16 MFMA 32x32x16 over their eighth of the tile's k range,
-//      reading both operands from LDS, into per-wave partial sums of T.
-// Two wavefronts per SIMD keep the quantizer's arithmetic busy.  The eight partial
-// sums meet in LDS at the end, in a fixed order; T is stored as [hi | lo] bf16
-// halves (row stride kl = 2 rpad) for the GEMM's low-rank pass.
+// segments, so HBM sees full lines.  The sixteen wavefronts split the work by kind:
+// wavefronts 0-3 issue every tile load and run the MFMAs, wavefronts 4-15
+// quantize (wavefront i usually runs on SIMD i mod 4, so that each SIMD holds one
+// loading and three quantizing wavefronts, and a tile's x slots, dealt out in
+// turn, spread evenly over the SIMDs with at most one per wavefront for up to 24
+// rows).
+// A load instruction waits at issue while the memory pipeline is full; with the
+// loads in wavefronts of their own, that wait overlaps the quantizer's arithmetic
+// instead of adding to it.  Per tile,
+//   1. quantizing wavefront 4 + q takes the x tile's 1 KB slots q, q + 12, ...
+//      (lane l holds eight values, lanes l and l ^ 1 one 16-element block) and
+//      store the packed codes (4 bytes per lane) and, from the block's first lane,
+//      its scale byte in the GEMM's slab-major layout [K/128][M][8], while the
+//      loading wavefronts issue the loads of tile kt + S - 1;
+//   2. the loading wavefronts run the bf16 MFMA 32x32x16 over their quarter of the
+//      tile's k range, reading both operands from LDS, into per-wave partial sums
+//      of T, while the quantizing ones work.
+// The four partial sums meet in LDS at the end, in a fixed order; T is stored as
+// [hi | lo] bf16 halves (row stride kl = 2 rpad) for the GEMM's low-rank pass.
 //
 // LDS layout: 16-byte chunk c of tile row r sits at chunk slot c ^ (r & 15) of
 // the row, so the MFMA operand reads (16 rows, one chunk) hit 16 different bank
@@ -290,8 +299,8 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict_
 // holds.
 //
 // SMOOTH (SVDQuant smoothing): each stage also holds the tile's TK smoothing
-// factors (one dword load per wavefront: wave w moves factors 64 w .. 64 w + 63,
-// zeros past TK or K).  Step 1 divides its values by them, quantizes the smoothed
+// factors (one dword load per loading wavefront: wave w moves factors
+// 64 w .. 64 w + 63, zeros past TK or K).  Step 1 divides its values by them, quantizes the smoothed
 // bf16 values and writes them back over the tile, and step 2 waits for every
 // wave's write-back, so that both branches read the same smoothed activation.
 //
@@ -307,28 +316,31 @@ struct LrTile {
   static constexpr int CPR = TK / 8;                // 16-byte chunks per tile row
   static constexpr int XB = 32 * TK * 2;            // x tile bytes
   static constexpr int LB = 32 * NCT * TK * 2;      // L1^T tile bytes
-  static constexpr int FB = SMOOTH ? 8 * 256 : 0;  // smoothing factor bytes (one 256-byte slot per wave)
+  static constexpr int FB = SMOOTH ? 4 * 256 : 0;  // smoothing factor bytes (one 256-byte slot per loading wave)
   static constexpr int SB = XB + LB + FB;           // stage bytes
   static constexpr int S = (NCT == 1 || NCT == 3) ? 4 : 3;  // stages in the ring (<= 128 KB, 144 KB for NCT 2)
-  static constexpr int NW = 8;                      // wavefronts
-  static constexpr int XI = XB / 1024 / NW;         // x loads (and xe stores) per wave per tile, 1 KB each
-  static constexpr int LI = LB / 1024 / NW;         // L1^T loads per wave per tile
-  static constexpr int DW = XI + LI + (SMOOTH ? 1 : 0);  // loads per wave per tile
-  static constexpr int SPT = 2 * XI;                      // stores per wave per tile (codes, scales)
+  static constexpr int NW = 16;                     // wavefronts: 0-3 load, 4-15 quantize
+  static constexpr int NQ = 12;                     // quantizing wavefronts
+  static constexpr int NM = 4;                      // multiplying wavefronts (the loading ones)
+  static constexpr int NSX = XB / 1024;             // 1 KB slots of the x tile
+  static constexpr int NSL = LB / 1024;             // 1 KB slots of the L1^T tile
+  static constexpr int DW = (NSX + NSL) / 4 + (SMOOTH ? 1 : 0);  // loads per loading wave per tile
+  static constexpr int QS = (NSX + NQ - 1) / NQ;    // x slots per quantizing wave per tile (at most)
+  static_assert(NSL % 4 == 0 && NSX % 4 == 0 && 64 * 4 >= TK && (TK / 16) % NM == 0, "even splits");
 };
 
 // xq: the packed E2M1 codes [M, K/2] (nvfp4) or the E4M3 code bytes [M, K] (INT4);
 // xs: the nvfp4 block scales slab-major [ceil(K/128), M, 8] (bytes) or the INT4
 // group scales group-major [K/64, M] (floats).
 template <int NCT, bool SMOOTH, bool INT4>
-__global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+__global__ __launch_bounds__(1024) void k_quant_act_lowrank(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                            float c6g, float rc6g, Nvfp4ScaleTable tab,
                                                            const uint16_t* __restrict__ l1t, int64_t kl,
                                                            const float* __restrict__ lam, int rpw,
                                                            uint8_t* __restrict__ xq, void* __restrict__ xs,
                                                            uint16_t* __restrict__ t_out) {
   using C = LrTile<NCT, SMOOTH, INT4>;
-  constexpr int TK = C::TK, CPR = C::CPR, S = C::S, XI = C::XI, LI = C::LI, NW = C::NW;
+  constexpr int TK = C::TK, CPR = C::CPR, S = C::S, NW = C::NW;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S * C::SB];
   __shared__ float tab_d[128], tab_rd[128];
   load_scale_table(tab, tab_d, tab_rd);
@@ -352,26 +364,32 @@ __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __res
   const uint32_t lbase = lds_address(lds);
   const int ntiles = (int)((K + TK - 1) / TK);
 
-  // Geometry of this lane's slot in load instruction j of the wave (the same for
-  // every tile): tile row, chunk held, byte offset within the tile.
-  auto slot_row = [&](int j, int per) { return ((wv * per + j) * 64 + lane) / CPR; };
-  auto slot_chunk = [&](int j, int per) {
-    const int sl = (wv * per + j) * 64 + lane;
-    return (sl % CPR) ^ ((sl / CPR) & 15);
+  // Geometry of this lane's part of 1 KB slot sl of a tile (the same for every
+  // tile): tile row and chunk held.
+  auto slot_row = [&](int sl) { return (sl * 64 + lane) / CPR; };
+  auto slot_chunk = [&](int sl) {
+    const int sv = sl * 64 + lane;
+    return (sv % CPR) ^ ((sv / CPR) & 15);
   };
   // Offsets valid for tile kt: chunks past K read zero (rows past M do through dx).
   auto voff = [&](int r, int c, int kt) -> uint32_t {
     return (int64_t)kt * TK + 8 * c < K ? (uint32_t)r * pitch + 16u * (uint32_t)c : kOutOfRange;
   };
+  const bool loader = wv < 4;
+  // The loads of tile kt (loading wavefronts): slots wv, wv + 4, ... of both tiles.
   auto issue = [&](int kt) {
     const uint32_t st = lbase + (uint32_t)((kt % S) * C::SB);
     const int soff = kt * TK * 2;
 #pragma unroll
-    for (int j = 0; j < XI; ++j)
-      dma16(st + (uint32_t)((wv * XI + j) * 1024), voff(slot_row(j, XI), slot_chunk(j, XI), kt), dx, soff);
+    for (int j = 0; j < C::NSX / 4; ++j) {
+      const int sl = 4 * j + wv;
+      dma16(st + (uint32_t)(sl * 1024), voff(slot_row(sl), slot_chunk(sl), kt), dx, soff);
+    }
 #pragma unroll
-    for (int j = 0; j < LI; ++j)
-      dma16(st + C::XB + (uint32_t)((wv * LI + j) * 1024), voff(slot_row(j, LI), slot_chunk(j, LI), kt), dl, soff);
+    for (int j = 0; j < C::NSL / 4; ++j) {
+      const int sl = 4 * j + wv;
+      dma16(st + C::XB + (uint32_t)(sl * 1024), voff(slot_row(sl), slot_chunk(sl), kt), dl, soff);
+    }
     if constexpr (SMOOTH) {
       const int64_t k = (int64_t)kt * TK + wv * 64 + lane;
       dma4(st + C::XB + C::LB + (uint32_t)(wv * 256),
@@ -383,98 +401,90 @@ __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __res
 #pragma unroll
   for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
 
+  if (loader) {
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t);
+    for (int t = 0; t < S - 1; ++t) issue(t);
+  }
   for (int kt = 0; kt < ntiles; ++kt) {
-    // tile kt has landed: loads and stores retire in order, and the ones issued
-    // after tile kt's loads are the later tiles' loads and this wave's stores
-    const int after = kt < S - 1 ? kt : S - 1;
-    switch (after) {
-      case 0: QPL_WAIT_VMCNT((S - 2) * C::DW); break;
-      case 1: QPL_WAIT_VMCNT((S - 2) * C::DW + C::SPT); break;
-      case 2: QPL_WAIT_VMCNT((S - 2) * C::DW + 2 * C::SPT); break;
-      default: QPL_WAIT_VMCNT((S - 2) * C::DW + 3 * C::SPT); break;
-    }
+    // tile kt has landed: a loading wave's loads retire in order, and the ones it
+    // issued after tile kt's are those of tiles kt + 1 .. kt + S - 2 (the
+    // quantizing waves issue only stores, and never wait on them here)
+    if (loader) QPL_WAIT_VMCNT((S - 2) * C::DW);
     QPL_WAIT_LGKM0();
-    __builtin_amdgcn_s_barrier();  // every wave's part of tile kt is in LDS; tile kt - 1's buffer is free
-    issue(kt + S - 1);             // past the end: out-of-range offsets, zeros into an unused buffer
+    __builtin_amdgcn_s_barrier();  // every part of tile kt is in LDS; tile kt - 1's buffer is free
     uint8_t* xt = lds + (kt % S) * C::SB;
     const uint8_t* lt = xt + C::XB;
 
-    // 1. quantize and expand this wave's part of the x tile
+    if (loader) {
+      issue(kt + S - 1);  // past the end: out-of-range offsets, zeros into an unused buffer
+    } else {
+      // 1. quantize and store this wave's slots of the x tile
 #pragma unroll
-    for (int j = 0; j < XI; ++j) {
-      const int r = slot_row(j, XI), c = slot_chunk(j, XI);
-      if ((wv * XI + j) * 64 / CPR >= rows) {
-        // rows past the workgroup's: no work, but the stores are still issued (and
-        // dropped) so that every wave retires the same number of operations
-        if constexpr (INT4) {
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, re, (int)kOutOfRange, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(0u, rsc, (int)kOutOfRange, 0, 0);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b32(0u, re, (int)kOutOfRange, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, rsc, (int)kOutOfRange, 0, 0);
-        }
-        continue;
-      }
-      u32x4* slot = reinterpret_cast<u32x4*>(xt + ((wv * XI + j) * 64 + lane) * 16);
-      const u32x4 v = *slot;
-      uint32_t p[4] = {v.x, v.y, v.z, v.w};
-      if constexpr (SMOOTH) {
-        if ((int64_t)kt * TK + 8 * c < K) {  // chunks past K hold zeros and no factors
-          const f32x4* f = reinterpret_cast<const f32x4*>(xt + C::XB + C::LB + 32 * c);
-          const f32x4 f0 = f[0], f1 = f[1];
-          p[0] = smooth_pair(p[0], f0[0], f0[1]);
-          p[1] = smooth_pair(p[1], f0[2], f0[3]);
-          p[2] = smooth_pair(p[2], f1[0], f1[1]);
-          p[3] = smooth_pair(p[3], f1[2], f1[3]);
-          *slot = u32x4{p[0], p[1], p[2], p[3]};
-        }
-      }
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = absmax_acc(m, p[i]);
-      // the other half of the block is in lane l ^ 1 (chunk c ^ 1 of the same row)
-      m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
-      if constexpr (INT4) {
-        // the rest of the 64-channel group: lanes l ^ 2 (quad_perm 2,3,0,1), then the
-        // other quad of the 8-lane block (row_half_mirror)
-        m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
-        m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
-        const float s = absmax_value(m) / 7.0f;
-        uint32_t w0 = 0, w1 = 0;
-        if (s > 0.0f) {
-          const bool ok = div_rn_ok(s);
-          const float rs = 1.0f / s;
-          float q[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = bf16_lo(p[i]), b = bf16_hi(p[i]);
-            q[2 * i] = __builtin_amdgcn_fmed3f(__builtin_rintf(ok ? div_rn_finite(a, s, rs) : a / s), -8.0f, 7.0f);
-            q[2 * i + 1] = __builtin_amdgcn_fmed3f(__builtin_rintf(ok ? div_rn_finite(b, s, rs) : b / s), -8.0f, 7.0f);
+      for (int j = 0; j < C::QS; ++j) {
+        const int sl = C::NQ * j + (wv - 4);
+        if (sl >= C::NSX || sl * 64 / CPR >= rows) continue;  // past the tile or the workgroup's rows (uniform)
+        const int r = slot_row(sl), c = slot_chunk(sl);
+        u32x4* slot = reinterpret_cast<u32x4*>(xt + (sl * 64 + lane) * 16);
+        const u32x4 v = *slot;
+        uint32_t p[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (SMOOTH) {
+          if ((int64_t)kt * TK + 8 * c < K) {  // chunks past K hold zeros and no factors
+            const f32x4* f = reinterpret_cast<const f32x4*>(xt + C::XB + C::LB + 32 * c);
+            const f32x4 f0 = f[0], f1 = f[1];
+            p[0] = smooth_pair(p[0], f0[0], f0[1]);
+            p[1] = smooth_pair(p[1], f0[2], f0[3]);
+            p[2] = smooth_pair(p[2], f1[0], f1[1]);
+            p[3] = smooth_pair(p[3], f1[2], f1[3]);
+            *slot = u32x4{p[0], p[1], p[2], p[3]};
           }
-          w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-          w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)w0, true);
-          w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-          w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)w1, true);
         }
-        const int64_t k0 = (int64_t)kt * TK + 8 * c;
-        const bool in_k = k0 < K;
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, re, in_k ? (int)(r * K + k0) : (int)kOutOfRange, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __float_as_uint(s), rsc,
-            in_k && (c & 7) == 0 && r < rows ? (int)(((k0 / 64) * M + m0 + r) * 4) : (int)kOutOfRange, 0, 0);
-      } else {
-        const Nvfp4Block sc = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
-        const int64_t k0 = (int64_t)kt * TK + 8 * c;
-        const bool in_k = k0 < K;
-        __builtin_amdgcn_raw_buffer_store_b32(nvfp4_word<true>(p, sc), re,
-                                              in_k ? (int)(r * qpitch + k0 / 2) : (int)kOutOfRange, 0, 0);
-        // the block's scale, from the lane holding its first half (even chunk)
-        const int64_t jb = k0 / 16;
-        __builtin_amdgcn_raw_buffer_store_b8(
-            (uint8_t)sc.sf, rsc,
-            in_k && (c & 1) == 0 && r < rows ? (int)(((jb >> 3) * M + m0 + r) * 8 + (jb & 7)) : (int)kOutOfRange, 0, 0);
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = absmax_acc(m, p[i]);
+        // the other half of the block is in lane l ^ 1 (chunk c ^ 1 of the same row)
+        m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+        if constexpr (INT4) {
+          // the rest of the 64-channel group: lanes l ^ 2 (quad_perm 2,3,0,1), then the
+          // other quad of the 8-lane block (row_half_mirror)
+          m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+          m = absmax_acc(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+          const float s = absmax_value(m) / 7.0f;
+          uint32_t w0 = 0, w1 = 0;
+          if (s > 0.0f) {
+            const bool ok = div_rn_ok(s);
+            const float rs = 1.0f / s;
+            float q[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float a = bf16_lo(p[i]), b = bf16_hi(p[i]);
+              q[2 * i] = __builtin_amdgcn_fmed3f(__builtin_rintf(ok ? div_rn_finite(a, s, rs) : a / s), -8.0f, 7.0f);
+              q[2 * i + 1] =
+                  __builtin_amdgcn_fmed3f(__builtin_rintf(ok ? div_rn_finite(b, s, rs) : b / s), -8.0f, 7.0f);
+            }
+            w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+            w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)w0, true);
+            w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+            w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)w1, true);
+          }
+          const int64_t k0 = (int64_t)kt * TK + 8 * c;
+          const bool in_k = k0 < K;
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, re, in_k ? (int)(r * K + k0) : (int)kOutOfRange, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __float_as_uint(s), rsc,
+              in_k && (c & 7) == 0 && r < rows ? (int)(((k0 / 64) * M + m0 + r) * 4) : (int)kOutOfRange, 0, 0);
+        } else {
+          const Nvfp4Block sc = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
+          const int64_t k0 = (int64_t)kt * TK + 8 * c;
+          const bool in_k = k0 < K;
+          __builtin_amdgcn_raw_buffer_store_b32(nvfp4_word<true>(p, sc), re,
+                                                in_k ? (int)(r * qpitch + k0 / 2) : (int)kOutOfRange, 0, 0);
+          // the block's scale, from the lane holding its first half (even chunk)
+          const int64_t jb = k0 / 16;
+          __builtin_amdgcn_raw_buffer_store_b8(
+              (uint8_t)sc.sf, rsc,
+              in_k && (c & 1) == 0 && r < rows ? (int)(((jb >> 3) * M + m0 + r) * 8 + (jb & 7)) : (int)kOutOfRange, 0,
+              0);
+        }
       }
     }
 
@@ -483,42 +493,34 @@ __global__ __launch_bounds__(512) void k_quant_act_lowrank(const uint16_t* __res
       __builtin_amdgcn_s_barrier();  // every wave's smoothed values are in the tile
     }
 
-    // 2. T += x_tile L1t_tile^T over this wave's part of the k range
+    // 2. T += x_tile L1t_tile^T over this wave's quarter of the k range (loading waves)
+    if (loader) {
 #pragma unroll
-    for (int ks = 0; ks < TK / 16 / NW; ++ks) {
-      const int ch = wv * (CPR / NW) + 2 * ks + (lane >> 5);  // chunk of the 32x32x16 operand
-      const int r = lane & 31;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(xt + (r * CPR + (ch ^ (r & 15))) * 16);
+      for (int ks = 0; ks < TK / 16 / C::NM; ++ks) {
+        const int ch = wv * (CPR / C::NM) + 2 * ks + (lane >> 5);  // chunk of the 32x32x16 operand
+        const int r = lane & 31;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(xt + (r * CPR + (ch ^ (r & 15))) * 16);
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        const int rb = 32 * c + r;
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(lt + (rb * CPR + (ch ^ (rb & 15))) * 16);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+        for (int c = 0; c < NCT; ++c) {
+          const int rb = 32 * c + r;
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(lt + (rb * CPR + (ch ^ (rb & 15))) * 16);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+        }
       }
     }
   }
   QPL_WAIT_VMCNT(0);
   __syncthreads();
 
-  // partial sums of the eight waves -> T: p_w = acc_w + acc_(w+4), then ((p0 + p1) + p2) + p3
+  // partial sums of the four multiplying waves -> T = ((p0 + p1) + p2) + p3
   f32x4* red = reinterpret_cast<f32x4*>(lds);  // [4][c][4][64]
-  if (wv >= 4) {
+  if (loader) {
 #pragma unroll
     for (int c = 0; c < NCT; ++c)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        red[(((wv - 4) * NCT + c) * 4 + q) * 64 + lane] =
+        red[((wv * NCT + c) * 4 + q) * 64 + lane] =
             f32x4{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]};
-  }
-  __syncthreads();
-  if (wv < 4) {
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4& r = red[((wv * NCT + c) * 4 + q) * 64 + lane];
-        r = f32x4{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]} + r;
-      }
   }
   __syncthreads();
   // acc[c][r] is T[m0 + (r / 4) * 8 + (lane / 32) * 4 + r % 4][32 c + lane % 32]
@@ -711,7 +713,7 @@ template <int NCT, bool SMOOTH, bool INT4>
 static void launch_act_lr(dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M, int64_t K, float c6g,
                           float rc6g, const Nvfp4ScaleTable& tab, const uint16_t* l1t, int64_t kl, const float* lam,
                           int rpw, uint8_t* xq, void* xs, uint16_t* t) {
-  hipLaunchKernelGGL((k_quant_act_lowrank<NCT, SMOOTH, INT4>), grid, dim3(512), 0, stream, x, M, K, c6g, rc6g, tab,
+  hipLaunchKernelGGL((k_quant_act_lowrank<NCT, SMOOTH, INT4>), grid, dim3(64 * LrTile<NCT, SMOOTH, INT4>::NW), 0, stream, x, M, K, c6g, rc6g, tab,
                      l1t, kl, lam, rpw, xq, xs, t);
 }
 
