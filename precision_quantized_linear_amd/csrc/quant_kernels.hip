@@ -363,6 +363,10 @@ __global__ __launch_bounds__(1024) void k_quant_act_lowrank(const uint16_t* __re
                                                                        (int)kRawBufferWord3);
   const uint32_t lbase = lds_address(lds);
   const int ntiles = (int)((K + TK - 1) / TK);
+  // 32-bit forms for the offsets (K <= 2^21 and every buffer below 2^31 bytes, checked
+  // by the host)
+  const int k32 = (int)K;
+  const uint32_t m32 = (uint32_t)M, row0 = (uint32_t)m0;
 
   // Geometry of this lane's part of 1 KB slot sl of a tile (the same for every
   // tile): tile row and chunk held.
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(1024) void k_quant_act_lowrank(const uint16_t* __re
   };
   // Offsets valid for tile kt: chunks past K read zero (rows past M do through dx).
   auto voff = [&](int r, int c, int kt) -> uint32_t {
-    return (int64_t)kt * TK + 8 * c < K ? (uint32_t)r * pitch + 16u * (uint32_t)c : kOutOfRange;
+    return kt * TK + 8 * c < k32 ? (uint32_t)r * pitch + 16u * (uint32_t)c : kOutOfRange;
   };
   const bool loader = wv < 4;
   // The loads of tile kt (loading wavefronts): slots wv, wv + 4, ... of both tiles.
@@ -428,7 +432,7 @@ __global__ __launch_bounds__(1024) void k_quant_act_lowrank(const uint16_t* __re
         const u32x4 v = *slot;
         uint32_t p[4] = {v.x, v.y, v.z, v.w};
         if constexpr (SMOOTH) {
-          if ((int64_t)kt * TK + 8 * c < K) {  // chunks past K hold zeros and no factors
+          if (kt * TK + 8 * c < k32) {  // chunks past K hold zeros and no factors
             const f32x4* f = reinterpret_cast<const f32x4*>(xt + C::XB + C::LB + 32 * c);
             const f32x4 f0 = f[0], f1 = f[1];
             p[0] = smooth_pair(p[0], f0[0], f0[1]);
@@ -466,24 +470,26 @@ __global__ __launch_bounds__(1024) void k_quant_act_lowrank(const uint16_t* __re
             w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
             w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)w1, true);
           }
-          const int64_t k0 = (int64_t)kt * TK + 8 * c;
-          const bool in_k = k0 < K;
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, re, in_k ? (int)(r * K + k0) : (int)kOutOfRange, 0, 0);
+          const uint32_t k0 = (uint32_t)(kt * TK + 8 * c);
+          const bool in_k = k0 < (uint32_t)k32;
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, re, in_k ? (int)((uint32_t)r * (uint32_t)k32 + k0) : (int)kOutOfRange, 0, 0);
           __builtin_amdgcn_raw_buffer_store_b32(
               __float_as_uint(s), rsc,
-              in_k && (c & 7) == 0 && r < rows ? (int)(((k0 / 64) * M + m0 + r) * 4) : (int)kOutOfRange, 0, 0);
+              in_k && (c & 7) == 0 && r < rows ? (int)(((k0 / 64) * m32 + row0 + (uint32_t)r) * 4) : (int)kOutOfRange, 0, 0);
         } else {
           const Nvfp4Block sc = nvfp4_scale(absmax_value(m), c6g, rc6g, tab_d, tab_rd);
-          const int64_t k0 = (int64_t)kt * TK + 8 * c;
-          const bool in_k = k0 < K;
+          const uint32_t k0 = (uint32_t)(kt * TK + 8 * c);
+          const bool in_k = k0 < (uint32_t)k32;
           __builtin_amdgcn_raw_buffer_store_b32(nvfp4_word<true>(p, sc), re,
-                                                in_k ? (int)(r * qpitch + k0 / 2) : (int)kOutOfRange, 0, 0);
+                                                in_k ? (int)((uint32_t)r * (uint32_t)qpitch + k0 / 2) : (int)kOutOfRange,
+                                                0, 0);
           // the block's scale, from the lane holding its first half (even chunk)
-          const int64_t jb = k0 / 16;
+          const uint32_t jb = k0 / 16;
           __builtin_amdgcn_raw_buffer_store_b8(
               (uint8_t)sc.sf, rsc,
-              in_k && (c & 1) == 0 && r < rows ? (int)(((jb >> 3) * M + m0 + r) * 8 + (jb & 7)) : (int)kOutOfRange, 0,
-              0);
+              in_k && (c & 1) == 0 && r < rows ? (int)(((jb >> 3) * m32 + row0 + (uint32_t)r) * 8 + (jb & 7))
+                                               : (int)kOutOfRange,
+              0, 0);
         }
       }
     }
