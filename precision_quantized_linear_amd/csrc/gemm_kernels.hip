@@ -9,30 +9,28 @@
 // GEMM with one E4M3 scale per 16 elements.  gfx950's scaled MFMA applies one
 // power-of-two (E8M0) scale per 32 elements, and a code times an E4M3 scale needs
 // up to 6 significant bits, which no 8-, 6- or 4-bit operand format holds.  The
-// exact route taken here: both operands are expanded to bf16 values
-// e2m1(code) * dec(sf) (exact) -- activations by the quantize kernel, weights by
-// one streaming pass over the packed weight -- and multiplied on the bf16 MFMA
-// (V_MFMA_F32_32X32X16_BF16).  The global factor input_scale * weight_scale_2
-// and the optional SVDQuant low-rank term (Nunchaku post, "Background: SVDQuant
-// and Nunchaku": the up-projection fused into the GEMM) are applied to the fp32
-// accumulators before the single bf16 rounding; the low-rank pass accumulates
-// (T / gscale) L2 into the same accumulators, and the epilogue scales by gscale.
+// exact route taken here: both operands travel packed (E2M1 codes and E4M3 block
+// scales) into LDS, and each lane expands its own fragments in registers to f16
+// values e2m1(code) * dec(sf) (exact) for the f16 MFMA
+// (V_MFMA_F32_32X32X16_F16).  The global factor input_scale * weight_scale_2
+// scales the fp32 accumulators; the optional SVDQuant low-rank term (Nunchaku
+// post, "Background: SVDQuant and Nunchaku": the up-projection fused into the
+// GEMM) then adds T L2 to them on the bf16 MFMA, before the single bf16 rounding.
 //
-// Pipeline (both GEMMs):
+// Common to the fp8r and nvfp4 GEMMs (the INT4 GEMM at the end of the file has a
+// ring of its own, described there):
 // * a 256-thread workgroup (4 wavefronts, 2 x 2) owns a 256 x 256 output tile; a
 //   wavefront owns 128 x 128 (16 MFMA tiles of 32 x 32, 256 fp32 accumulators
 //   per lane in AGPRs, one wavefront per SIMD);
-// * K is walked in 64-byte slabs (64 fp8 or 32 bf16 elements per row); each
-//   stage holds the 256-row slab of both operands (32 KB) and four stages ring
-//   through 128 KB of the 160 KB LDS;
-// * slabs move global -> LDS with buffer_load_dwordx4 ... lds (no register
-//   staging): slab g + 4 is issued while slab g is multiplied, three steps before
-//   its fragments are first read, spread between the MFMAs; rows past the matrix
-//   and bytes past K read as zero through the buffer range check;
-// * the 16-byte chunks of each 64-byte row are XOR-swizzled with
-//   (r ^ r >> 3) & 3, which makes the MFMA operand reads bank-conflict free;
-// * operand fragments of the next slab are read into the registers of the
-//   current slab's fragments as each one is used for the last time;
+// * workgroups are persistent and walk an XCD-grouped tile order; the tail tiles
+//   of the last round are split into 128-row halves;
+// * K is walked in pairs of slabs whose rows are whole 128-byte lines; two stages
+//   ring through the LDS, and a pair's loads (buffer_load_dwordx4 ... lds, no
+//   register staging) are issued one after an MFMA while the previous pair is
+//   multiplied; rows past the matrix and bytes past K read as zero through the
+//   buffer range check;
+// * chunk c of a 128-byte stage row r sits at chunk c ^ (r % 8), which keeps the
+//   16-byte operand reads of a wavefront on distinct banks;
 // * operands are swapped (the MFMA computes y^T), so each lane ends with runs of
 //   four consecutive output columns of a row; lanes l and l + 32 swap halves
 //   (V_PERMLANE32_SWAP) and each stores eight consecutive columns as one 16-byte
@@ -46,8 +44,8 @@ namespace qpl {
 
 namespace {
 
-constexpr int SROW = 64;            // bytes per slab row
-constexpr int NST = 4;              // stages in a ring of 64-byte slabs
+constexpr int SROW = 64;            // bytes per slab row of the INT4 GEMM (one 64-channel group)
+constexpr int NST = 4;              // slabs per tile from which workgroups are persistent
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int soff(int r, int c) { return r * SROW + ((c ^ swz(r)) << 4); }
