@@ -1,7 +1,7 @@
 // The nvfp4 block rule on the device (Diffusers guide "BFL (fp8r / nvfp4)", intro
 // bullet on nvfp4), used by the quantizers: per 16-element block
-// sf = E4M3(bmax / (6 g)), d = dec(sf) * g, codes E2M1(x / d) with correctly rounded
-// divisions, and the exact bf16 expansion e2m1(code) * dec(sf).
+// sf = E4M3(bmax / (6 g)), d = dec(sf) * g, codes E2M1(x / d) equal to those of the
+// correctly rounded divisions, and the exact bf16 expansion e2m1(code) * dec(sf).
 #pragma once
 
 #include "qpl_device.h"

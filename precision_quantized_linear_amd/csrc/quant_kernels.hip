@@ -5,9 +5,10 @@
 //
 // Numerics follow the schemes of the Diffusers guide "BFL (fp8r / nvfp4)" (intro
 // bullets) as read in qpl.h: fp8r s = amax / 448, codes E4M3(x / s); nvfp4
-// sf = E4M3(bmax / (6 g)), d = dec(sf) * g, codes E2M1(x / d).  Divisions are
-// correctly rounded (a reciprocal with one fma correction, or IEEE division where
-// that is not exact), so codes match an fp32 reference bit for bit.
+// sf = E4M3(bmax / (6 g)), d = dec(sf) * g, codes E2M1(x / d).  Divisions give
+// the codes of the correctly rounded quotient (a reciprocal with one fma
+// correction, or IEEE division outside the range where that holds; see div_rn),
+// so codes match an fp32 reference bit for bit.
 #include <cmath>
 
 #include "qpl_dma.h"
@@ -552,9 +553,10 @@ __global__ __launch_bounds__(1024) void k_quant_act_lowrank(const uint16_t* __re
 
 // ---------------------------------------------------------------------------
 // INT4 (the INT4 variant of svdq_w4a4): one lane per group of 64 channels.
-// s = amax / 7 (correctly rounded); q = clamp(rint(x / s), -8, 7), the quotient
-// correctly rounded (Markstein step from RN(1/s) inside div_rn's range, IEEE
-// division outside); an all-zero group gives s = 0 and codes 0.  F8: each code is
+// s = amax / 7 (correctly rounded); q = clamp(rint(x / s), -8, 7), rint taken of
+// the quotient div_rn forms inside its range (whose integer is that of the
+// correctly rounded quotient) and of the IEEE quotient outside; an all-zero group
+// gives s = 0 and codes 0.  F8: each code is
 // written as the E4M3 byte of its integer value [rows, K] (the GEMM's operand:
 // -8..7 are exact in E4M3) and the scales group-major [K/64, rows] (so that the
 // GEMM reads one group's scales of consecutive rows contiguously); otherwise the
