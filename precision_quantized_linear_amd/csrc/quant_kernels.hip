@@ -285,9 +285,9 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict_
 // instead of adding to it.  Per tile,
 //   1. quantizing wavefront 4 + q takes the x tile's 1 KB slots q, q + 12, ...
 //      (lane l holds eight values, lanes l and l ^ 1 one 16-element block) and
-//      store the packed codes (4 bytes per lane) and, from the block's first lane,
-//      its scale byte in the GEMM's slab-major layout [K/128][M][8], while the
-//      loading wavefronts issue the loads of tile kt + S - 1;
+//      stores the packed codes (4 bytes per lane) and, from the block's first
+//      lane, its scale byte in the GEMM's slab-major layout [K/128][M][8], while
+//      the loading wavefronts issue the loads of tile kt + S - 1;
 //   2. the loading wavefronts run the bf16 MFMA 32x32x16 over their quarter of the
 //      tile's k range, reading both operands from LDS, into per-wave partial sums
 //      of T, while the quantizing ones work.
@@ -301,9 +301,10 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const uint16_t* __restrict_
 //
 // SMOOTH (SVDQuant smoothing): each stage also holds the tile's TK smoothing
 // factors (one dword load per loading wavefront: wave w moves factors
-// 64 w .. 64 w + 63, zeros past TK or K).  Step 1 divides its values by them, quantizes the smoothed
-// bf16 values and writes them back over the tile, and step 2 waits for every
-// wave's write-back, so that both branches read the same smoothed activation.
+// 64 w .. 64 w + 63, zeros past TK or K).  Step 1 divides its values by them,
+// quantizes the smoothed bf16 values and writes them back over the tile, and step
+// 2 waits at a barrier for every wave's write-back, so that both branches read the
+// same smoothed activation.
 //
 // INT4 (the INT4 variant of svdq_w4a4): step 1 quantizes 64-channel groups
 // instead (s = amax / 7, q = clamp(rint(x / s), -8, 7)): a group is eight chunks of
@@ -319,7 +320,7 @@ struct LrTile {
   static constexpr int LB = 32 * NCT * TK * 2;      // L1^T tile bytes
   static constexpr int FB = SMOOTH ? 4 * 256 : 0;  // smoothing factor bytes (one 256-byte slot per loading wave)
   static constexpr int SB = XB + LB + FB;           // stage bytes
-  static constexpr int S = (NCT == 1 || NCT == 3) ? 4 : 3;  // stages in the ring (<= 128 KB, 144 KB for NCT 2)
+  static constexpr int S = (NCT == 1 || NCT == 3) ? 4 : 3;  // stages in the ring (at most 147 KB)
   static constexpr int NW = 16;                     // wavefronts: 0-3 load, 4-15 quantize
   static constexpr int NQ = 12;                     // quantizing wavefronts
   static constexpr int NM = 4;                      // multiplying wavefronts (the loading ones)
