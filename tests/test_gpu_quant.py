@@ -268,6 +268,8 @@ def random_weight(N, K, seed):
     ("svdq_w4a4", 300, 400, 48, False, 0),       # ragged: K % 128 != 0 (a partial last scale slab)
     ("svdq_w4a4", 37, 272, 33, True, 0),         # smoothed, odd rows
     ("nvfp4_dit", 1, 16, 1, False, 0),           # one block
+    ("nvfp4_dit", 64, 3072, 12288, False, 0),    # the DiT weight's scales: 1152 relay workgroups in the quantizer's launch
+    ("svdq_w4a4", 64, 400, 4100, False, 0),      # ragged weight relay: K % 128 != 0, N % 256 != 0
     ("svdq_w4a4", None, None, 64, False, 32),    # the SVDQuant workload at full size, fused x L1 quantizer
     ("svdq_w4a4", None, None, 64, True, 32),     # the same with smoothing
     ("svdq_w4a4", 300, 400, 48, False, 32),      # ragged M and K
