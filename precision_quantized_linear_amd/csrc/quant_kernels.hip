@@ -218,7 +218,7 @@ __device__ __forceinline__ void nvfp4_prep_block(const Nvfp4Prep& a, unsigned bl
   }
 }
 
-Nvfp4Prep nvfp4_prep_args(const uint8_t* wbs, int64_t N, int64_t K, uint8_t* wsl, int64_t M, uint8_t* xs) {
+static Nvfp4Prep nvfp4_prep_args(const uint8_t* wbs, int64_t N, int64_t K, uint8_t* wsl, int64_t M, uint8_t* xs) {
   Nvfp4Prep a;
   a.wbs = wbs;
   a.wsl = wsl;
