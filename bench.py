@@ -146,8 +146,8 @@ def main():
 
     # ---------------------------------------------------------------- timed region
     # No events here (an event pair holds the stream for a few microseconds on each
-    # side of a launch); the per-kernel and per-linear breakdown comes from a second
-    # pass below with every launch bracketed.
+    # side of a launch); the per-linear and per-kernel figures come from two passes
+    # below, one with events around each linear, one around each launch.
     qpl.timing_collect()  # drop anything recorded so far
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -201,7 +201,7 @@ def main():
     kernels = {k: {"launches": n, "avg_us": round(1e3 * t / n, 2)} for k, (n, t) in kern.items() if n}
 
     # ---------------------------------------------------------------- roofline (dominant kernel)
-    # every launch of the breakdown pass (clocks ramped by the warm-up and the timed region)
+    # every launch of the per-kernel pass (clocks ramped by the warm-up and the timed region)
     n_g, t_g = kern["gemm_nvfp4"]
     avg_s = t_g / n_g * 1e-3
     e = lin["nvfp4"]

@@ -63,13 +63,6 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 // tile's first row to the matrix end).
 __device__ __forceinline__ int64_t M_rows(int64_t rows_left) { return rows_left < 256 ? rows_left : 256; }
 
-// Buffer descriptor over the tile's rows of a row-major byte matrix: reads past
-// the tile's last valid row return zero.
-__device__ __forceinline__ u32x4 tile_desc(const void* base, int64_t rows_left, int64_t pitch) {
-  const int64_t rows = rows_left < 256 ? rows_left : 256;
-  return make_desc(base, rows * pitch);
-}
-
 // MFMA operands.  fp8: a 32x32x64 MFMA operand (32 K-bytes per lane).  bf16: a
 // 32x32x16 MFMA operand (8 K-values per lane, one 16-byte chunk); a 64-byte slab
 // holds two of them (sub-steps).
@@ -543,11 +536,6 @@ struct PackedArgs {
   int pitch2, kbytes2; // low-rank rows: 2 kl bytes
   int tiles_m, tiles_n, ntiles, nwg, nfull, ntail;
 };
-
-// (s, s) as an f16 pair for the E4M3 scale in byte j of sc (exact).
-__device__ __forceinline__ f16x2 e4m3_pair(uint32_t sc, uint32_t j) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(sc, sc, j * 0x01010101u), 1.0f, false);
-}
 
 // Eight E2M1 codes (a dword, element 2i in the low nibble of byte i) times the
 // pair s: f16 values code * s in element order.
