@@ -44,8 +44,9 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // SVDQuant smoothing of a bf16 pair (Nunchaku post, "Background: SVDQuant and
 // Nunchaku": activation outliers move into the weights, so input channel k is
-// divided by its factor): bf16_rne(x / l) per half, with the correctly rounded
-// fp32 division of this build.  l0 divides the low half, l1 the high half.
+// divided by its factor): bf16_rne(x / l) per half, with a correctly rounded fp32
+// division (the library is compiled with -fhip-fp32-correctly-rounded-divide-sqrt).
+// l0 divides the low half, l1 the high half.
 __device__ __forceinline__ uint32_t smooth_pair(uint32_t pair, float l0, float l1) {
   return f32_to_bf16(bf16_lo(pair) / l0) | (f32_to_bf16(bf16_hi(pair) / l1) << 16);
 }
